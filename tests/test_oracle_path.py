@@ -1,0 +1,235 @@
+"""Pins of the oracle's decode path: brute force with Python loops on tiny
+inputs, hand-computable cases, PyTorch's own float64 attention routine, and
+the identities the pages state (sparse = dense when top-k covers every
+entry; the hierarchical path = the flat path when the pool covers every
+block; a Reuse layer fed a Full layer's top-k reproduces its attention)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa2 as O
+from oracle import formats as F
+
+SCALE = float(np.float32(1.0 / math.sqrt(512)))
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(
+        torch.bfloat16).view(torch.uint16).numpy()
+
+
+def _case(n, seed, n_swa=128):
+    rng = np.random.default_rng(seed)
+    main = rng.standard_normal((n, 512)).astype(np.float32)
+    idx = rng.standard_normal((n, 128)).astype(np.float32)
+    swa = rng.standard_normal((128, 512)).astype(np.float32)
+    mc, ms = O.pack_main(main)
+    ic, is_ = O.pack_idx(idx)
+    return dict(mc=mc, ms=ms, ic=ic, is_=is_, sw=O.pack_swa(swa),
+                qi=_bf16(rng.standard_normal((32, 128))),
+                w=rng.uniform(0, 1, 32).astype(np.float32),
+                q=_bf16(rng.standard_normal((64, 512))), n=n, n_swa=n_swa)
+
+
+# ------------------------------------------------------------- indexer ----
+def test_scores_bruteforce_loops():
+    c = _case(6, 0)
+    keys = O.unpack_idx(c["ic"], c["is_"])
+    q = F.bf16_bits_to_f64(c["qi"])
+    got = O.indexer_scores(c["qi"], c["w"], keys)
+    for j in range(6):
+        tot = 0.0
+        for h in range(32):
+            dot = math.fsum(float(q[h, d]) * float(keys[j, d])
+                            for d in range(128))
+            tot += float(c["w"][h]) * max(dot, 0.0)
+        assert got[j] == pytest.approx(tot, rel=1e-13, abs=1e-13)
+
+
+def test_scores_hand_cases():
+    keys = np.zeros((3, 128))
+    keys[0, 5] = 2.0          # one-hot key
+    keys[1, 5] = -2.0         # negative dot for every head -> ReLU 0
+    keys[2, 7] = 1.0
+    qi = np.zeros((32, 128), np.float32)
+    qi[:, 5] = 1.5
+    qi[3, 7] = -1.0
+    w = np.linspace(0.1, 1.0, 32).astype(np.float32)
+    s = O.indexer_scores(_bf16(qi), w, keys)
+    assert s[0] == pytest.approx(3.0 * float(np.sum(w.astype(np.float64))))
+    assert s[1] == 0.0
+    assert s[2] == 0.0        # only head 3 touches dim 7, with a negative dot
+
+
+def test_scores_permutation_equivariant():
+    c = _case(50, 1)
+    keys = O.unpack_idx(c["ic"], c["is_"])
+    perm = np.random.default_rng(2).permutation(50)
+    a = O.indexer_scores(c["qi"], c["w"], keys)
+    b = O.indexer_scores(c["qi"], c["w"], keys[perm])
+    assert np.array_equal(a[perm], b)
+
+
+# --------------------------------------------------------------- top-k ----
+def test_topk_bruteforce_and_ties():
+    rng = np.random.default_rng(3)
+    s = rng.integers(0, 20, 300).astype(np.float64)      # many exact ties
+    for k in (1, 7, 64, 300, 512):
+        ranked = sorted(range(300), key=lambda j: (-s[j], j))[:k]
+        want = sorted(ranked) + [-1] * max(0, k - 300)
+        assert O.topk(s, k).tolist() == want
+
+
+def test_topk_invariants():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal(5000)
+    sel = O.topk(s, 512)
+    assert np.all(np.diff(sel) > 0)
+    mask = np.zeros(5000, bool)
+    mask[sel] = True
+    assert s[mask].min() >= s[~mask].max()
+
+
+def test_topk_with_ids_reports_ids():
+    s = np.array([1.0, 5.0, 5.0, 2.0])
+    ids = np.array([40, 30, 10, 20])
+    # 5.0 at ids 30 and 10 tie: lower id first; k = 2 -> {10, 30}
+    assert O.topk(s, 2, ids=ids).tolist() == [10, 30]
+    assert O.topk(s, 3, ids=ids).tolist() == [10, 20, 30]
+
+
+def test_topk_gap():
+    assert O.topk_gap([4.0, 3.0, 2.0], 2) == pytest.approx(1 / 3)
+    assert O.topk_gap([4.0, 3.0], 2) == np.inf
+
+
+# ----------------------------------------------------------- attention ----
+def test_attention_vs_torch_sdpa():
+    rng = np.random.default_rng(5)
+    q = _bf16(rng.standard_normal((64, 512)))
+    keys = rng.standard_normal((100, 512))
+    got = O.mqa_decode(q, keys, SCALE)
+    qt = torch.from_numpy(F.bf16_bits_to_f64(q))[None, :, None, :]
+    kt = torch.from_numpy(keys)[None, None].expand(1, 64, 100, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, kt, scale=SCALE)[0, :, 0, :].numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_degenerate_cases():
+    rng = np.random.default_rng(6)
+    q = _bf16(rng.standard_normal((64, 512)))
+    k1 = rng.standard_normal((1, 512))
+    assert np.allclose(O.mqa_decode(q, k1, SCALE), np.repeat(k1, 64, 0))
+    same = np.repeat(k1, 9, 0)
+    assert np.allclose(O.mqa_decode(q, same, SCALE), np.repeat(k1, 64, 0))
+    keys = rng.standard_normal((33, 512))
+    o = O.mqa_decode(q, keys, SCALE)
+    assert np.all(o <= keys.max(0) + 1e-12) and np.all(o >= keys.min(0) - 1e-12)
+
+
+def test_attention_tiny_loops():
+    rng = np.random.default_rng(7)
+    q = _bf16(rng.standard_normal((64, 512)))
+    keys = rng.standard_normal((5, 512))
+    got = O.mqa_decode(q, keys, SCALE)
+    qf = F.bf16_bits_to_f64(q)
+    for h in (0, 17, 63):
+        lg = [SCALE * math.fsum(qf[h, d] * keys[j, d] for d in range(512))
+              for j in range(5)]
+        m = max(lg)
+        e = [math.exp(x - m) for x in lg]
+        z = math.fsum(e)
+        for d in (0, 100, 511):
+            want = math.fsum(e[j] / z * keys[j, d] for j in range(5))
+            assert got[h, d] == pytest.approx(want, rel=1e-11, abs=1e-12)
+
+
+# -------------------------------------------------------- whole layers ----
+def test_sparse_equals_dense_when_k_covers_all():
+    c = _case(40, 8)
+    sel, out, _ = O.full_layer(c["mc"], c["ms"], c["ic"], c["is_"], 40,
+                               c["qi"], c["w"], c["q"], c["sw"], 128, 512,
+                               SCALE)
+    assert sel[:40].tolist() == list(range(40)) and np.all(sel[40:] == -1)
+    # dense attention over all entries + the window, by torch's routine
+    keys = np.concatenate([O.unpack_main(c["mc"], c["ms"]),
+                           O.unpack_swa(c["sw"])])
+    qt = torch.from_numpy(F.bf16_bits_to_f64(c["q"]))[None, :, None, :]
+    kt = torch.from_numpy(keys)[None, None].expand(1, 64, keys.shape[0], 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, kt, scale=SCALE)[0, :, 0, :].numpy()
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_reuse_with_full_topk_reproduces_full():
+    c = _case(700, 9)
+    sel, out, _ = O.full_layer(c["mc"], c["ms"], c["ic"], c["is_"], 700,
+                               c["qi"], c["w"], c["q"], c["sw"], 128, 512,
+                               SCALE)
+    out2 = O.reuse_layer(c["mc"], c["ms"], sel, c["q"], c["sw"], 128, SCALE)
+    assert np.array_equal(out, out2)
+
+
+def test_full_layer_topk_is_bruteforce_over_scores():
+    c = _case(900, 10)
+    sel, _, sc = O.full_layer(c["mc"], c["ms"], c["ic"], c["is_"], 800,
+                              c["qi"], c["w"], c["q"], c["sw"], 128, 512,
+                              SCALE)
+    assert len(sc) == 800                                    # causal bound
+    order = sorted(range(800), key=lambda j: (-sc[j], j))[:512]
+    assert sel.tolist() == sorted(order)
+
+
+def test_hierarchical_equals_flat_when_pool_covers_all():
+    c = _case(8 * 40 + 5, 11)
+    n = c["n"]
+    bk = O.block_keys(c["ic"], c["is_"], n)
+    sel_h, out_h, pool, _ = O.hier_layer(
+        c["mc"], c["ms"], c["ic"], c["is_"], bk, n, c["qi"], c["w"], c["q"],
+        c["sw"], 128, 64, SCALE, n_keep=2048)
+    assert pool[:n].tolist() == list(range(n)) and np.all(pool[n:] == -1)
+    sel_f, out_f, _ = O.full_layer(c["mc"], c["ms"], c["ic"], c["is_"], n,
+                                   c["qi"], c["w"], c["q"], c["sw"], 128, 64,
+                                   SCALE)
+    assert np.array_equal(sel_h, sel_f)
+    assert np.allclose(out_h, out_f, rtol=0, atol=1e-12)
+
+
+def test_hierarchical_stage2_is_fine_scoring_in_pool():
+    c = _case(8 * 64, 12)
+    n = c["n"]
+    bk = O.block_keys(c["ic"], c["is_"], n)
+    sel, _, pool, fine = O.hier_layer(
+        c["mc"], c["ms"], c["ic"], c["is_"], bk, n, c["qi"], c["w"], c["q"],
+        c["sw"], 128, 32, SCALE, n_keep=16)
+    # pool = union of the 16 best blocks under block scores
+    bs = O.indexer_scores(c["qi"], c["w"], F.bf16_bits_to_f64(bk))
+    best = sorted(range(64), key=lambda b: (-bs[b], b))[:16]
+    assert pool.tolist() == sorted(8 * b + i for b in best for i in range(8))
+    # stage 2: brute-force fine scoring restricted to the pool
+    keys = O.unpack_idx(c["ic"], c["is_"])
+    allsc = O.indexer_scores(c["qi"], c["w"], keys)
+    ranked = sorted(pool.tolist(), key=lambda j: (-allsc[j], j))[:32]
+    assert sel.tolist() == sorted(ranked)
+
+
+def test_attention_rows_with_far_apart_logits():
+    # Heads whose logits sit thousands apart: each row needs its own maximum
+    # subtracted, or the low rows underflow to 0/0.
+    rng = np.random.default_rng(13)
+    keys = rng.standard_normal((20, 512)) * 30.0
+    qf = np.zeros((64, 512), np.float32)
+    qf[0] = keys[3] * 3.0
+    qf[1] = -keys[3] * 3.0
+    qf[2:] = rng.standard_normal((62, 512))
+    q = _bf16(qf)
+    got = O.mqa_decode(q, keys, SCALE)
+    assert np.all(np.isfinite(got))
+    qt = torch.from_numpy(F.bf16_bits_to_f64(q))[None, :, None, :]
+    kt = torch.from_numpy(keys)[None, None].expand(1, 64, 20, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, kt, scale=SCALE)[0, :, 0, :].numpy()
+    assert np.allclose(got, ref, rtol=1e-10, atol=1e-10)
