@@ -1,0 +1,246 @@
+"""Python binding of libcsa2 (ctypes).  Argument marshalling only: every
+step of the decode path runs in the library's HIP kernels.  Tensors are
+torch device tensors; calls are enqueued on torch's current stream.
+
+The names mirror the C ABI in include/csa2.h (csa2_pack_kv -> pack_kv, ...).
+A missing or unloadable library raises immediately: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+FMT_MAIN, FMT_IDX, FMT_SWA = 0, 1, 2
+KEYS_MXFP4, KEYS_BF16 = 0, 1
+OP_TOPK, OP_DECODE, OP_REUSE = 0, 1, 2
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGNMENT",
+          4: "WORKSPACE", 5: "HIP"}
+EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
+           "csa2_indexer_score", "csa2_topk", "csa2_sparse_attn_decode",
+           "csa2_reuse_attn", "csa2_workspace_size", "csa2_entry_bytes",
+           "csa2_kv_bytes_per_token", "csa2_last_error", "csa2_version"]
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libcsa2 {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("main_codes", ctypes.c_void_p),
+                ("main_scales", ctypes.c_void_p),
+                ("idx_codes", ctypes.c_void_p),
+                ("idx_scales", ctypes.c_void_p),
+                ("block_keys", ctypes.c_void_p),
+                ("n_cap", ctypes.c_int64),
+                ("n_entries", ctypes.c_void_p)]
+
+
+class PoolOpts(ctypes.Structure):
+    _fields_ = [("n_blocks_keep", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+_lib = None
+
+P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                        ctypes.c_float, ctypes.c_size_t)
+
+
+def load(path=None):
+    """Load libcsa2.so (built by `python -m fp4_kv_cache_amd.build`)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libcsa2 is not built: {p} is missing "
+                          "(run python -m fp4_kv_cache_amd.build)")
+    lib = ctypes.CDLL(p)
+    sig = {
+        "csa2_pack_kv": (I32, [I32, P, I64, P, P, P]),
+        "csa2_unpack_kv": (I32, [I32, P, P, I64, P, P]),
+        "csa2_build_block_keys": (I32, [P, P, I64, P, I32, I32, P, P]),
+        "csa2_indexer_score": (I32, [I32, P, P, I64, P, P, I32, P, P, I32, P,
+                                     P]),
+        "csa2_topk": (I32, [P, I64, P, P, I32, I32, I32, P, P, P, SZ, P]),
+        "csa2_sparse_attn_decode": (I32, [ctypes.POINTER(CacheDesc), P, P, P,
+                                          P, P, I32, I32, F32,
+                                          ctypes.POINTER(PoolOpts), P, P, P,
+                                          SZ, P]),
+        "csa2_reuse_attn": (I32, [P, P, I64, P, I32, P, P, P, I32, F32, P, P,
+                                  SZ, P]),
+        "csa2_workspace_size": (SZ, [I32, I32, I64, I32,
+                                     ctypes.POINTER(PoolOpts)]),
+        "csa2_entry_bytes": (I32, [I32]),
+        "csa2_kv_bytes_per_token": (ctypes.c_double,
+                                    [ctypes.POINTER(I32), I32]),
+        "csa2_last_error": (ctypes.c_char_p, []),
+        "csa2_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise Csa2Error(status, load().csa2_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, shape=None, name="tensor"):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def version():
+    return load().csa2_version().decode()
+
+
+def entry_bytes(fmt):
+    return load().csa2_entry_bytes(fmt)
+
+
+def kv_bytes_per_token(m_of_kv_layers):
+    arr = (I32 * len(m_of_kv_layers))(*m_of_kv_layers)
+    return load().csa2_kv_bytes_per_token(arr, len(m_of_kv_layers))
+
+
+def workspace_size(op, B, n_cap, k, pool=None):
+    po = PoolOpts(*pool) if pool is not None else None
+    return load().csa2_workspace_size(op, B, n_cap, k,
+                                      ctypes.byref(po) if po else None)
+
+
+def workspace(nbytes, device):
+    """A 256-byte aligned device workspace of at least nbytes."""
+    t = torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8,
+                    device=device)
+    off = (-t.data_ptr()) % 256
+    return t[off:off + max(int(nbytes), 1)]
+
+
+# ------------------------------------------------------------------ calls --
+def pack_kv(fmt, src, codes=None, scales=None):
+    """Quantise float32 rows [n, 512|128] into (codes, scales)."""
+    _need(src, torch.float32, name="src")
+    n = src.shape[0]
+    cw, sw = {FMT_MAIN: (256, 32), FMT_IDX: (64, 4), FMT_SWA: (512, 0)}[fmt]
+    if codes is None:
+        codes = torch.empty((n, cw), dtype=torch.uint8, device=src.device)
+    if scales is None and sw:
+        scales = torch.empty((n, sw), dtype=torch.uint8, device=src.device)
+    _check(load().csa2_pack_kv(fmt, _ptr(src), n, _ptr(codes), _ptr(scales),
+                               _stream()))
+    return codes, scales
+
+
+def unpack_kv(fmt, codes, scales=None):
+    n = codes.shape[0]
+    dim = 128 if fmt == FMT_IDX else 512
+    out = torch.empty((n, dim), dtype=torch.float32, device=codes.device)
+    _check(load().csa2_unpack_kv(fmt, _ptr(codes), _ptr(scales), n, _ptr(out),
+                                 _stream()))
+    return out
+
+
+def build_block_keys(idx_codes, idx_scales, n_entries, block=8):
+    """idx planes [B, n_cap, 64] / [B, n_cap, 4] -> bf16 keys [B, nb, 128]."""
+    B, n_cap = idx_codes.shape[0], idx_codes.shape[1]
+    nb = (n_cap + block - 1) // block
+    out = torch.empty((B, nb, 128), dtype=torch.bfloat16,
+                      device=idx_codes.device)
+    _check(load().csa2_build_block_keys(_ptr(idx_codes), _ptr(idx_scales),
+                                        n_cap, _ptr(n_entries), B, block,
+                                        _ptr(out), _stream()))
+    return out
+
+
+def indexer_score(keyfmt, k_codes, k_scales, n_entries, q_idx, w, cand=None):
+    """Scores [B, n_cap] (or [B, n_cand] for candidate ids)."""
+    B, n_cap = k_codes.shape[0], k_codes.shape[1]
+    rows = n_cap if cand is None else cand.shape[1]
+    out = torch.empty((B, rows), dtype=torch.float32, device=k_codes.device)
+    _check(load().csa2_indexer_score(
+        keyfmt, _ptr(k_codes), _ptr(k_scales), n_cap, _ptr(n_entries),
+        _ptr(cand), 0 if cand is None else cand.shape[1], _ptr(q_idx),
+        _ptr(w), B, _ptr(out), _stream()))
+    return out
+
+
+def topk(scores, k, n_valid=None, ids=None, block=1, limit=None, ws=None):
+    B, ld = scores.shape
+    out = torch.empty((B, k * block), dtype=torch.int32, device=scores.device)
+    need = workspace_size(OP_TOPK, B, ld, k)
+    if ws is None:
+        ws = workspace(need, scores.device)
+    _check(load().csa2_topk(_ptr(scores), ld, _ptr(n_valid), _ptr(ids), B, k,
+                            block, _ptr(limit), _ptr(out), _ptr(ws),
+                            ws.numel(), _stream()))
+    return out
+
+
+def cache_desc(main_codes, main_scales, idx_codes, idx_scales, n_entries,
+               block_keys=None):
+    return CacheDesc(main_codes.data_ptr(), main_scales.data_ptr(),
+                     idx_codes.data_ptr(), idx_scales.data_ptr(),
+                     0 if block_keys is None else block_keys.data_ptr(),
+                     main_codes.shape[1], n_entries.data_ptr())
+
+
+def sparse_attn_decode(cache, q_idx, w, q, swa, n_swa, k, scale, pool=None,
+                       out=None, topk_out=None, ws=None):
+    """One Full-layer decode step.  `cache` is a CacheDesc (keep the
+    tensors it points to alive).  Returns (out bf16 [B,64,512], topk
+    [B,k])."""
+    B = q.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
+    if topk_out is None:
+        topk_out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    po = PoolOpts(*pool) if pool is not None else None
+    if ws is None:
+        need = load().csa2_workspace_size(OP_DECODE, B, cache.n_cap, k,
+                                          ctypes.byref(po) if po else None)
+        ws = workspace(need, dev)
+    _check(load().csa2_sparse_attn_decode(
+        ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
+        _ptr(n_swa), B, k, float(scale), ctypes.byref(po) if po else None,
+        _ptr(out), _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
+    return out, topk_out
+
+
+def reuse_attn(main_codes, main_scales, topk_ids, q, swa, n_swa, scale,
+               out=None, ws=None):
+    B, k = topk_ids.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(workspace_size(OP_REUSE, B, main_codes.shape[1], k), dev)
+    _check(load().csa2_reuse_attn(
+        _ptr(main_codes), _ptr(main_scales), main_codes.shape[1],
+        _ptr(topk_ids), k, _ptr(q), _ptr(swa), _ptr(n_swa), B, float(scale),
+        _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out

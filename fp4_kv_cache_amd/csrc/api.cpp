@@ -1,0 +1,416 @@
+// libcsa2 C ABI: argument validation, workspace layout and the enqueue
+// order of each call.  Every check happens before the first launch; on
+// failure nothing is enqueued and a thread-local message is kept.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/csa2.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa2_status fail(csa2_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+csa2_status hip_fail(hipError_t e, const char* what) {
+  return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Device present and current?
+csa2_status need_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "no HIP device");
+  return CSA2_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+constexpr int kMaxK = 2048;
+constexpr int kMaxBlock = 64;
+constexpr int64_t kMaxCap = INT32_MAX;
+
+// Workspace layout of csa2_sparse_attn_decode.
+struct DecodeLayout {
+  bool pool;
+  int64_t nb = 0, n_cand = 0;
+  int kb = 0;
+  size_t off_scores = 0, off_nblk = 0, off_bscores = 0, off_pool = 0,
+         off_pscores = 0, off_topk = 0, off_attn = 0, total = 0;
+  csa2::TopkPlan p1{}, p2{};
+};
+
+DecodeLayout decode_layout(int B, int64_t n_cap, int k,
+                           const csa2_pool_opts* pool) {
+  DecodeLayout L;
+  L.pool = pool != nullptr;
+  size_t off = 0;
+  size_t tk = 0;
+  if (!L.pool) {
+    L.off_scores = off;
+    off += align256((size_t)B * n_cap * 4);
+    L.p1 = csa2::topk_plan(n_cap, k);
+    tk = csa2::topk_workspace(B, L.p1);
+  } else {
+    L.nb = (n_cap + pool->block - 1) / pool->block;
+    L.kb = (int)std::min<int64_t>(pool->n_blocks_keep, L.nb);
+    if (L.kb < 1) L.kb = 1;
+    L.n_cand = (int64_t)L.kb * pool->block;
+    L.off_nblk = off;
+    off += align256((size_t)B * 4);
+    L.off_bscores = off;
+    off += align256((size_t)B * L.nb * 4);
+    L.off_pool = off;
+    off += align256((size_t)B * L.n_cand * 4);
+    L.off_pscores = off;
+    off += align256((size_t)B * L.n_cand * 4);
+    L.p1 = csa2::topk_plan(L.nb, L.kb);
+    L.p2 = csa2::topk_plan(L.n_cand, k);
+    tk = std::max(csa2::topk_workspace(B, L.p1), csa2::topk_workspace(B, L.p2));
+  }
+  L.off_topk = off;
+  off += align256(tk);
+  L.off_attn = off;
+  off += align256(csa2::attn_workspace(B, k));
+  L.total = off;
+  return L;
+}
+
+csa2_status check_pool(const csa2_pool_opts* pool) {
+  if (!pool) return CSA2_OK;
+  if (pool->n_blocks_keep < 1 || pool->block < 1 || pool->block > kMaxBlock)
+    return fail(CSA2_ERR_UNSUPPORTED,
+                "pool: n_blocks_keep must be >= 1 and block in 1..%d",
+                kMaxBlock);
+  if ((int64_t)pool->n_blocks_keep * pool->block > (int64_t)1 << 26)
+    return fail(CSA2_ERR_UNSUPPORTED, "pool: n_blocks_keep * block too large");
+  return CSA2_OK;
+}
+
+csa2_status check_attn_common(const uint8_t* main_codes,
+                              const uint8_t* main_scales, int64_t n_cap,
+                              const uint16_t* q, const uint8_t* swa,
+                              const int32_t* n_swa, int32_t B, int32_t k,
+                              float scale, const uint16_t* out) {
+  if (B < 0) return fail(CSA2_ERR_INVALID_ARG, "B must be >= 0");
+  if (k < 1 || k > kMaxK)
+    return fail(CSA2_ERR_UNSUPPORTED, "k must be in 1..%d (got %d)", kMaxK, k);
+  if (n_cap < 0 || n_cap > kMaxCap)
+    return fail(CSA2_ERR_INVALID_ARG, "n_cap must be in 0..2^31-1");
+  if (!(scale == scale) || scale == 0.0f)
+    return fail(CSA2_ERR_INVALID_ARG, "scale must be a finite nonzero float");
+  if (B == 0) return CSA2_OK;
+  if (!main_codes || !main_scales || !q || !swa || !n_swa || !out)
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(main_codes, 16) || !aligned(q, 16) || !aligned(out, 16) ||
+      !aligned(swa, 16) || !aligned(main_scales, 4) || !aligned(n_swa, 4))
+    return fail(CSA2_ERR_ALIGNMENT,
+                "main_codes, q, out, swa need 16-byte and main_scales, "
+                "n_swa 4-byte alignment");
+  const size_t out_bytes = (size_t)B * 64 * 512 * 2;
+  if (overlap(out, out_bytes, q, out_bytes) ||
+      overlap(out, out_bytes, swa, (size_t)B * 128 * 512) ||
+      overlap(out, out_bytes, main_codes, (size_t)B * n_cap * 256))
+    return fail(CSA2_ERR_INVALID_ARG, "out overlaps an input");
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_last_error(void) { return g_err; }
+
+const char* csa2_version(void) { return "libcsa2 0.1.0 (gfx950)"; }
+
+int32_t csa2_entry_bytes(int32_t fmt) {
+  switch (fmt) {
+    case CSA2_FMT_MAIN: return 256 + 32;
+    case CSA2_FMT_IDX: return 64 + 4;
+    case CSA2_FMT_SWA: return 512;
+    default: return -1;
+  }
+}
+
+double csa2_kv_bytes_per_token(const int32_t* m, int32_t n) {
+  if (!m || n < 0) return -1.0;
+  const double entry = csa2_entry_bytes(CSA2_FMT_MAIN) + csa2_entry_bytes(CSA2_FMT_IDX);
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) {
+    if (m[i] < 1) return -1.0;
+    s += entry / m[i];
+  }
+  return s;
+}
+
+size_t csa2_workspace_size(int32_t op, int32_t B, int64_t n_cap, int32_t k,
+                           const csa2_pool_opts* pool) {
+  if (B < 0 || n_cap < 0 || n_cap > kMaxCap || k < 1 || k > kMaxK) return 0;
+  switch (op) {
+    case CSA2_OP_TOPK:
+      return csa2::topk_workspace(B, csa2::topk_plan(n_cap, k));
+    case CSA2_OP_DECODE:
+      if (pool && (pool->block < 1 || pool->block > kMaxBlock ||
+                   pool->n_blocks_keep < 1))
+        return 0;
+      return decode_layout(B, n_cap, k, pool).total;
+    case CSA2_OP_REUSE:
+      return csa2::attn_workspace(B, k);
+    default:
+      return 0;
+  }
+}
+
+csa2_status csa2_pack_kv(int32_t fmt, const float* src, int64_t n_rows,
+                         void* dst_codes, void* dst_scales, void* stream) {
+  if (fmt != CSA2_FMT_MAIN && fmt != CSA2_FMT_IDX && fmt != CSA2_FMT_SWA)
+    return fail(CSA2_ERR_INVALID_ARG, "unknown format %d", fmt);
+  if (n_rows < 0) return fail(CSA2_ERR_INVALID_ARG, "n_rows must be >= 0");
+  if (n_rows == 0) return CSA2_OK;
+  if (!src || !dst_codes)
+    return fail(CSA2_ERR_INVALID_ARG, "null src or dst_codes");
+  if (fmt == CSA2_FMT_SWA && dst_scales)
+    return fail(CSA2_ERR_INVALID_ARG, "CSA2_FMT_SWA has no scale plane");
+  if (fmt != CSA2_FMT_SWA && !dst_scales)
+    return fail(CSA2_ERR_INVALID_ARG, "null dst_scales");
+  if (!aligned(src, 16) || !aligned(dst_codes, 16))
+    return fail(CSA2_ERR_ALIGNMENT, "src and dst_codes need 16-byte alignment");
+  const int dim = fmt == CSA2_FMT_IDX ? 128 : 512;
+  const size_t cb = (size_t)n_rows * (fmt == CSA2_FMT_MAIN ? 256 : (fmt == CSA2_FMT_IDX ? 64 : 512));
+  const size_t sb = (size_t)n_rows * (fmt == CSA2_FMT_MAIN ? 32 : 4);
+  if (overlap(src, (size_t)n_rows * dim * 4, dst_codes, cb) ||
+      (dst_scales && overlap(src, (size_t)n_rows * dim * 4, dst_scales, sb)) ||
+      (dst_scales && overlap(dst_codes, cb, dst_scales, sb)))
+    return fail(CSA2_ERR_INVALID_ARG, "buffers overlap");
+  csa2_status st = need_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (fmt == CSA2_FMT_MAIN)
+    e = csa2::launch_pack_main(src, n_rows, static_cast<uint8_t*>(dst_codes),
+                               static_cast<uint8_t*>(dst_scales), s);
+  else if (fmt == CSA2_FMT_IDX)
+    e = csa2::launch_pack_idx(src, n_rows, static_cast<uint8_t*>(dst_codes),
+                              static_cast<uint8_t*>(dst_scales), s);
+  else
+    e = csa2::launch_pack_swa(src, n_rows, static_cast<uint8_t*>(dst_codes), s);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_pack_kv launch");
+}
+
+csa2_status csa2_unpack_kv(int32_t fmt, const void* codes, const void* scales,
+                           int64_t n_rows, float* dst, void* stream) {
+  if (fmt != CSA2_FMT_MAIN && fmt != CSA2_FMT_IDX && fmt != CSA2_FMT_SWA)
+    return fail(CSA2_ERR_INVALID_ARG, "unknown format %d", fmt);
+  if (n_rows < 0) return fail(CSA2_ERR_INVALID_ARG, "n_rows must be >= 0");
+  if (n_rows == 0) return CSA2_OK;
+  if (!codes || !dst || (fmt != CSA2_FMT_SWA && !scales))
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(dst, 8)) return fail(CSA2_ERR_ALIGNMENT, "dst needs 8-byte alignment");
+  csa2_status st = need_device();
+  if (st) return st;
+  hipError_t e = csa2::launch_unpack(fmt, static_cast<const uint8_t*>(codes),
+                                     static_cast<const uint8_t*>(scales),
+                                     n_rows, dst, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_unpack_kv launch");
+}
+
+csa2_status csa2_build_block_keys(const uint8_t* idx_codes,
+                                  const uint8_t* idx_scales, int64_t n_cap,
+                                  const int32_t* n_entries, int32_t B,
+                                  int32_t block, uint16_t* block_keys,
+                                  void* stream) {
+  if (B < 0 || n_cap < 0 || n_cap > kMaxCap)
+    return fail(CSA2_ERR_INVALID_ARG, "bad B or n_cap");
+  if (block < 1 || block > kMaxBlock)
+    return fail(CSA2_ERR_UNSUPPORTED, "block must be in 1..%d", kMaxBlock);
+  if (B == 0 || n_cap == 0) return CSA2_OK;
+  if (!idx_codes || !idx_scales || !n_entries || !block_keys)
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  csa2_status st = need_device();
+  if (st) return st;
+  hipError_t e = csa2::launch_block_keys(idx_codes, idx_scales, n_cap,
+                                         n_entries, B, block, block_keys,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_build_block_keys launch");
+}
+
+csa2_status csa2_indexer_score(int32_t keyfmt, const void* k_codes,
+                               const void* k_scales, int64_t n_cap,
+                               const int32_t* n_entries, const int32_t* cand,
+                               int32_t n_cand, const uint16_t* q_idx,
+                               const float* w, int32_t B, float* scores,
+                               void* stream) {
+  if (keyfmt != CSA2_KEYS_MXFP4 && keyfmt != CSA2_KEYS_BF16)
+    return fail(CSA2_ERR_INVALID_ARG, "unknown key format %d", keyfmt);
+  if (B < 0 || n_cap < 0 || n_cap > kMaxCap || (cand && n_cand < 0))
+    return fail(CSA2_ERR_INVALID_ARG, "bad B, n_cap or n_cand");
+  const int64_t rows = cand ? n_cand : n_cap;
+  if (B == 0 || rows == 0) return CSA2_OK;
+  if (!k_codes || !n_entries || !q_idx || !w || !scores)
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  if (keyfmt == CSA2_KEYS_MXFP4 && !k_scales)
+    return fail(CSA2_ERR_INVALID_ARG, "MXFP4 keys need k_scales");
+  if (keyfmt == CSA2_KEYS_BF16 && k_scales)
+    return fail(CSA2_ERR_INVALID_ARG, "bf16 keys take no k_scales");
+  if (!aligned(k_codes, 16) || !aligned(q_idx, 16) || !aligned(w, 4) ||
+      !aligned(scores, 4) || (k_scales && !aligned(k_scales, 4)))
+    return fail(CSA2_ERR_ALIGNMENT,
+                "k_codes and q_idx need 16-byte, k_scales, w, scores 4-byte "
+                "alignment");
+  const size_t kbytes = (size_t)B * n_cap * (keyfmt == CSA2_KEYS_MXFP4 ? 64 : 256);
+  if (overlap(scores, (size_t)B * rows * 4, k_codes, kbytes) ||
+      overlap(scores, (size_t)B * rows * 4, q_idx, (size_t)B * 32 * 128 * 2))
+    return fail(CSA2_ERR_INVALID_ARG, "scores overlap an input");
+  csa2_status st = need_device();
+  if (st) return st;
+  hipError_t e = csa2::launch_indexer(
+      keyfmt, k_codes, static_cast<const uint8_t*>(k_scales), n_cap, n_entries,
+      cand, rows, q_idx, w, B, scores, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_indexer_score launch");
+}
+
+csa2_status csa2_topk(const float* scores, int64_t ld, const int32_t* n_valid,
+                      const int32_t* ids, int32_t B, int32_t k, int32_t block,
+                      const int32_t* limit, int32_t* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (B < 0 || ld < 1 || ld > kMaxCap)
+    return fail(CSA2_ERR_INVALID_ARG, "bad B or ld");
+  if (k < 1 || k > kMaxK)
+    return fail(CSA2_ERR_UNSUPPORTED, "k must be in 1..%d (got %d)", kMaxK, k);
+  if (block < 1 || block > kMaxBlock)
+    return fail(CSA2_ERR_UNSUPPORTED, "block must be in 1..%d", kMaxBlock);
+  if (B == 0) return CSA2_OK;
+  if (!scores || !out) return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(scores, 4) || !aligned(out, 4))
+    return fail(CSA2_ERR_ALIGNMENT, "scores and out need 4-byte alignment");
+  const csa2::TopkPlan p = csa2::topk_plan(ld, k);
+  const size_t need = csa2::topk_workspace(B, p);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(CSA2_ERR_WORKSPACE, "topk needs %zu bytes of 256-byte aligned "
+                "workspace (got %zu)", need, ws_bytes);
+  if (overlap(out, (size_t)B * k * block * 4, scores, (size_t)B * ld * 4))
+    return fail(CSA2_ERR_INVALID_ARG, "out overlaps scores");
+  csa2_status st = need_device();
+  if (st) return st;
+  hipError_t e = csa2::launch_topk(scores, ld, n_valid, ids, B, k, block,
+                                   limit, out, ws, p,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_topk launch");
+}
+
+csa2_status csa2_reuse_attn(const uint8_t* main_codes,
+                            const uint8_t* main_scales, int64_t n_cap,
+                            const int32_t* topk, int32_t k, const uint16_t* q,
+                            const uint8_t* swa, const int32_t* n_swa,
+                            int32_t B, float scale, uint16_t* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  csa2_status st = check_attn_common(main_codes, main_scales, n_cap, q, swa,
+                                     n_swa, B, k, scale, out);
+  if (st) return st;
+  if (B == 0) return CSA2_OK;
+  if (!topk) return fail(CSA2_ERR_INVALID_ARG, "null topk");
+  const size_t need = csa2::attn_workspace(B, k);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(CSA2_ERR_WORKSPACE, "reuse needs %zu bytes of 256-byte aligned "
+                "workspace (got %zu)", need, ws_bytes);
+  st = need_device();
+  if (st) return st;
+  hipError_t e = csa2::launch_attn(main_codes, main_scales, n_cap, topk, k, q,
+                                   swa, n_swa, B, scale, out, ws,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_reuse_attn launch");
+}
+
+csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
+                                    const uint16_t* q_idx, const float* w,
+                                    const uint16_t* q, const uint8_t* swa,
+                                    const int32_t* n_swa, int32_t B, int32_t k,
+                                    float scale, const csa2_pool_opts* pool,
+                                    uint16_t* out, int32_t* topk_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (!kv) return fail(CSA2_ERR_INVALID_ARG, "null cache descriptor");
+  csa2_status st = check_attn_common(kv->main_codes, kv->main_scales,
+                                     kv->n_cap, q, swa, n_swa, B, k, scale, out);
+  if (st) return st;
+  st = check_pool(pool);
+  if (st) return st;
+  if (B == 0) return CSA2_OK;
+  if (kv->n_cap < 1) return fail(CSA2_ERR_INVALID_ARG, "n_cap must be >= 1");
+  if (!kv->idx_codes || !kv->idx_scales || !kv->n_entries || !q_idx || !w ||
+      !topk_out)
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  if (pool && !kv->block_keys)
+    return fail(CSA2_ERR_INVALID_ARG, "a pool needs kv->block_keys");
+  if (!aligned(kv->idx_codes, 16) || !aligned(kv->idx_scales, 4) ||
+      !aligned(q_idx, 16) || !aligned(w, 4) || !aligned(topk_out, 4) ||
+      (pool && !aligned(kv->block_keys, 16)))
+    return fail(CSA2_ERR_ALIGNMENT, "misaligned indexer argument");
+  const DecodeLayout L = decode_layout(B, kv->n_cap, k, pool);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(CSA2_ERR_WORKSPACE, "decode needs %zu bytes of 256-byte "
+                "aligned workspace (got %zu)", L.total, ws_bytes);
+  st = need_device();
+  if (st) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  hipError_t e;
+  if (!pool) {
+    float* scores = reinterpret_cast<float*>(base + L.off_scores);
+    e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
+                             kv->n_cap, kv->n_entries, nullptr, kv->n_cap,
+                             q_idx, w, B, scores, s);
+    if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    e = csa2::launch_topk(scores, kv->n_cap, kv->n_entries, nullptr, B, k, 1,
+                          nullptr, topk_out, base + L.off_topk, L.p1, s);
+    if (e != hipSuccess) return hip_fail(e, "topk launch");
+  } else {
+    int32_t* nblk = reinterpret_cast<int32_t*>(base + L.off_nblk);
+    float* bscores = reinterpret_cast<float*>(base + L.off_bscores);
+    int32_t* pool_ids = reinterpret_cast<int32_t*>(base + L.off_pool);
+    float* pscores = reinterpret_cast<float*>(base + L.off_pscores);
+    e = csa2::launch_nblocks(kv->n_entries, B, pool->block, nblk, s);
+    if (e != hipSuccess) return hip_fail(e, "block count launch");
+    e = csa2::launch_indexer(CSA2_KEYS_BF16, kv->block_keys, nullptr, L.nb,
+                             nblk, nullptr, L.nb, q_idx, w, B, bscores, s);
+    if (e != hipSuccess) return hip_fail(e, "block indexer launch");
+    e = csa2::launch_topk(bscores, L.nb, nblk, nullptr, B, L.kb, pool->block,
+                          kv->n_entries, pool_ids, base + L.off_topk, L.p1, s);
+    if (e != hipSuccess) return hip_fail(e, "block topk launch");
+    e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
+                             kv->n_cap, kv->n_entries, pool_ids, L.n_cand,
+                             q_idx, w, B, pscores, s);
+    if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
+    e = csa2::launch_topk(pscores, L.n_cand, nullptr, pool_ids, B, k, 1,
+                          nullptr, topk_out, base + L.off_topk, L.p2, s);
+    if (e != hipSuccess) return hip_fail(e, "pool topk launch");
+  }
+  e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
+                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return CSA2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Device-side types and helpers shared by the libcsa2 kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMainDim = 512;     // main latent width
+constexpr int kMainCodeBytes = 256;
+constexpr int kMainScaleBytes = 32;
+constexpr int kIdxDim = 128;      // indexer head width
+constexpr int kIdxCodeBytes = 64;
+constexpr int kIdxScaleBytes = 4;
+constexpr int kIdxHeads = 32;
+constexpr int kHeads = 64;        // attention query heads
+constexpr int kWindow = 128;      // sliding-window rows per sequence
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+// E8M0 code -> float32 2^(c-127) (code 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  return c == 0 ? u2f(0x00400000u) : u2f(c << 23);
+}
+
+// Bit-reinterpret helpers between packed bf16 pairs and uint32.
+__device__ __forceinline__ uint32_t bf2_bits(bf16x2 v) {
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16x8 bits_to_bf8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Order-preserving map float32 -> uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = f2u(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return u2f((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+}  // namespace csa2

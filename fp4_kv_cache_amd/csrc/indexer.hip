@@ -1,0 +1,211 @@
+// Lightning-indexer scan: I_j = sum_{h<32} w_h * ReLU(q_h . K_j).
+//
+// Source: "DeepSeek-V4: Towards Highly Efficient Million-Token Context
+// Intelligence" (baisen.site), CSA step 2, index-score equation; the same
+// form in "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression"
+// (mer.run) section 4.1.  Keys are OCP MXFP4 (E2M1 + E8M0 per 32), section 2
+// of the latter page; the pooled block keys of its section 4.3 are bf16.
+//
+// gfx950 mapping.  One wavefront scores 32 entries per step with the bf16
+// matrix core (v_mfma_f32_32x32x16_bf16, 8 issues for the 128-dim dot):
+// A = the 32 query heads (held in VGPRs for the whole scan), B = 32 keys
+// dequantised in registers from their FP4 codes with the packed
+// scale-convert (E2M1 x 2^e is exact in bf16, so every product is exact and
+// only the float32 accumulation rounds).  The dot product does not depend on
+// the order of its terms, so lane half h of the wave takes dims
+// 64h .. 64h+63 of its key: each lane streams one contiguous 32-byte run of
+// codes (two 16-byte loads) and the query is permuted the same way.  The
+// accumulator comes out head-major (16 heads per lane); ReLU, the head
+// weights and the head sum are applied per lane and the two lane halves are
+// folded with one cross-half swap.  HBM traffic per entry: 64 + 4 bytes
+// read, 4 bytes of score written.
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTilesPerWave = 8;    // 32-entry tiles per wavefront
+constexpr int kEntriesPerBlock = kWaves * kTilesPerWave * 32;
+
+// Raw key data one lane holds for one 32-entry tile.
+template <int KEYFMT> struct RawKey;
+template <> struct RawKey<0> {       // MXFP4: 32 code bytes + 2 scale bytes
+  u32x4 c0, c1;
+  uint32_t sc;
+};
+template <> struct RawKey<1> {       // bf16: 64 dims = 128 bytes
+  u32x4 v[8];
+};
+
+template <int KEYFMT>
+__device__ __forceinline__ void load_key(RawKey<KEYFMT>& r, const void* codes,
+                                         const uint8_t* scales, int64_t row,
+                                         int half, bool valid);
+
+template <>
+__device__ __forceinline__ void load_key<0>(RawKey<0>& r, const void* codes,
+                                            const uint8_t* scales, int64_t row,
+                                            int half, bool valid) {
+  if (valid) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(
+        static_cast<const uint8_t*>(codes) + row * 64 + 32 * half);
+    r.c0 = p[0];
+    r.c1 = p[1];
+    r.sc = *reinterpret_cast<const uint32_t*>(scales + row * 4);
+  } else {
+    r.c0 = u32x4{0, 0, 0, 0};
+    r.c1 = u32x4{0, 0, 0, 0};
+    r.sc = 0x7F7F7F7Fu;
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_key<1>(RawKey<1>& r, const void* codes,
+                                            const uint8_t*, int64_t row,
+                                            int half, bool valid) {
+  if (valid) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(codes) + row * 128 + 64 * half);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.v[s] = p[s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.v[s] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// B operand of step s: 8 dims 64h + 8s .. +7 of this lane's key, as bf16.
+template <int KEYFMT>
+__device__ __forceinline__ bf16x8 key_operand(const RawKey<KEYFMT>& r, int s,
+                                              int half);
+
+template <>
+__device__ __forceinline__ bf16x8 key_operand<0>(const RawKey<0>& r, int s,
+                                                 int half) {
+  const uint32_t cw = s < 4 ? r.c0[s] : r.c1[s - 4];
+  const uint32_t sbyte = (r.sc >> (8 * (2 * half + (s >> 2)))) & 0xFFu;
+  const float sf = e8m0_to_f32(sbyte);
+  u32x4 o;
+  o[0] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 0));
+  o[1] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 1));
+  o[2] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 2));
+  o[3] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 3));
+  return bits_to_bf8(o);
+}
+
+template <>
+__device__ __forceinline__ bf16x8 key_operand<1>(const RawKey<1>& r, int s,
+                                                 int) {
+  return bits_to_bf8(r.v[s]);
+}
+
+// Row id and validity of tile position i of sequence b.
+__device__ __forceinline__ int64_t row_of(const int32_t* cand, int64_t n_rows,
+                                          int64_t n, int b, int64_t i,
+                                          bool& valid) {
+  if (cand == nullptr) {
+    valid = i < n;
+    return i;
+  }
+  int64_t e = -1;
+  if (i < n_rows) e = cand[(int64_t)b * n_rows + i];
+  valid = e >= 0 && e < n;
+  return e;
+}
+
+template <int KEYFMT>
+__global__ __launch_bounds__(256) void indexer_kernel(
+    const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    int64_t n_cap, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ cand, int64_t n_rows,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    float* __restrict__ scores) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  int64_t n = n_entries[b];
+  n = n < 0 ? 0 : (n > n_cap ? n_cap : n);        // never past the cache
+  const int64_t seq_base = (int64_t)b * n_cap;
+
+  // A operand: head `col`, dims 64*half + 8*s .. +7 for step s.
+  bf16x8 qa[8];
+  const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
+      q_idx + ((int64_t)b * kIdxHeads + col) * kIdxDim + 64 * half);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qa[s] = qrow[s];
+  // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
+  float wr[16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      wr[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 * half + r];
+
+  const int64_t base =
+      ((int64_t)blockIdx.x * kWaves + wave) * (kTilesPerWave * 32);
+  if (base >= n_rows) return;
+  // Rows past the visible range need no loads at all.
+  const int64_t scan_end = cand ? n_rows : (n < n_rows ? n : n_rows);
+
+  RawKey<KEYFMT> cur, nxt;
+  {
+    bool v;
+    const int64_t e = row_of(cand, n_rows, n, b, base + col, v);
+    load_key<KEYFMT>(cur, k_codes, k_scales, seq_base + e, half, v);
+  }
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    const int64_t tile = base + 32 * t;
+    if (tile >= n_rows) break;                       // wave-uniform
+    const int64_t i = tile + col;
+    bool valid;
+    row_of(cand, n_rows, n, b, i, valid);
+    // Prefetch the next tile before this one's matrix work.
+    if (t + 1 < kTilesPerWave && tile + 32 < scan_end) {
+      bool v2;
+      const int64_t e2 = row_of(cand, n_rows, n, b, i + 32, v2);
+      load_key<KEYFMT>(nxt, k_codes, k_scales, seq_base + e2, half, v2);
+    }
+    float total = -__builtin_inff();
+    if (tile < scan_end) {                           // wave-uniform
+      f32x16 acc = {};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            qa[s], key_operand<KEYFMT>(cur, s, half), acc, 0, 0, 0);
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) part += wr[j] * fmaxf(acc[j], 0.0f);
+      const float sum = part + __shfl_xor(part, 32);
+      if (valid) total = sum;
+    }
+    if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total;
+    cur = nxt;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer(int keyfmt, const void* k_codes,
+                          const uint8_t* k_scales, int64_t n_cap,
+                          const int32_t* n_entries, const int32_t* cand,
+                          int64_t n_rows, const uint16_t* q_idx,
+                          const float* w, int B, float* scores, hipStream_t s) {
+  if (n_rows == 0 || B == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_rows + kEntriesPerBlock - 1) / kEntriesPerBlock),
+                  (unsigned)B);
+  if (keyfmt == 0)
+    hipLaunchKernelGGL(indexer_kernel<0>, grid, dim3(256), 0, s, k_codes,
+                       k_scales, n_cap, n_entries, cand, n_rows, q_idx, w,
+                       scores);
+  else
+    hipLaunchKernelGGL(indexer_kernel<1>, grid, dim3(256), 0, s, k_codes,
+                       k_scales, n_cap, n_entries, cand, n_rows, q_idx, w,
+                       scores);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,57 @@
+// Host-side launchers behind the C ABI (enqueue only; arguments validated
+// by the caller in api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// pack.hip
+hipError_t launch_pack_main(const float* src, int64_t n, uint8_t* codes,
+                            uint8_t* scales, hipStream_t s);
+hipError_t launch_pack_idx(const float* src, int64_t n, uint8_t* codes,
+                           uint8_t* scales, hipStream_t s);
+hipError_t launch_pack_swa(const float* src, int64_t n, uint8_t* codes,
+                           hipStream_t s);
+hipError_t launch_unpack(int fmt, const uint8_t* codes, const uint8_t* scales,
+                         int64_t n, float* dst, hipStream_t s);
+hipError_t launch_block_keys(const uint8_t* codes, const uint8_t* scales,
+                             int64_t n_cap, const int32_t* n_entries, int B,
+                             int block, uint16_t* keys, hipStream_t s);
+hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
+                          int32_t* nblk, hipStream_t s);
+
+// indexer.hip
+hipError_t launch_indexer(int keyfmt, const void* k_codes,
+                          const uint8_t* k_scales, int64_t n_cap,
+                          const int32_t* n_entries, const int32_t* cand,
+                          int64_t n_rows, const uint16_t* q_idx,
+                          const float* w, int B, float* scores, hipStream_t s);
+
+// topk.hip
+struct TopkPlan {
+  int64_t ld;          // row length
+  int k;
+  int chunk;           // elements per first-stage segment
+  int n_stages;        // 1 = single pass
+  int segs[8];         // segments per row at each stage
+  int64_t len[8];      // row length at each stage
+};
+TopkPlan topk_plan(int64_t ld, int k);
+size_t topk_workspace(int B, const TopkPlan& p);
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
+                       const int32_t* ids, int B, int k, int block,
+                       const int32_t* limit, int32_t* out, void* ws,
+                       const TopkPlan& p, hipStream_t s);
+
+// attn.hip
+int attn_splits(int B, int k);
+size_t attn_workspace(int B, int k);
+hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
+                       int64_t n_cap, const int32_t* topk, int k,
+                       const uint16_t* q, const uint8_t* swa,
+                       const int32_t* n_swa, int B, float scale,
+                       uint16_t* out, void* ws, hipStream_t s);
+
+}  // namespace csa2

@@ -1,0 +1,48 @@
+"""Shared helpers of the GPU parity tests (not collected by pytest)."""
+import numpy as np
+import torch
+
+from oracle import csa2 as O
+
+REL_L2_TOL = 5e-3          # attention output vs the float64 oracle
+GAP_TOL = 1e-5             # top-k near-tie band (relative)
+SCORE_RTOL = 2e-6          # float32-accumulated scores vs float64
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def bf16_bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def topk_set_ok(gpu_ids, ref_scores, k, ids=None):
+    """The gap rule for one row: with s_(k) the oracle's k-th score, the GPU
+    set must contain every id scoring above s_(k)(1 + tol) and only ids
+    scoring at least s_(k)(1 - tol); when the (k, k+1) gap is >= tol it must
+    equal the oracle's set.  Returns (ok, message)."""
+    s = np.asarray(ref_scores, np.float64)
+    ids = np.arange(len(s)) if ids is None else np.asarray(ids)
+    g = np.asarray(gpu_ids)
+    g = g[g >= 0]
+    want = O.topk(s, k, ids)
+    want = want[want >= 0]
+    if len(g) != len(want):
+        return False, f"size {len(g)} != {len(want)}"
+    if np.array_equal(np.sort(g), want):
+        return True, "equal"
+    gap = O.topk_gap(s, k)
+    if gap >= GAP_TOL:
+        return False, f"sets differ with gap {gap:.3g}"
+    pos = {int(i): j for j, i in enumerate(ids)}
+    sg = np.array([s[pos[int(i)]] for i in g])
+    kth = np.sort(s)[::-1][k - 1]
+    must = ids[s > kth * (1 + GAP_TOL)]
+    if not set(must.tolist()) <= set(g.tolist()):
+        return False, "missing a clear winner"
+    if np.any(sg < kth * (1 - GAP_TOL)):
+        return False, "contains a clear loser"
+    return True, f"near-tie (gap {gap:.3g})"

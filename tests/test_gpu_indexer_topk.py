@@ -1,0 +1,141 @@
+"""GPU indexer scores and top-k against the oracle.
+
+Scores: float32 accumulation of exact products, compared with the float64
+oracle at a relative tolerance far inside the 1e-5 top-k gap band.
+Top-k: both sides select over the SAME float32 score values, so the chosen
+ids must be identical (ties included)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa2 as O
+from oracle import formats as F
+from fp4_kv_cache_amd import csa2
+from _util import SCORE_RTOL, bf16_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _keys(B, n_cap, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B * n_cap, 128)).astype(np.float32)
+    c, s = csa2.pack_kv(csa2.FMT_IDX, torch.from_numpy(x).to(DEV))
+    return c.view(B, n_cap, 64), s.view(B, n_cap, 4)
+
+
+def _query(B, seed):
+    rng = np.random.default_rng(seed)
+    q = torch.from_numpy(rng.standard_normal((B, 32, 128)).astype(np.float32))
+    w = torch.from_numpy(rng.uniform(0, 1, (B, 32)).astype(np.float32))
+    return q.to(torch.bfloat16).to(DEV), w.to(DEV)
+
+
+def _ref_scores(c, s, qi, w, b, rows):
+    keys = O.unpack_idx(c[b, rows], s[b, rows])
+    return O.indexer_scores(bf16_bits(qi[b]), w[b].cpu().numpy(), keys)
+
+
+def test_indexer_scores_ragged():
+    B, n_cap = 4, 3000 + 17
+    c, s = _keys(B, n_cap, 0)
+    qi, w = _query(B, 1)
+    n_entries = [n_cap, 1234, 1, 0]
+    ne = torch.tensor(n_entries, dtype=torch.int32, device=DEV)
+    sc = csa2.indexer_score(csa2.KEYS_MXFP4, c, s, ne, qi, w).cpu().numpy()
+    cc, ss = c.cpu().numpy(), s.cpu().numpy()
+    for b in range(B):
+        n = n_entries[b]
+        if n:
+            ref = _ref_scores(cc, ss, qi, w, b, np.arange(n))
+            np.testing.assert_allclose(sc[b, :n], ref, rtol=SCORE_RTOL,
+                                       atol=1e-4)
+        assert np.all(np.isneginf(sc[b, n:]))
+
+
+def test_indexer_candidates_and_bf16_keys():
+    B, n_cap = 2, 2048
+    c, s = _keys(B, n_cap, 2)
+    qi, w = _query(B, 3)
+    ne = torch.tensor([n_cap, 1500], dtype=torch.int32, device=DEV)
+    rng = np.random.default_rng(4)
+    cand = rng.integers(-5, n_cap + 5, (B, 700)).astype(np.int32)
+    sc = csa2.indexer_score(csa2.KEYS_MXFP4, c, s, ne, qi, w,
+                            cand=torch.from_numpy(cand).to(DEV)).cpu().numpy()
+    cc, ss = c.cpu().numpy(), s.cpu().numpy()
+    for b, n in enumerate([n_cap, 1500]):
+        ok = (cand[b] >= 0) & (cand[b] < n)
+        ref = _ref_scores(cc, ss, qi, w, b, cand[b][ok])
+        np.testing.assert_allclose(sc[b][ok], ref, rtol=SCORE_RTOL, atol=1e-4)
+        assert np.all(np.isneginf(sc[b][~ok]))
+    # bf16 block keys
+    bk = torch.from_numpy(rng.standard_normal((B, 300, 128)).astype(
+        np.float32)).to(torch.bfloat16).to(DEV)
+    nb = torch.tensor([300, 77], dtype=torch.int32, device=DEV)
+    sb = csa2.indexer_score(csa2.KEYS_BF16, bk, None, nb, qi, w).cpu().numpy()
+    for b, n in enumerate([300, 77]):
+        ref = O.indexer_scores(bf16_bits(qi[b]), w[b].cpu().numpy(),
+                               F.bf16_bits_to_f64(bf16_bits(bk[b, :n])))
+        np.testing.assert_allclose(sb[b, :n], ref, rtol=SCORE_RTOL, atol=1e-4)
+        assert np.all(np.isneginf(sb[b, n:]))
+
+
+@pytest.mark.parametrize("ld,k", [(1024, 512), (5000, 1), (40000, 512),
+                                  (70000, 2048), (16384, 7)])
+def test_topk_exact_vs_oracle(ld, k):
+    rng = np.random.default_rng(ld + k)
+    B = 3
+    sc = rng.standard_normal((B, ld)).astype(np.float32)
+    sc[1] = np.round(sc[1] * 4) / 4          # heavy ties
+    sc[2, ::7] = -np.inf                     # invalid entries
+    sc[2, 3] = np.nan
+    nv = [ld, ld - 123, max(1, ld // 3)]
+    out = csa2.topk(torch.from_numpy(sc).to(DEV), k,
+                    n_valid=torch.tensor(nv, dtype=torch.int32, device=DEV))
+    out = out.cpu().numpy()
+    for b in range(B):
+        s = sc[b, :nv[b]].astype(np.float64)
+        ok = np.isfinite(s)
+        ref = O.topk(s[ok], k, ids=np.arange(nv[b])[ok])
+        assert np.array_equal(out[b], ref), b
+
+
+def test_topk_all_equal_and_short_rows():
+    sc = np.zeros((2, 3000), np.float32)
+    sc[1, :] = 5.0
+    nv = torch.tensor([3000, 100], dtype=torch.int32, device=DEV)
+    out = csa2.topk(torch.from_numpy(sc).to(DEV), 512, n_valid=nv).cpu().numpy()
+    assert out[0].tolist() == list(range(512))
+    assert out[1, :100].tolist() == list(range(100))
+    assert np.all(out[1, 100:] == -1)
+
+
+def test_topk_ids_and_block_expansion():
+    rng = np.random.default_rng(9)
+    B, ld, kb, blk = 2, 20000, 300, 8
+    sc = rng.standard_normal((B, ld)).astype(np.float32)
+    limit = [ld * blk - 5, 8 * 1000 + 3]
+    nv = [ld, 1001]
+    out = csa2.topk(torch.from_numpy(sc).to(DEV), kb,
+                    n_valid=torch.tensor(nv, dtype=torch.int32, device=DEV),
+                    block=blk,
+                    limit=torch.tensor(limit, dtype=torch.int32, device=DEV))
+    out = out.cpu().numpy()
+    for b in range(B):
+        blocks = O.topk(sc[b, :nv[b]].astype(np.float64), kb)
+        blocks = blocks[blocks >= 0]
+        pos = (blocks[:, None] * blk + np.arange(blk)).reshape(-1)
+        want = np.where(pos < limit[b], pos, -1)
+        assert np.array_equal(out[b, :len(want)], want)
+        assert np.all(out[b, len(want):] == -1)
+    # explicit ids (ascending with -1 holes), reported instead of positions
+    ids = np.sort(rng.choice(10 ** 6, (B, 5000), replace=False), axis=1)
+    ids = ids.astype(np.int32)
+    ids[:, -40:] = -1
+    sc2 = rng.standard_normal((B, 5000)).astype(np.float32)
+    out2 = csa2.topk(torch.from_numpy(sc2).to(DEV), 512,
+                     ids=torch.from_numpy(ids).to(DEV)).cpu().numpy()
+    for b in range(B):
+        ok = ids[b] >= 0
+        ref = O.topk(sc2[b][ok].astype(np.float64), 512, ids=ids[b][ok])
+        assert np.array_equal(out2[b], ref)
