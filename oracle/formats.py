@@ -52,8 +52,8 @@ def e2m1_encode(r):
     a = np.abs(r)
     # The midpoints between consecutive magnitudes.
     mids = (E2M1_MAGNITUDES[:-1] + E2M1_MAGNITUDES[1:]) / 2.0
-    above = (a[..., None] > mids).sum(axis=-1)      # code if no tie
-    tie = (a[..., None] == mids).any(axis=-1)
+    above = np.searchsorted(mids, a, side="left")   # midpoints below a
+    tie = mids[np.minimum(above, len(mids) - 1)] == a
     code = np.where(tie & (above % 2 == 1), above + 1, above)
     sign = np.signbit(r).astype(np.int64) << 3
     return (code | sign).astype(np.uint8)
