@@ -176,11 +176,15 @@ def build_block_keys(idx_codes, idx_scales, n_entries, block=8):
     return out
 
 
-def indexer_score(keyfmt, k_codes, k_scales, n_entries, q_idx, w, cand=None):
+def indexer_score(keyfmt, k_codes, k_scales, n_entries, q_idx, w, cand=None,
+                  out=None):
     """Scores [B, n_cap] (or [B, n_cand] for candidate ids)."""
     B, n_cap = k_codes.shape[0], k_codes.shape[1]
     rows = n_cap if cand is None else cand.shape[1]
-    out = torch.empty((B, rows), dtype=torch.float32, device=k_codes.device)
+    if out is None:
+        out = torch.empty((B, rows), dtype=torch.float32,
+                          device=k_codes.device)
+    _need(out, torch.float32, (B, rows), "out")
     _check(load().csa2_indexer_score(
         keyfmt, _ptr(k_codes), _ptr(k_scales), n_cap, _ptr(n_entries),
         _ptr(cand), 0 if cand is None else cand.shape[1], _ptr(q_idx),
@@ -188,9 +192,13 @@ def indexer_score(keyfmt, k_codes, k_scales, n_entries, q_idx, w, cand=None):
     return out
 
 
-def topk(scores, k, n_valid=None, ids=None, block=1, limit=None, ws=None):
+def topk(scores, k, n_valid=None, ids=None, block=1, limit=None, ws=None,
+         out=None):
     B, ld = scores.shape
-    out = torch.empty((B, k * block), dtype=torch.int32, device=scores.device)
+    if out is None:
+        out = torch.empty((B, k * block), dtype=torch.int32,
+                          device=scores.device)
+    _need(out, torch.int32, (B, k * block), "out")
     need = workspace_size(OP_TOPK, B, ld, k)
     if ws is None:
         ws = workspace(need, scores.device)

@@ -57,22 +57,22 @@ struct DecodeLayout {
   bool pool;
   int64_t nb = 0, n_cand = 0;
   int kb = 0;
-  size_t off_scores = 0, off_nblk = 0, off_bscores = 0, off_pool = 0,
-         off_pscores = 0, off_topk = 0, off_attn = 0, total = 0;
-  csa2::TopkPlan p1{}, p2{};
+  size_t off_scores = 0, off_tmax = 0, off_nblk = 0, off_bscores = 0,
+         off_pool = 0, off_pscores = 0, off_attn = 0, total = 0;
 };
+
+inline size_t tiles_of(int64_t rows) { return (size_t)((rows + 31) / 32); }
 
 DecodeLayout decode_layout(int B, int64_t n_cap, int k,
                            const csa2_pool_opts* pool) {
   DecodeLayout L;
   L.pool = pool != nullptr;
   size_t off = 0;
-  size_t tk = 0;
   if (!L.pool) {
     L.off_scores = off;
     off += align256((size_t)B * n_cap * 4);
-    L.p1 = csa2::topk_plan(n_cap, k);
-    tk = csa2::topk_workspace(B, L.p1);
+    L.off_tmax = off;
+    off += align256((size_t)B * tiles_of(n_cap) * 4);
   } else {
     L.nb = (n_cap + pool->block - 1) / pool->block;
     L.kb = (int)std::min<int64_t>(pool->n_blocks_keep, L.nb);
@@ -86,12 +86,9 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     off += align256((size_t)B * L.n_cand * 4);
     L.off_pscores = off;
     off += align256((size_t)B * L.n_cand * 4);
-    L.p1 = csa2::topk_plan(L.nb, L.kb);
-    L.p2 = csa2::topk_plan(L.n_cand, k);
-    tk = std::max(csa2::topk_workspace(B, L.p1), csa2::topk_workspace(B, L.p2));
+    L.off_tmax = off;
+    off += align256((size_t)B * std::max(tiles_of(L.nb), tiles_of(L.n_cand)) * 4);
   }
-  L.off_topk = off;
-  off += align256(tk);
   L.off_attn = off;
   off += align256(csa2::attn_workspace(B, k));
   L.total = off;
@@ -170,7 +167,7 @@ size_t csa2_workspace_size(int32_t op, int32_t B, int64_t n_cap, int32_t k,
   if (B < 0 || n_cap < 0 || n_cap > kMaxCap || k < 1 || k > kMaxK) return 0;
   switch (op) {
     case CSA2_OP_TOPK:
-      return csa2::topk_workspace(B, csa2::topk_plan(n_cap, k));
+      return csa2::topk_workspace(B, n_cap);
     case CSA2_OP_DECODE:
       if (pool && (pool->block < 1 || pool->block > kMaxBlock ||
                    pool->n_blocks_keep < 1))
@@ -305,8 +302,7 @@ csa2_status csa2_topk(const float* scores, int64_t ld, const int32_t* n_valid,
   if (!scores || !out) return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(scores, 4) || !aligned(out, 4))
     return fail(CSA2_ERR_ALIGNMENT, "scores and out need 4-byte alignment");
-  const csa2::TopkPlan p = csa2::topk_plan(ld, k);
-  const size_t need = csa2::topk_workspace(B, p);
+  const size_t need = csa2::topk_workspace(B, ld);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
     return fail(CSA2_ERR_WORKSPACE, "topk needs %zu bytes of 256-byte aligned "
                 "workspace (got %zu)", need, ws_bytes);
@@ -315,7 +311,7 @@ csa2_status csa2_topk(const float* scores, int64_t ld, const int32_t* n_valid,
   csa2_status st = need_device();
   if (st) return st;
   hipError_t e = csa2::launch_topk(scores, ld, n_valid, ids, B, k, block,
-                                   limit, out, ws, p,
+                                   limit, out, ws,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_topk launch");
 }
@@ -377,15 +373,16 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   hipError_t e;
+  float* tmax = reinterpret_cast<float*>(base + L.off_tmax);
   if (!pool) {
     float* scores = reinterpret_cast<float*>(base + L.off_scores);
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, nullptr, kv->n_cap,
-                             q_idx, w, B, scores, s);
+                             q_idx, w, B, scores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
-    e = csa2::launch_topk(scores, kv->n_cap, kv->n_entries, nullptr, B, k, 1,
-                          nullptr, topk_out, base + L.off_topk, L.p1, s);
-    if (e != hipSuccess) return hip_fail(e, "topk launch");
+    e = csa2::launch_row_select(scores, tmax, kv->n_cap, kv->n_entries,
+                                nullptr, B, k, 1, nullptr, topk_out, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
   } else {
     int32_t* nblk = reinterpret_cast<int32_t*>(base + L.off_nblk);
     float* bscores = reinterpret_cast<float*>(base + L.off_bscores);
@@ -394,18 +391,19 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
     e = csa2::launch_nblocks(kv->n_entries, B, pool->block, nblk, s);
     if (e != hipSuccess) return hip_fail(e, "block count launch");
     e = csa2::launch_indexer(CSA2_KEYS_BF16, kv->block_keys, nullptr, L.nb,
-                             nblk, nullptr, L.nb, q_idx, w, B, bscores, s);
+                             nblk, nullptr, L.nb, q_idx, w, B, bscores, s,
+                             tmax);
     if (e != hipSuccess) return hip_fail(e, "block indexer launch");
-    e = csa2::launch_topk(bscores, L.nb, nblk, nullptr, B, L.kb, pool->block,
-                          kv->n_entries, pool_ids, base + L.off_topk, L.p1, s);
-    if (e != hipSuccess) return hip_fail(e, "block topk launch");
+    e = csa2::launch_row_select(bscores, tmax, L.nb, nblk, nullptr, B, L.kb,
+                                pool->block, kv->n_entries, pool_ids, s);
+    if (e != hipSuccess) return hip_fail(e, "block top-k launch");
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, pool_ids, L.n_cand,
-                             q_idx, w, B, pscores, s);
+                             q_idx, w, B, pscores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
-    e = csa2::launch_topk(pscores, L.n_cand, nullptr, pool_ids, B, k, 1,
-                          nullptr, topk_out, base + L.off_topk, L.p2, s);
-    if (e != hipSuccess) return hip_fail(e, "pool topk launch");
+    e = csa2::launch_row_select(pscores, tmax, L.n_cand, nullptr, pool_ids,
+                                B, k, 1, nullptr, topk_out, s);
+    if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
   }
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
                         k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);

@@ -16,17 +16,28 @@
 // k..k+127 the window rows); wavefront w owns heads 16w..16w+15 with its
 // queries resident in VGPRs.  Key tiles of 32 slots are gathered straight
 // from HBM (one 256-byte code row per wavefront instruction), dequantised
-// exactly to bf16 and written to LDS twice: key-major for S^T = K Q^T and,
+// exactly to fp16 and written to LDS twice: key-major for S^T = K Q^T and,
 // through a register transpose, slot-grouped for O^T = V^T P^T, so both
-// products run on v_mfma_f32_16x16x32_bf16 with all operands read as
-// 16-byte LDS vectors (XOR-swizzled, bank-conflict free).  The S^T output
-// layout equals the P^T operand layout, so probabilities never leave
-// registers.  Softmax is online in float32 with the exp2 reference point
-// moved only when the tile maximum rises by more than 2^8 (exact algebra,
-// fewer rescales).  LDS is double buffered: the gather of tile t+1 is in
-// flight while tile t runs on the matrix cores.  With several workgroups
-// per sequence, un-normalised partials (m, l, O) are merged by a second
-// kernel.
+// products run on v_mfma_f32_16x16x32_f16 with all operands read as 16-byte
+// LDS vectors (XOR-swizzled, bank-conflict free).
+//
+// Why fp16: an E2M1 value times an E4M3 scale has at most 6 significant
+// bits and lies in [2^-10, 2688], so it is exact in fp16, and the scale
+// multiply is one packed fp16 multiply after the FP4->fp16 convert (the
+// hardware convert applies only the exponent of its scale operand).  E4M3
+// window values are exact in fp16 too.  The bf16 queries are converted to
+// fp16 once (exact for |q| >= 2^-14; below that the absolute error is under
+// 2^-25), and probabilities in fp16 keep 11 significant bits.
+//
+// The S^T output layout equals the P^T operand layout, so probabilities never
+// leave registers.  Softmax is online in float32 with the exp2 reference
+// point moved only when the tile maximum rises by more than 2^8 (exact
+// algebra, fewer rescales).  LDS is double buffered: the gather of tile t+1
+// is in flight while tile t runs on the matrix cores.  With several
+// workgroups per sequence, each writes its output normalised by its own sum
+// (fp16, plus its max and sum in float32) and a second kernel merges them;
+// the workgroups of one sequence are placed on one XCD so the query reads
+// and the partials stay in that XCD's L2.
 #include "common.h"
 #include "internal.h"
 
@@ -34,7 +45,7 @@ namespace csa2 {
 namespace {
 
 constexpr int kTile = 32;                   // key slots per tile
-constexpr int kKtStride = 520;              // bf16 per Kt row (+16 B pad)
+constexpr int kKtStride = 520;              // fp16 per Kt row (+16 B pad)
 constexpr int kKtElems = kTile * kKtStride;
 constexpr int kVsElems = 4 * 512 * 8;
 constexpr int kBufElems = kKtElems + kVsElems;
@@ -42,17 +53,15 @@ constexpr int kSmemBytes = 2 * kBufElems * 2 + 2 * kTile * 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;       // log2 units
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t x) {
-  const uint32_t s = (x & 0x80u) << 8;
-  const uint32_t e = (x >> 3) & 15u, m = x & 7u;
-  if (e) return s | ((e + 120u) << 7) | (m << 4);
-  return s | (f2u((float)m * 0.001953125f) >> 16);
+__device__ __forceinline__ uint32_t f16x2_bits(f16x2_t v) {
+  return __builtin_bit_cast(uint32_t, v);
 }
-
-__device__ __forceinline__ float e4m3_to_f32_fast(uint32_t x) {
-  return u2f(e4m3_to_bf16_bits(x) << 16);
+__device__ __forceinline__ f16x2_t bits_f16x2(uint32_t v) {
+  return __builtin_bit_cast(f16x2_t, v);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -74,8 +83,9 @@ struct AttnArgs {
   const int32_t* n_swa;
   float scale_log2;        // scale * log2(e)
   uint16_t* out;           // final output when splits == 1
-  float* part_o;           // [B][S][64][512]
-  float* part_ml;          // [B][S][64][2]
+  uint16_t* part_o;        // [B][S][64][512] fp16, normalised per split
+  float* part_ml;          // [B][S][64][2] (max in log2 units, sum)
+  int B;
   int splits;
   int tiles_per_split;
   int n_tiles;
@@ -87,79 +97,74 @@ struct Raw {
   uint32_t c[8];
 };
 
-// Slot kind: 0 empty, 1 main entry, 2 window row.
-__device__ __forceinline__ int slot_kind(const AttnArgs& p, int b, int slot,
-                                         int nswa, int64_t& row) {
-  if (slot < p.k) {
-    const int id = p.topk[(int64_t)b * p.k + slot];
-    row = id;
-    return (id >= 0 && id < p.n_cap) ? 1 : 0;
-  }
-  const int r = slot - p.k;
-  row = r;
-  return r < nswa ? 2 : 0;
-}
-
+// Gather the raw bytes of the 8 slots this lane dequantises in one tile
+// (wavefront `quarter` owns slots {4q..4q+3, 16+4q..16+4q+3}, lane g owns
+// dims 8g..8g+7).  All top-k ids are loaded first and every data load uses
+// a clamped (always valid) row, so no load waits on another; `kinds` records
+// per slot 0 = empty, 1 = main entry, 2 = window row.
 __device__ __forceinline__ void gather(const AttnArgs& p, int b, int tile,
                                        int quarter, int g, int nswa, Raw& raw,
                                        uint32_t& kinds) {
+  int32_t idv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
+    const int slot = tile * kTile + j;
+    idv[e] = p.topk[(int64_t)b * p.k + (slot < p.k ? slot : 0)];
+  }
   kinds = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
     const int slot = tile * kTile + j;
-    int64_t row = 0;
-    const int kind = slot_kind(p, b, slot, nswa, row);
-    kinds |= (uint32_t)kind << (2 * e);
-    raw.a[e] = 0;
-    raw.c[e] = 0;
-    if (kind == 1) {
-      const int64_t r = (int64_t)b * p.n_cap + row;
+    if (slot < p.k) {                                  // wave-uniform
+      const bool ok = idv[e] >= 0 && idv[e] < p.n_cap;
+      const int64_t r = (int64_t)b * p.n_cap + (ok ? idv[e] : 0);
       raw.a[e] = *reinterpret_cast<const uint32_t*>(p.main_codes + r * 256 + 4 * g);
       raw.c[e] = p.main_scales[r * 32 + (g >> 1)];
-    } else if (kind == 2) {
+      kinds |= (ok ? 1u : 0u) << (2 * e);
+    } else {
+      const int rr = slot - p.k;
+      const bool ok = rr < nswa;
       const uint2 v = *reinterpret_cast<const uint2*>(
-          p.swa + ((int64_t)b * kWindow + row) * 512 + 8 * g);
+          p.swa + ((int64_t)b * kWindow + (ok ? rr : 0)) * 512 + 8 * g);
       raw.a[e] = v.x;
       raw.c[e] = v.y;
+      kinds |= (ok ? 2u : 0u) << (2 * e);
     }
   }
 }
 
-// Dequantise the gathered slots and write both LDS layouts of one buffer.
+// Dequantise the gathered slots (exactly, to fp16) and write both LDS
+// layouts of one buffer.
 __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
                                               int quarter, int g,
-                                              __bf16* buf, int32_t* valid) {
+                                              _Float16* buf, int32_t* valid) {
   uint32_t kd[8][4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t kind = (kinds >> (2 * e)) & 3u;
     if (kind == 1) {
-      const float sf = e4m3_to_f32_fast(raw.c[e]);
+      // (s, s) in fp16 from the E4M3 scale byte duplicated into two lanes.
+      const f16x2_t ss = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+          raw.c[e] * 0x101u, 1.0f, false);
       const uint32_t cw = raw.a[e];
-      const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
-      const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
-      const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
-      const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
-      kd[e][0] = pack_bf16(v0[0] * sf, v0[1] * sf);
-      kd[e][1] = pack_bf16(v1[0] * sf, v1[1] * sf);
-      kd[e][2] = pack_bf16(v2[0] * sf, v2[1] * sf);
-      kd[e][3] = pack_bf16(v3[0] * sf, v3[1] * sf);
+      kd[e][0] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ss);
+      kd[e][1] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ss);
+      kd[e][2] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * ss);
+      kd[e][3] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss);
     } else if (kind == 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = i < 2 ? raw.a[e] : raw.c[e];
-        const uint32_t sh = 16 * (i & 1);
-        kd[e][i] = e4m3_to_bf16_bits((w >> sh) & 0xFFu) |
-                   (e4m3_to_bf16_bits((w >> (sh + 8)) & 0xFFu) << 16);
-      }
+      kd[e][0] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.a[e], 1.0f, false));
+      kd[e][1] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.a[e], 1.0f, true));
+      kd[e][2] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.c[e], 1.0f, false));
+      kd[e][3] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.c[e], 1.0f, true));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) kd[e][i] = 0;
     }
   }
   // Key-major rows: slot j, dims 8g .. 8g+7.
-  __bf16* kt = buf;
+  _Float16* kt = buf;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
@@ -167,7 +172,7 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
     *reinterpret_cast<u32x4*>(kt + j * kKtStride + 8 * g) = v;
   }
   // Slot-grouped columns: for dim d, the 8 slots of this quarter.
-  __bf16* vs = buf + kKtElems + quarter * (512 * 8);
+  _Float16* vs = buf + kKtElems + quarter * (512 * 8);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     u32x4 lo, hi;
@@ -190,12 +195,24 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
   }
 }
 
+// Workgroup -> (sequence, split), placing all splits of a sequence on one
+// XCD: workgroups are dealt to the 8 XCDs round-robin by their linear id,
+// so id % 8 picks the XCD and sequences b with b % 8 == id % 8 live there.
+__device__ __forceinline__ bool map_workgroup(int id, int B, int S, int& b,
+                                              int& split) {
+  const int xcd = id & 7, slot = id >> 3;
+  b = xcd + 8 * (slot / S);
+  split = slot % S;
+  return b < B;
+}
+
 __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  __bf16* bufs = reinterpret_cast<__bf16*>(smem_raw);
+  _Float16* bufs = reinterpret_cast<_Float16*>(smem_raw);
   int32_t* valid_base = reinterpret_cast<int32_t*>(smem_raw + 2 * kBufElems * 2);
 
-  const int split = blockIdx.x, b = blockIdx.y;
+  int b, split;
+  if (!map_workgroup(blockIdx.x, p.B, p.splits, b, split)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;          // head within the wave / row in A
@@ -208,13 +225,21 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   int t1 = t0 + p.tiles_per_split;
   if (t1 > p.n_tiles) t1 = p.n_tiles;
 
-  // Q^T operand: head `head`, dims 32s + 8*q4 .. +7.
-  bf16x8_t qb[16];
+  Raw raw;
+  uint32_t kinds = 0;
+  if (t0 < t1) gather(p, b, t0, wave, lane, nswa, raw, kinds);
+
+  // Q^T operand: head `head`, dims 32s + 8*q4 .. +7, converted to fp16.
+  f16x8_t qb[16];
   {
     const bf16x8_t* qr = reinterpret_cast<const bf16x8_t*>(
         p.q + ((int64_t)b * kHeads + head) * 512 + 8 * q4);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qb[s] = qr[4 * s];
+    for (int s = 0; s < 16; ++s) {
+      const bf16x8_t v = qr[4 * s];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)(float)v[j];
+    }
   }
   f32x4 acc[32];
 #pragma unroll
@@ -222,12 +247,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
-  Raw raw;
-  uint32_t kinds = 0;
-  if (t0 < t1) {
-    gather(p, b, t0, wave, lane, nswa, raw, kinds);
-    dequant_store(raw, kinds, wave, lane, bufs, valid_base);
-  }
+  if (t0 < t1) dequant_store(raw, kinds, wave, lane, bufs, valid_base);
   __syncthreads();
 
   for (int t = t0; t < t1; ++t) {
@@ -235,20 +255,20 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
     const bool has_next = t + 1 < t1;
     if (has_next) gather(p, b, t + 1, wave, lane, nswa, raw, kinds);
 
-    const __bf16* kt = bufs + cur * kBufElems;
-    const __bf16* vs = kt + kKtElems;
+    const _Float16* kt = bufs + cur * kBufElems;
+    const _Float16* vs = kt + kKtElems;
     const int32_t* valid = valid_base + cur * kTile;
 
     // S^T = K Q^T for the 32 slots of this tile.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(
+      const f16x8_t a0 = *reinterpret_cast<const f16x8_t*>(
           kt + col * kKtStride + 32 * s + 8 * q4);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(
+      const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(
           kt + (16 + col) * kKtStride + 32 * s + 8 * q4);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[s], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[s], s1, 0, 0, 0);
     }
     // Logits in log2 units; lane holds slots 4*q4 + r and 16 + 4*q4 + r.
     float x[8];
@@ -264,25 +284,19 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const bool bump = mt > m_run + kRescaleSlack;   // also true from -inf
     if (__any(bump)) {
-      const float m_new = bump ? mt : m_run;
-      const float alpha = (m_run == -__builtin_inff()) ? 0.0f
-                                                       : exp2f(m_run - m_new);
       if (bump) {
+        const float alpha = (m_run == -__builtin_inff()) ? 0.0f
+                                                         : exp2f(m_run - mt);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-        m_run = m_new;
+        m_run = mt;
       }
     }
     const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
-    float pr[8];
+    f16x8_t pb;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      pr[r] = exp2f(x[r] - mref);
-    }
-    bf16x8_t pb;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) pb[r] = (__bf16)pr[r];
+    for (int r = 0; r < 8; ++r) pb[r] = (_Float16)exp2f(x[r] - mref);
     // The running sum takes the same rounded weights the product uses.
 #pragma unroll
     for (int r = 0; r < 8; ++r) l_run += (float)pb[r];
@@ -290,9 +304,9 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
     // O^T += V^T P^T.
 #pragma unroll
     for (int blk = 0; blk < 32; ++blk) {
-      const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
+      const f16x8_t va = *reinterpret_cast<const f16x8_t*>(
           vs + q4 * (512 * 8) + vs_phys(16 * blk + col) * 8);
-      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[blk], 0, 0, 0);
+      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[blk], 0, 0, 0);
     }
 
     if (has_next)
@@ -304,9 +318,9 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   // Fold the running sums of the four lanes that share a head.
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 
   if (p.splits == 1) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     uint16_t* orow = p.out + ((int64_t)b * kHeads + head) * 512 + 4 * q4;
 #pragma unroll
     for (int blk = 0; blk < 32; ++blk) {
@@ -316,56 +330,87 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
     }
     return;
   }
+  // Partial of this split, normalised by its own sum (a convex combination
+  // of keys, so |value| <= 2688 fits fp16 with 11 significant bits).
   const int64_t ps = ((int64_t)b * p.splits + split) * kHeads + head;
-  float* orow = p.part_o + ps * 512 + 4 * q4;
+  uint16_t* orow = p.part_o + ps * 512 + 4 * q4;
 #pragma unroll
-  for (int blk = 0; blk < 32; ++blk)
-    *reinterpret_cast<f32x4*>(orow + 16 * blk) = acc[blk];
+  for (int blk = 0; blk < 32; ++blk) {
+    const f16x2_t lo = {(_Float16)(acc[blk][0] * inv), (_Float16)(acc[blk][1] * inv)};
+    const f16x2_t hi = {(_Float16)(acc[blk][2] * inv), (_Float16)(acc[blk][3] * inv)};
+    *reinterpret_cast<uint2*>(orow + 16 * blk) = make_uint2(f16x2_bits(lo), f16x2_bits(hi));
+  }
   if (q4 == 0) {
     p.part_ml[ps * 2 + 0] = m_run;
     p.part_ml[ps * 2 + 1] = l_tot;
   }
 }
 
-// Merge of split partials: one thread per (sequence, head, 4 dims).
+// Merge of split partials: one thread per (sequence, head, 8 dims).
+// o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - M).  Every load is
+// issued before any is used (at most kMaxSplits partials).
+constexpr int kMaxSplits = 16;
+
 __global__ __launch_bounds__(256) void attn_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
     int splits, int B, uint16_t* __restrict__ out) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)B * kHeads * 128) return;
-  const int d4 = (int)(t & 127);
-  const int64_t bh = t >> 7;
+  if (t >= (int64_t)B * kHeads * 64) return;
+  const int d8 = (int)(t & 63);
+  const int64_t bh = t >> 6;
   const int head = (int)(bh % kHeads);
   const int64_t b = bh / kHeads;
+  float2 ml[kMaxSplits];
+  u32x4 v[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < splits) {
+      const int64_t ps = (b * splits + s) * kHeads + head;
+      ml[s] = *reinterpret_cast<const float2*>(part_ml + ps * 2);
+      v[s] = *reinterpret_cast<const u32x4*>(part_o + ps * 512 + 8 * d8);
+    }
+  }
   float M = -__builtin_inff();
-  for (int s = 0; s < splits; ++s)
-    M = fmaxf(M, part_ml[((b * splits + s) * kHeads + head) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < splits) M = fmaxf(M, ml[s].x);
   const float mref = M == -__builtin_inff() ? 0.0f : M;
   float L = 0.0f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const int64_t ps = (b * splits + s) * kHeads + head;
-    const float ms = part_ml[ps * 2];
-    const float wgt = ms == -__builtin_inff() ? 0.0f : exp2f(ms - mref);
-    L += part_ml[ps * 2 + 1] * wgt;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + ps * 512 + 4 * d4);
-    o += v * wgt;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < splits) {
+      const float wgt = ml[s].x == -__builtin_inff()
+                            ? 0.0f : ml[s].y * exp2f(ml[s].x - mref);
+      L += wgt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x2_t h = bits_f16x2(v[s][i]);
+        o[2 * i] += wgt * (float)h[0];
+        o[2 * i + 1] += wgt * (float)h[1];
+      }
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const uint32_t lo = pack_bf16(o[0] * inv, o[1] * inv);
-  const uint32_t hi = pack_bf16(o[2] * inv, o[3] * inv);
-  *reinterpret_cast<uint2*>(out + bh * 512 + 4 * d4) = make_uint2(lo, hi);
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16(o[2 * i] * inv, o[2 * i + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + bh * 512 + 8 * d8) = w;
 }
 
 }  // namespace
 
 int attn_splits(int B, int k) {
   const int n_tiles = (k + kWindow + kTile - 1) / kTile;
-  // Aim for about two workgroups per compute unit (256 CUs).
-  int s = (512 + B - 1) / (B > 0 ? B : 1);
-  if (s > n_tiles) s = n_tiles;
+  // About one workgroup per compute unit (256 CUs, one workgroup each:
+  // the double-buffered tiles take 129 KB of LDS); with many sequences at
+  // least 3 tiles each, to bound the partials' traffic.
+  int s = (256 + B - 1) / (B > 0 ? B : 1);
+  const int max_s = B >= 16 ? (n_tiles + 2) / 3 : n_tiles;
+  if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   // Re-balance so every split has the same number of tiles.
+  if (s > kMaxSplits) s = kMaxSplits;
   const int tps = (n_tiles + s - 1) / s;
   return (n_tiles + tps - 1) / tps;
 }
@@ -373,7 +418,7 @@ int attn_splits(int B, int k) {
 size_t attn_workspace(int B, int k) {
   const int s = attn_splits(B, k);
   if (s <= 1) return 0;
-  const size_t o = (size_t)B * s * kHeads * 512 * 4;
+  const size_t o = (size_t)B * s * kHeads * 512 * 2;
   const size_t ml = (size_t)B * s * kHeads * 2 * 4;
   return ((o + 255) & ~size_t(255)) + ((ml + 255) & ~size_t(255));
 }
@@ -384,9 +429,9 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        const int32_t* n_swa, int B, float scale,
                        uint16_t* out, void* ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(attn_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(attn_kernel),
+                                  kSmemBytes, lds_set);
   if (e != hipSuccess) return e;
   AttnArgs a{};
   a.main_codes = main_codes;
@@ -399,20 +444,22 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   a.n_swa = n_swa;
   a.scale_log2 = scale * kLog2e;
   a.out = out;
+  a.B = B;
   a.n_tiles = (k + kWindow + kTile - 1) / kTile;
   a.splits = attn_splits(B, k);
   a.tiles_per_split = (a.n_tiles + a.splits - 1) / a.splits;
   if (a.splits > 1) {
-    const size_t o = (size_t)B * a.splits * kHeads * 512 * 4;
-    a.part_o = static_cast<float*>(ws);
+    const size_t o = (size_t)B * a.splits * kHeads * 512 * 2;
+    a.part_o = static_cast<uint16_t*>(ws);
     a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                          ((o + 255) & ~size_t(255)));
   }
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)a.splits, (unsigned)B),
-                     dim3(256), kSmemBytes, s, a);
+  const int groups = (B + 7) / 8;
+  const unsigned grid = (unsigned)(8 * groups * a.splits);
+  hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(256), kSmemBytes, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const int64_t threads = (int64_t)B * kHeads * 128;
+  const int64_t threads = (int64_t)B * kHeads * 64;
   hipLaunchKernelGGL(attn_combine_kernel,
                      dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                      a.part_o, a.part_ml, a.splits, B, out);

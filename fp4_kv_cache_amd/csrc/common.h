@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace csa2 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -46,6 +48,19 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
   return u2f((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Raise a kernel's dynamic-LDS limit once per device (host side).
+inline hipError_t ensure_lds_limit(const void* func, int bytes,
+                                   std::atomic<uint64_t>& done_mask) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done_mask.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done_mask.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 }  // namespace csa2

@@ -19,6 +19,10 @@
 // weights and the head sum are applied per lane and the two lane halves are
 // folded with one cross-half swap.  HBM traffic per entry: 64 + 4 bytes
 // read, 4 bytes of score written.
+//
+// Tile maxima (the decode path): each 32-row tile's largest score is also
+// written (one wave reduction per tile); the top-k stage uses them to read
+// only the tiles that can hold a winner.
 #include "common.h"
 #include "internal.h"
 
@@ -115,13 +119,13 @@ __device__ __forceinline__ int64_t row_of(const int32_t* cand, int64_t n_rows,
   return e;
 }
 
-template <int KEYFMT>
+template <int KEYFMT, bool TMAX>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ cand, int64_t n_rows,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, float* __restrict__ tmax) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -147,7 +151,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 
   const int64_t base =
       ((int64_t)blockIdx.x * kWaves + wave) * (kTilesPerWave * 32);
-  if (base >= n_rows) return;
   // Rows past the visible range need no loads at all.
   const int64_t scan_end = cand ? n_rows : (n < n_rows ? n : n_rows);
 
@@ -183,6 +186,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       if (valid) total = sum;
     }
     if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total;
+    if constexpr (TMAX) {
+      // Largest score of the tile (lanes of both halves hold the same 32).
+      float mx = total;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (lane == 0) tmax[(int64_t)b * ((n_rows + 31) >> 5) + (tile >> 5)] = mx;
+    }
     cur = nxt;
   }
 }
@@ -193,18 +203,27 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,
                           const int32_t* n_entries, const int32_t* cand,
                           int64_t n_rows, const uint16_t* q_idx,
-                          const float* w, int B, float* scores, hipStream_t s) {
+                          const float* w, int B, float* scores, hipStream_t s,
+                          float* tmax) {
   if (n_rows == 0 || B == 0) return hipSuccess;
   const dim3 grid((unsigned)((n_rows + kEntriesPerBlock - 1) / kEntriesPerBlock),
                   (unsigned)B);
-  if (keyfmt == 0)
-    hipLaunchKernelGGL(indexer_kernel<0>, grid, dim3(256), 0, s, k_codes,
-                       k_scales, n_cap, n_entries, cand, n_rows, q_idx, w,
-                       scores);
+  if (keyfmt == 0 && tmax)
+    hipLaunchKernelGGL((indexer_kernel<0, true>), grid, dim3(256), 0, s,
+                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
+                       q_idx, w, scores, tmax);
+  else if (keyfmt == 0)
+    hipLaunchKernelGGL((indexer_kernel<0, false>), grid, dim3(256), 0, s,
+                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
+                       q_idx, w, scores, tmax);
+  else if (tmax)
+    hipLaunchKernelGGL((indexer_kernel<1, true>), grid, dim3(256), 0, s,
+                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
+                       q_idx, w, scores, tmax);
   else
-    hipLaunchKernelGGL(indexer_kernel<1>, grid, dim3(256), 0, s, k_codes,
-                       k_scales, n_cap, n_entries, cand, n_rows, q_idx, w,
-                       scores);
+    hipLaunchKernelGGL((indexer_kernel<1, false>), grid, dim3(256), 0, s,
+                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
+                       q_idx, w, scores, tmax);
   return hipGetLastError();
 }
 

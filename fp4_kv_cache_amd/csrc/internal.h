@@ -23,27 +23,30 @@ hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
                           int32_t* nblk, hipStream_t s);
 
 // indexer.hip
+// Scores rows (all n_rows, or the n_rows candidate ids `cand`) into
+// scores[B][n_rows]; with `tmax`, also each 32-row tile's largest score into
+// tmax[B][ceil(n_rows/32)].
 hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,
                           const int32_t* n_entries, const int32_t* cand,
                           int64_t n_rows, const uint16_t* q_idx,
-                          const float* w, int B, float* scores, hipStream_t s);
+                          const float* w, int B, float* scores, hipStream_t s,
+                          float* tmax = nullptr);
 
 // topk.hip
-struct TopkPlan {
-  int64_t ld;          // row length
-  int k;
-  int chunk;           // elements per first-stage segment
-  int n_stages;        // 1 = single pass
-  int segs[8];         // segments per row at each stage
-  int64_t len[8];      // row length at each stage
-};
-TopkPlan topk_plan(int64_t ld, int k);
-size_t topk_workspace(int B, const TopkPlan& p);
+// Exact per-row top-k (see topk.hip); `tmax` (tile maxima, nullable)
+// enables tile pruning.
+hipError_t launch_row_select(const float* scores, const float* tmax,
+                             int64_t ld, const int32_t* n_valid,
+                             const int32_t* ids, int B, int k, int block,
+                             const int32_t* limit, int32_t* out,
+                             hipStream_t s);
+// Standalone top-k over a score array (computes tile maxima in `ws`).
+size_t topk_workspace(int B, int64_t ld);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int32_t* ids, int B, int k, int block,
                        const int32_t* limit, int32_t* out, void* ws,
-                       const TopkPlan& p, hipStream_t s);
+                       hipStream_t s);
 
 // attn.hip
 int attn_splits(int B, int k);

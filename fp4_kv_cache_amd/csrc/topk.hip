@@ -8,336 +8,313 @@
 // positions).  The pages give no tie rule; here a higher score wins and
 // equal scores go to the lower id.
 //
-// Design.  A row is cut into segments of at most kChunk elements; one
-// 1024-thread workgroup selects the exact top-k of a segment entirely in
-// LDS, and the survivors of all segments (still in id order) are selected
-// again until one segment remains.  The union of per-segment top-k sets
-// contains the row's top-k, so the result is exact.
-//
-// Inside a segment the k-th value is found by narrowing a value interval
-// [lo, hi] that holds it: the candidates in the interval are binned by a
-// linear, monotone map of their value into 2048 bins (LDS atomics; a linear
-// map spreads the data, so few lanes collide on a bin), a block scan finds
-// the bin where the running count from the top reaches the number still
-// needed, and the interval shrinks to that bin's actual minimum and maximum.
-// Each pass shrinks the interval at least 2048-fold, so it ends after a few
-// passes either with the bin holding exactly the number needed or with all
-// candidates equal (then the lowest ids win).  The chosen elements are then
-// written in id order with a block-wide prefix sum.
+// Tile pruning.  Rows are cut into 32-element tiles and each tile's largest
+// score is known (the indexer writes it; tilemax_kernel computes it for a
+// plain score array).  Let M be the k-th largest tile maximum: k different
+// tiles each hold an element >= M, so the k-th largest score is >= M, and
+// every top-k element lies in a tile whose maximum is >= M.  One 512-thread
+// workgroup per row therefore (1) finds M by selecting the top-k tile
+// maxima, (2) lists, in order, every tile whose maximum is >= M (about k
+// tiles), and (3) selects the top-k among those tiles' scores only.  Rows
+// short enough for one pass skip the pruning.  Each selection streams its
+// input through block_select in passes of 16,384 register-held keys, keeping
+// the running winners (in id order) in LDS.
 #include <math.h>
 
 #include "common.h"
 #include "internal.h"
+#include "select.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kChunk = 16384;               // max elements per segment
-constexpr int kPer = kChunk / kThreads;     // elements per thread
-constexpr int kBins = 2048;
-constexpr int kWavesTk = kThreads / 64;
+constexpr int kNT = 512;                    // threads per row
+constexpr int kPer = 32;                    // keys per thread
+constexpr int kCap = kNT * kPer;            // 16384 keys per pass
+constexpr int kNB = 2048;
+constexpr int kTileList = 4096;             // candidate tiles held in LDS
+static_assert(kNB >= 2048, "winners (k <= 2048) are staged in the histogram");
 
-struct TkSmem {
-  float v[kChunk];
-  int32_t id[kChunk];
-  int32_t hist[kBins];
-  int32_t red[kWavesTk];
-  float fred[2][kWavesTk];
-  int32_t bstar, cum_before;
+struct RowSmem {
+  uint32_t key[kCap];
+  int32_t id[kCap];
+  int32_t tiles[kTileList];
+  SelSmem<kNT, kNB> sel;
 };
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
+// Top-k of the `count` (key, id) pairs held in sm.key/sm.id (ids in
+// order): the winners are compacted, still in id order, to the front.
+// Returns their number.  PER keys per thread; count <= kNT * PER.
+template <int PER>
+__device__ __forceinline__ int select_dense(RowSmem& sm, int count, int k) {
+  const int tid = threadIdx.x;
+  uint32_t key[PER];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+  for (int j = 0; j < PER; ++j) {
+    const int pos = tid * PER + j;
+    key[j] = pos < count ? sm.key[pos] : 0u;
   }
-  return x;
+  const SelResult r = block_select<kNT, PER, kNB>(key, k, sm.sel);
+  int tot;
+  int p = sel_excl_scan<kNT, kNB>(__popc(r.mask), tot, sm.sel);
+  // In-order compaction of the winners (at most k <= kNB): keys come from
+  // registers; ids are staged through the histogram buffer (free after the
+  // selection) so no thread overwrites an id another has yet to read.
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (r.mask & (1u << j)) {
+      sm.sel.hist[p] = sm.id[tid * PER + j];
+      sm.key[p] = key[j];
+      ++p;
+    }
+  __syncthreads();
+  for (int q = tid; q < tot; q += kNT) sm.id[q] = sm.sel.hist[q];
+  __syncthreads();
+  return tot;
 }
 
-// Block-wide exclusive prefix sum; also returns the block total.
-__device__ __forceinline__ int block_excl_scan(int x, int& total, TkSmem& sm) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(x);
-  if (lane == 63) sm.red[wv] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWavesTk; ++i) {
-    const int t = sm.red[i];
-    before += i < wv ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  total = tot;
-  return before + incl - x;
+__device__ __forceinline__ int select_any(RowSmem& sm, int count, int k) {
+  if (count <= kNT * 2) return select_dense<2>(sm, count, k);
+  if (count <= kNT * 8) return select_dense<8>(sm, count, k);
+  return select_dense<kPer>(sm, count, k);
 }
 
-__device__ __forceinline__ void block_minmax(float& mn, float& mx, TkSmem& sm) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// Streaming top-k into LDS: feeds src(i, key, id) for i < n (ids ascending
+// in i) through passes of up to kCap keys; afterwards key/id[0..count) hold
+// the winners in id order.
+template <typename Src>
+__device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
+                                             Src src) {
+  const int tid = threadIdx.x;
+  int count = 0;
+  int64_t pos = 0;
+  bool first = true;
+  while (first || pos < n) {
+    first = false;
+    // Fill the free slots after the current winners: loads of a half pass
+    // are all issued before their stores.
+    const int64_t room = kCap - count;
+    const int fill = (int)(n - pos < room ? n - pos : room);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
-  if (lane == 0) { sm.fred[0][wv] = mn; sm.fred[1][wv] = mx; }
-  __syncthreads();
-  mn = sm.fred[0][0];
-  mx = sm.fred[1][0];
+    for (int h = 0; h < 2; ++h) {
+      constexpr int kH = kCap / kNT / 2;
+      uint32_t fk[kH];
+      int32_t fi[kH];
 #pragma unroll
-  for (int i = 1; i < kWavesTk; ++i) {
-    mn = fminf(mn, sm.fred[0][i]);
-    mx = fmaxf(mx, sm.fred[1][i]);
+      for (int j = 0; j < kH; ++j) {
+        const int s = (h * kH + j) * kNT + tid;
+        fk[j] = 0;
+        fi[j] = -1;
+        if (s >= count && s < count + fill) src(pos + (s - count), fk[j], fi[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < kH; ++j) {
+        const int s = (h * kH + j) * kNT + tid;
+        if (s >= count && s < count + fill) { sm.key[s] = fk[j]; sm.id[s] = fi[j]; }
+      }
+    }
+    pos += fill;
+    __syncthreads();
+    count = select_any(sm, count + fill, k);
   }
-  __syncthreads();
+  return count;
 }
 
-__device__ __forceinline__ int bin_of(float v, float hi, double inv) {
-  const double x = ((double)hi - (double)v) * inv;
-  return x >= (double)(kBins - 1) ? kBins - 1 : (int)x;
-}
+// Element sources for stream_select (ids ascending in i).
+struct ScoreSrc {                 // a score row; ids = positions or ids[]
+  const float* row;
+  const int32_t* idrow;
+  __device__ __forceinline__ void operator()(int64_t i, uint32_t& key,
+                                             int32_t& id) const {
+    const int32_t d = idrow ? idrow[i] : (int32_t)i;
+    key = d >= 0 ? score_key(row[i]) : 0u;
+    id = d;
+  }
+};
+struct TileSrc {                  // tile maxima; ids = tile numbers
+  const float* trow;
+  __device__ __forceinline__ void operator()(int64_t t, uint32_t& key,
+                                             int32_t& id) const {
+    key = score_key(trow[t]);
+    id = (int32_t)t;
+  }
+};
 
-struct TkArgs {
-  const float* vals;        // input values, row stride ld
-  const int32_t* ids;       // nullable: ids = positions
+struct RowArgs {
+  const float* scores;      // row stride ld
+  const float* tmax;        // nullable; row stride ceil(ld / 32)
   int64_t ld;
-  const int32_t* n_valid;   // nullable (rows then have length `len`)
-  int64_t len;              // row length at this stage
-  int seg_len;
-  int segs;                 // segments per row at this stage
+  const int32_t* n_valid;   // nullable
+  const int32_t* ids;       // nullable
   int k;
-  // intermediate output: [B][segs][k]
-  float* out_vals;
-  int32_t* out_ids;
-  // final output (when segs == 1): [B][k * block]
-  int32_t* out;
   int block;
-  const int32_t* limit;
+  const int32_t* limit;     // nullable
+  int32_t* out;             // [B][k * block]
 };
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TkArgs a) {
+__global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  TkSmem& sm = *reinterpret_cast<TkSmem*>(smem_raw);
-  const int seg = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  int64_t row_len = a.len;
+  RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int64_t len = a.ld;
   if (a.n_valid) {
     const int64_t nv = a.n_valid[b];
-    row_len = nv < row_len ? (nv > 0 ? nv : 0) : row_len;
+    len = nv < len ? (nv > 0 ? nv : 0) : len;
   }
-  const int64_t s0 = (int64_t)seg * a.seg_len;
-  int64_t s1 = s0 + a.seg_len;
-  if (s1 > row_len) s1 = row_len;
-  const float NEG = -__builtin_inff();
-
-  // 1. Coalesced load into LDS; invalid elements become -inf.
-  for (int j = 0; j < kPer; ++j) {
-    const int li = j * kThreads + tid;
-    const int64_t gi = s0 + li;
-    float v = NEG;
-    int32_t id = -1;
-    if (gi < s1) {
-      v = a.vals[(int64_t)b * a.ld + gi];
-      id = a.ids ? a.ids[(int64_t)b * a.ld + gi] : (int32_t)gi;
-      if (!(v > NEG) || id < 0) v = NEG;     // NaN, -inf, bad id
-    }
-    sm.v[li] = v;
-    sm.id[li] = id;
-  }
-  __syncthreads();
-
-  // 2. Each thread owns a contiguous run of kPer elements.
-  float vr[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) vr[j] = sm.v[tid * kPer + j];
-  int nval = 0;
-  float mn = __builtin_inff(), mx = NEG;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (vr[j] > NEG) { ++nval; mn = fminf(mn, vr[j]); mx = fmaxf(mx, vr[j]); }
-  int total_valid;
-  block_excl_scan(nval, total_valid, sm);
-  block_minmax(mn, mx, sm);
-
-  // 3. Narrow [lo, hi] until the selection is decided.
-  // Selected: v > hi, plus -- if take_all -- every v in [lo, hi], else (all
-  // candidates equal) the first `need` of them in id order.
-  float lo = mn, hi = mx;
-  int need = a.k;
-  bool take_all = true;
-  if (total_valid > a.k) {
-    take_all = false;
-    for (int it = 0; it < 64; ++it) {
-      if (!(lo < hi)) break;                   // all candidates tie
-      for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
-      __syncthreads();
-      const double inv = (double)kBins / ((double)hi - (double)lo);
+  const ScoreSrc from_scores{a.scores + (int64_t)b * a.ld,
+                             a.ids ? a.ids + (int64_t)b * a.ld : nullptr};
+  const int64_t n_t = (len + 31) >> 5;
+  int count = 0;
+  bool pruned = a.tmax != nullptr && n_t > a.k;
+  if (pruned) {
+    const float* trow = a.tmax + (int64_t)b * ((a.ld + 31) >> 5);
+    // (1) M = the k-th largest tile maximum.
+    const int ct = stream_select(sm, n_t, a.k, TileSrc{trow});
+    uint32_t mk = 0xFFFFFFFFu, dummy = 0u;
+    for (int p = tid; p < ct; p += kNT) mk = min(mk, sm.key[p]);
+    sel_minmax<kNT, kNB>(mk, dummy, sm.sel);
+    // (2) every tile whose maximum is >= M, in order (each thread scans a
+    // run of kPer tiles).
+    int n_list = 0;
+    for (int64_t t0 = 0; t0 < n_t; t0 += kCap) {
+      const int64_t tb = t0 + (int64_t)tid * kPer;
+      uint32_t fl = 0;
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (vr[j] >= lo && vr[j] <= hi) atomicAdd(&sm.hist[bin_of(vr[j], hi, inv)], 1);
-      __syncthreads();
-      const int h0 = sm.hist[2 * tid], h1 = sm.hist[2 * tid + 1];
+        if (tb + j < n_t && score_key(trow[tb + j]) >= mk) fl |= 1u << j;
       int tot;
-      const int ex = block_excl_scan(h0 + h1, tot, sm);
-      if (ex < need && ex + h0 + h1 >= need) {
-        if (ex + h0 >= need) { sm.bstar = 2 * tid; sm.cum_before = ex; }
-        else { sm.bstar = 2 * tid + 1; sm.cum_before = ex + h0; }
-      }
-      __syncthreads();
-      const int bs = sm.bstar;
-      const int cnt = sm.hist[bs];
-      need -= sm.cum_before;
-      float bmn = __builtin_inff(), bmx = NEG;
+      int p = sel_excl_scan<kNT, kNB>(__popc(fl), tot, sm.sel);
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (vr[j] >= lo && vr[j] <= hi && bin_of(vr[j], hi, inv) == bs) {
-          bmn = fminf(bmn, vr[j]);
-          bmx = fmaxf(bmx, vr[j]);
+        if (fl & (1u << j)) {
+          if (n_list + p < kTileList) sm.tiles[n_list + p] = (int32_t)(tb + j);
+          ++p;
         }
-      block_minmax(bmn, bmx, sm);
-      lo = bmn;
-      hi = bmx;
-      if (cnt == need) { take_all = true; break; }
+      n_list += tot;
     }
-  }
-
-  // 4. Flags, ranks among ties, and the in-order compaction.
-  int ntie = 0;
-  if (!take_all) {
+    __syncthreads();
+    // (3) the elements >= M of the listed tiles, densely, in id order.
+    if (n_list <= kTileList) {
+      int n_c = 0;
+      for (int l0 = 0; l0 < n_list; l0 += kNT) {
+        const int l = l0 + tid;
+        uint32_t kk[32];
+        int32_t ii[32];
+        uint32_t fl = 0;
+        if (l < n_list) {
+          const int64_t base = (int64_t)sm.tiles[l] * 32;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) ntie += (vr[j] == lo) ? 1 : 0;
-  }
-  int tie_total;
-  int tie_rank = block_excl_scan(ntie, tie_total, sm);
-  uint32_t selmask = 0;
-  int nsel = 0;
+          for (int j = 0; j < 32; ++j) {
+            kk[j] = 0;
+            ii[j] = -1;
+            if (base + j < len) from_scores(base + j, kk[j], ii[j]);
+            if (kk[j] >= mk) fl |= 1u << j;
+          }
+        }
+        int tot;
+        int p = sel_excl_scan<kNT, kNB>(__popc(fl), tot, sm.sel);
+        if (n_c + tot <= kCap) {
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    bool s;
-    if (!(vr[j] > NEG)) s = false;
-    else if (take_all) s = vr[j] >= lo;
-    else if (vr[j] > hi) s = true;
-    else if (vr[j] == lo) { s = tie_rank < need; ++tie_rank; }
-    else s = false;
-    if (s) { selmask |= 1u << j; ++nsel; }
-  }
-  int nsel_total;
-  int pos = block_excl_scan(nsel, nsel_total, sm);
-
-  const bool final_stage = a.segs == 1;
-  if (!final_stage) {
-    const int64_t ob = ((int64_t)b * a.segs + seg) * a.k;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (selmask & (1u << j)) {
-        a.out_vals[ob + pos] = vr[j];
-        a.out_ids[ob + pos] = sm.id[tid * kPer + j];
-        ++pos;
+          for (int j = 0; j < 32; ++j)
+            if (fl & (1u << j)) {
+              sm.key[n_c + p] = kk[j];
+              sm.id[n_c + p] = ii[j];
+              ++p;
+            }
+        }
+        n_c += tot;
       }
-    for (int p = nsel_total + tid; p < a.k; p += kThreads) {
-      a.out_vals[ob + p] = NEG;
-      a.out_ids[ob + p] = -1;
+      __syncthreads();
+      if (n_c <= kCap) count = select_any(sm, n_c, a.k);
+      else pruned = false;     // (massive ties) fall back to a full pass
+    } else {
+      pruned = false;
     }
-    return;
   }
+  if (!pruned) count = stream_select(sm, len, a.k, from_scores);
+  // Winners in id order -> out[b], expanded by `block` and clipped.
   const int64_t ob = (int64_t)b * a.k * a.block;
   const int64_t lim = a.limit ? (int64_t)a.limit[b] : INT64_MAX;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (selmask & (1u << j)) {
-      const int64_t id = sm.id[tid * kPer + j];
-      for (int t = 0; t < a.block; ++t) {
-        const int64_t p = id * a.block + t;
-        a.out[ob + (int64_t)pos * a.block + t] = p < lim ? (int32_t)p : -1;
-      }
-      ++pos;
+  for (int p = tid; p < count; p += kNT) {
+    const int64_t id = sm.id[p];
+    for (int t = 0; t < a.block; ++t) {
+      const int64_t q = id * a.block + t;
+      a.out[ob + (int64_t)p * a.block + t] = q < lim ? (int32_t)q : -1;
     }
-  for (int64_t p = (int64_t)nsel_total * a.block + tid; p < (int64_t)a.k * a.block;
-       p += kThreads)
+  }
+  for (int64_t p = (int64_t)count * a.block + tid; p < (int64_t)a.k * a.block;
+       p += kNT)
     a.out[ob + p] = -1;
+}
+
+// Tile maxima of a plain score array (entries with a negative id count as
+// -inf).  One thread per tile.
+__global__ void tilemax_kernel(const float* __restrict__ scores, int64_t ld,
+                               const int32_t* __restrict__ ids, int B,
+                               float* __restrict__ tmax) {
+  const int64_t nt = (ld + 31) >> 5;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nt * B) return;
+  const int64_t b = t / nt, tt = t % nt;
+  float mx = -__builtin_inff();
+  for (int j = 0; j < 32; ++j) {
+    const int64_t i = tt * 32 + j;
+    if (i >= ld) break;
+    const float v = scores[b * ld + i];
+    if ((!ids || ids[b * ld + i] >= 0) && v > mx) mx = v;
+  }
+  tmax[t] = mx;
 }
 
 }  // namespace
 
-TopkPlan topk_plan(int64_t ld, int k) {
-  TopkPlan p{};
-  p.ld = ld;
-  p.k = k;
-  p.chunk = kChunk;
-  int64_t len = ld;
-  int st = 0;
-  for (;;) {
-    const int64_t segs = (len + kChunk - 1) / kChunk;
-    p.len[st] = len;
-    p.segs[st] = (int)(segs > 0 ? segs : 1);
-    ++st;
-    if (segs <= 1 || st >= 8) break;
-    len = segs * (int64_t)k;
-  }
-  p.n_stages = st;
-  return p;
+size_t topk_workspace(int B, int64_t ld) {
+  if (ld <= kCap) return 0;
+  return (((size_t)B * ((ld + 31) >> 5) * 4) + 255) & ~size_t(255);
 }
 
-size_t topk_workspace(int B, const TopkPlan& p) {
-  size_t mx = 0;
-  for (int s = 0; s + 1 < p.n_stages; ++s) {
-    const size_t e = (size_t)B * p.segs[s] * p.k;
-    if (e > mx) mx = e;
-  }
-  // two ping-pong buffers of (value, id) pairs, 256-byte aligned
-  const size_t one = ((mx * 8) + 255) & ~size_t(255);
-  return 2 * one;
+hipError_t launch_row_select(const float* scores, const float* tmax,
+                             int64_t ld, const int32_t* n_valid,
+                             const int32_t* ids, int B, int k, int block,
+                             const int32_t* limit, int32_t* out,
+                             hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(
+      reinterpret_cast<const void*>(row_select_kernel), (int)sizeof(RowSmem),
+      lds_set);
+  if (e != hipSuccess) return e;
+  RowArgs a{};
+  a.scores = scores;
+  a.tmax = tmax;
+  a.ld = ld;
+  a.n_valid = n_valid;
+  a.ids = ids;
+  a.k = k;
+  a.block = block;
+  a.limit = limit;
+  a.out = out;
+  hipLaunchKernelGGL(row_select_kernel, dim3((unsigned)B), dim3(kNT),
+                     sizeof(RowSmem), s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int32_t* ids, int B, int k, int block,
                        const int32_t* limit, int32_t* out, void* ws,
-                       const TopkPlan& p, hipStream_t s) {
+                       hipStream_t s) {
   if (B == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(topk_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(TkSmem));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  size_t mx = 0;
-  for (int st = 0; st + 1 < p.n_stages; ++st) {
-    const size_t e = (size_t)B * p.segs[st] * p.k;
-    if (e > mx) mx = e;
-  }
-  const size_t one = ((mx * 8) + 255) & ~size_t(255);
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  const float* in_vals = scores;
-  const int32_t* in_ids = ids;
-  int64_t in_ld = ld;
-  for (int st = 0; st < p.n_stages; ++st) {
-    TkArgs a{};
-    a.vals = in_vals;
-    a.ids = in_ids;
-    a.ld = in_ld;
-    a.n_valid = st == 0 ? n_valid : nullptr;
-    a.len = p.len[st];
-    a.seg_len = kChunk;
-    a.segs = p.segs[st];
-    a.k = k;
-    uint8_t* buf = base + (st & 1) * one;
-    a.out_vals = reinterpret_cast<float*>(buf);
-    a.out_ids = reinterpret_cast<int32_t*>(buf + mx * 4);
-    a.out = out;
-    a.block = block;
-    a.limit = limit;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.segs, (unsigned)B),
-                       dim3(kThreads), sizeof(TkSmem), s, a);
+  float* tmax = nullptr;
+  if (ld > kCap) {
+    tmax = static_cast<float*>(ws);
+    const int64_t n = (int64_t)B * ((ld + 31) >> 5);
+    hipLaunchKernelGGL(tilemax_kernel, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, scores, ld, ids, B, tmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    in_vals = a.out_vals;
-    in_ids = a.out_ids;
-    in_ld = (int64_t)a.segs * k;
   }
-  return hipSuccess;
+  return launch_row_select(scores, tmax, ld, n_valid, ids, B, k, block, limit,
+                           out, s);
 }
 
 }  // namespace csa2
