@@ -8,7 +8,7 @@
 
 #include <algorithm>
 
-#include "../../include/csa2.h"
+#include "csa2.h"
 #include "internal.h"
 
 namespace {

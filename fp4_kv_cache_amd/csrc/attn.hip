@@ -99,9 +99,11 @@ struct Raw {
 
 // Gather the raw bytes of the 8 slots this lane dequantises in one tile
 // (wavefront `quarter` owns slots {4q..4q+3, 16+4q..16+4q+3}, lane g owns
-// dims 8g..8g+7).  All top-k ids are loaded first and every data load uses
-// a clamped (always valid) row, so no load waits on another; `kinds` records
-// per slot 0 = empty, 1 = main entry, 2 = window row.
+// dims 8g..8g+7).  All top-k ids are loaded first; then every slot issues the
+// same two unconditional dword loads from a clamped (always valid) address:
+// main entry -> code dword + the dword holding its scale byte, window row ->
+// its 8 bytes.  With no load under a branch, loads of a tile stay in flight
+// together.  `kinds` records per slot 0 = empty, 1 = main entry, 2 = window.
 __device__ __forceinline__ void gather(const AttnArgs& p, int b, int tile,
                                        int quarter, int g, int nswa, Raw& raw,
                                        uint32_t& kinds) {
@@ -117,21 +119,21 @@ __device__ __forceinline__ void gather(const AttnArgs& p, int b, int tile,
   for (int e = 0; e < 8; ++e) {
     const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
     const int slot = tile * kTile + j;
-    if (slot < p.k) {                                  // wave-uniform
-      const bool ok = idv[e] >= 0 && idv[e] < p.n_cap;
-      const int64_t r = (int64_t)b * p.n_cap + (ok ? idv[e] : 0);
-      raw.a[e] = *reinterpret_cast<const uint32_t*>(p.main_codes + r * 256 + 4 * g);
-      raw.c[e] = p.main_scales[r * 32 + (g >> 1)];
-      kinds |= (ok ? 1u : 0u) << (2 * e);
-    } else {
-      const int rr = slot - p.k;
-      const bool ok = rr < nswa;
-      const uint2 v = *reinterpret_cast<const uint2*>(
-          p.swa + ((int64_t)b * kWindow + (ok ? rr : 0)) * 512 + 8 * g);
-      raw.a[e] = v.x;
-      raw.c[e] = v.y;
-      kinds |= (ok ? 2u : 0u) << (2 * e);
-    }
+    const bool is_main = slot < p.k;
+    const bool ok_main = is_main && idv[e] >= 0 && idv[e] < p.n_cap;
+    const int rr = slot - p.k;
+    const bool ok_swa = !is_main && rr < nswa;
+    const int64_t mrow = (int64_t)b * p.n_cap + (ok_main ? idv[e] : 0);
+    const int64_t srow = (int64_t)b * kWindow + (ok_swa ? rr : 0);
+    const uint8_t* pa = is_main ? p.main_codes + mrow * 256 + 4 * g
+                                : p.swa + srow * 512 + 8 * g;
+    const uint8_t* pc = is_main ? p.main_scales + mrow * 32 + ((g >> 1) & ~3)
+                                : pa + 4;
+    const uint32_t va = *reinterpret_cast<const uint32_t*>(pa);
+    const uint32_t vc = *reinterpret_cast<const uint32_t*>(pc);
+    raw.a[e] = va;
+    raw.c[e] = is_main ? (vc >> (8 * ((g >> 1) & 3))) & 0xFFu : vc;
+    kinds |= (ok_main ? 1u : (ok_swa ? 2u : 0u)) << (2 * e);
   }
 }
 

@@ -43,41 +43,33 @@ template <> struct RawKey<1> {       // bf16: 64 dims = 128 bytes
   u32x4 v[8];
 };
 
+// Loads are unconditional (the caller clamps `row` to a row that exists), so
+// no load sits inside a branch and the compiler can keep several tiles of
+// loads in flight with exact wait counts.
 template <int KEYFMT>
 __device__ __forceinline__ void load_key(RawKey<KEYFMT>& r, const void* codes,
                                          const uint8_t* scales, int64_t row,
-                                         int half, bool valid);
+                                         int half);
 
 template <>
 __device__ __forceinline__ void load_key<0>(RawKey<0>& r, const void* codes,
                                             const uint8_t* scales, int64_t row,
-                                            int half, bool valid) {
-  if (valid) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(
-        static_cast<const uint8_t*>(codes) + row * 64 + 32 * half);
-    r.c0 = p[0];
-    r.c1 = p[1];
-    r.sc = *reinterpret_cast<const uint32_t*>(scales + row * 4);
-  } else {
-    r.c0 = u32x4{0, 0, 0, 0};
-    r.c1 = u32x4{0, 0, 0, 0};
-    r.sc = 0x7F7F7F7Fu;
-  }
+                                            int half) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(
+      static_cast<const uint8_t*>(codes) + row * 64 + 32 * half);
+  r.c0 = p[0];
+  r.c1 = p[1];
+  r.sc = *reinterpret_cast<const uint32_t*>(scales + row * 4);
 }
 
 template <>
 __device__ __forceinline__ void load_key<1>(RawKey<1>& r, const void* codes,
                                             const uint8_t*, int64_t row,
-                                            int half, bool valid) {
-  if (valid) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(codes) + row * 128 + 64 * half);
+                                            int half) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(
+      static_cast<const uint16_t*>(codes) + row * 128 + 64 * half);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) r.v[s] = p[s];
-  } else {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) r.v[s] = u32x4{0, 0, 0, 0};
-  }
+  for (int s = 0; s < 8; ++s) r.v[s] = p[s];
 }
 
 // B operand of step s: 8 dims 64h + 8s .. +7 of this lane's key, as bf16.
@@ -105,19 +97,9 @@ __device__ __forceinline__ bf16x8 key_operand<1>(const RawKey<1>& r, int s,
   return bits_to_bf8(r.v[s]);
 }
 
-// Row id and validity of tile position i of sequence b.
-__device__ __forceinline__ int64_t row_of(const int32_t* cand, int64_t n_rows,
-                                          int64_t n, int b, int64_t i,
-                                          bool& valid) {
-  if (cand == nullptr) {
-    valid = i < n;
-    return i;
-  }
-  int64_t e = -1;
-  if (i < n_rows) e = cand[(int64_t)b * n_rows + i];
-  valid = e >= 0 && e < n;
-  return e;
-}
+// Tiles of loads kept in flight ahead of the matrix work.
+template <int KEYFMT> struct Depth { static constexpr int value = 2; };
+template <> struct Depth<1> { static constexpr int value = 1; };
 
 template <int KEYFMT, bool TMAX>
 __global__ __launch_bounds__(256) void indexer_kernel(
@@ -126,14 +108,35 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const int32_t* __restrict__ cand, int64_t n_rows,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     float* __restrict__ scores, float* __restrict__ tmax) {
+  constexpr int D = Depth<KEYFMT>::value;
+  constexpr int T = kTilesPerWave;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int half = lane >> 5;
+  const int64_t base =
+      ((int64_t)blockIdx.x * kWaves + wave) * (kTilesPerWave * 32);
+  if (base >= n_rows) return;                  // wave-uniform; no barriers
   int64_t n = n_entries[b];
-  n = n < 0 ? 0 : (n > n_cap ? n_cap : n);        // never past the cache
+  n = n < 0 ? 0 : (n > n_cap ? n_cap : n);     // never past the cache
   const int64_t seq_base = (int64_t)b * n_cap;
+  const int nt = (int)((n_rows - base + 31) >> 5) < T
+                     ? (int)((n_rows - base + 31) >> 5) : T;
+
+  // Row of every tile position this lane will read (candidate ids first,
+  // all in one round), with validity; invalid rows are clamped to row 0.
+  int64_t row[T];
+  uint32_t vmask = 0;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t i = base + 32 * t + col;
+    int64_t e = i;
+    if (cand) e = cand[(int64_t)b * n_rows + (i < n_rows ? i : n_rows - 1)];
+    const bool v = i < n_rows && e >= 0 && e < n;
+    vmask |= (v ? 1u : 0u) << t;
+    row[t] = seq_base + (v ? e : 0);
+  }
 
   // A operand: head `col`, dims 64*half + 8*s .. +7 for step s.
   bf16x8 qa[8];
@@ -149,31 +152,19 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     for (int r = 0; r < 4; ++r)
       wr[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 * half + r];
 
-  const int64_t base =
-      ((int64_t)blockIdx.x * kWaves + wave) * (kTilesPerWave * 32);
-  // Rows past the visible range need no loads at all.
-  const int64_t scan_end = cand ? n_rows : (n < n_rows ? n : n_rows);
-
-  RawKey<KEYFMT> cur, nxt;
-  {
-    bool v;
-    const int64_t e = row_of(cand, n_rows, n, b, base + col, v);
-    load_key<KEYFMT>(cur, k_codes, k_scales, seq_base + e, half, v);
-  }
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int64_t tile = base + 32 * t;
-    if (tile >= n_rows) break;                       // wave-uniform
-    const int64_t i = tile + col;
-    bool valid;
-    row_of(cand, n_rows, n, b, i, valid);
-    // Prefetch the next tile before this one's matrix work.
-    if (t + 1 < kTilesPerWave && tile + 32 < scan_end) {
-      bool v2;
-      const int64_t e2 = row_of(cand, n_rows, n, b, i + 32, v2);
-      load_key<KEYFMT>(nxt, k_codes, k_scales, seq_base + e2, half, v2);
-    }
-    float total = -__builtin_inff();
-    if (tile < scan_end) {                           // wave-uniform
+  RawKey<KEYFMT> buf[D + 1];
+#pragma unroll
+  for (int t = 0; t < D; ++t)
+    load_key<KEYFMT>(buf[t], k_codes, k_scales, row[t], half);
+  float total[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (t + D < T)
+      load_key<KEYFMT>(buf[(t + D) % (D + 1)], k_codes, k_scales, row[t + D],
+                       half);
+    total[t] = -__builtin_inff();
+    if (t < nt && base + 32 * t < (cand ? n_rows : n)) {   // wave-uniform
+      const RawKey<KEYFMT>& cur = buf[t % (D + 1)];
       f32x16 acc = {};
 #pragma unroll
       for (int s = 0; s < 8; ++s)
@@ -183,17 +174,23 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) part += wr[j] * fmaxf(acc[j], 0.0f);
       const float sum = part + __shfl_xor(part, 32);
-      if (valid) total = sum;
+      if (vmask & (1u << t)) total[t] = sum;
     }
-    if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total;
+  }
+  // Stores after the loop keep the loads' wait counts static.
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (t >= nt) break;
+    const int64_t i = base + 32 * t + col;
+    if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
     if constexpr (TMAX) {
-      // Largest score of the tile (lanes of both halves hold the same 32).
-      float mx = total;
+      // Largest score of the tile (both lane halves hold the same 32).
+      float mx = total[t];
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      if (lane == 0) tmax[(int64_t)b * ((n_rows + 31) >> 5) + (tile >> 5)] = mx;
+      if (lane == 0)
+        tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
     }
-    cur = nxt;
   }
 }
 

@@ -27,17 +27,33 @@ struct SelSmem {
   int32_t bstar, cum_before;
 };
 
+// Wavefront inclusive prefix sum with DPP: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then row 15 -> rows 1 and 3 and lane 31 -> rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Wavefront min and max of unsigned keys (result in every lane).
+__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
+}
+
 // Block-wide exclusive prefix sum over threads; returns the block total.
 template <int NT, int NB>
 __device__ __forceinline__ int sel_excl_scan(int x, int& total,
                                              SelSmem<NT, NB>& sm) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan(x);
   if (lane == 63) sm.red[wv] = incl;
   __syncthreads();
   int before = 0, tot = 0;
@@ -56,11 +72,7 @@ template <int NT, int NB>
 __device__ __forceinline__ void sel_minmax(uint32_t& mn, uint32_t& mx,
                                            SelSmem<NT, NB>& sm) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  }
+  wave_minmax(mn, mx);
   if (lane == 0) { sm.kred[0][wv] = mn; sm.kred[1][wv] = mx; }
   __syncthreads();
   mn = sm.kred[0][0];

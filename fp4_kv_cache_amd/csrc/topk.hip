@@ -79,7 +79,7 @@ __device__ __forceinline__ int select_any(RowSmem& sm, int count, int k) {
   return select_dense<kPer>(sm, count, k);
 }
 
-// Streaming top-k into LDS: feeds src(i, key, id) for i < n (ids ascending
+// Streaming top-k into LDS: feeds src.load(i, value, id) for i < n (ids ascending
 // in i) through passes of up to kCap keys; afterwards key/id[0..count) hold
 // the winners in id order.
 template <typename Src>
@@ -98,19 +98,24 @@ __device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       constexpr int kH = kCap / kNT / 2;
-      uint32_t fk[kH];
+      float fv[kH];
       int32_t fi[kH];
 #pragma unroll
       for (int j = 0; j < kH; ++j) {
+        // Unconditional raw loads from a clamped index (n >= 1 whenever
+        // fill > 0); keys are formed only after every load is issued.
         const int s = (h * kH + j) * kNT + tid;
-        fk[j] = 0;
-        fi[j] = -1;
-        if (s >= count && s < count + fill) src(pos + (s - count), fk[j], fi[j]);
+        int64_t i = pos + (s - count);
+        i = i < 0 ? 0 : (i >= n ? (n > 0 ? n - 1 : 0) : i);
+        src.load(i, fv[j], fi[j]);
       }
 #pragma unroll
       for (int j = 0; j < kH; ++j) {
         const int s = (h * kH + j) * kNT + tid;
-        if (s >= count && s < count + fill) { sm.key[s] = fk[j]; sm.id[s] = fi[j]; }
+        if (s >= count && s < count + fill) {
+          sm.key[s] = fi[j] >= 0 ? score_key(fv[j]) : 0u;
+          sm.id[s] = fi[j];
+        }
       }
     }
     pos += fill;
@@ -120,22 +125,21 @@ __device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
   return count;
 }
 
-// Element sources for stream_select (ids ascending in i).
+// Element sources for stream_select (ids ascending in i): load(i, v, id)
+// reads the raw value and id of element i (always a valid index).
+template <bool HAS_IDS>
 struct ScoreSrc {                 // a score row; ids = positions or ids[]
   const float* row;
   const int32_t* idrow;
-  __device__ __forceinline__ void operator()(int64_t i, uint32_t& key,
-                                             int32_t& id) const {
-    const int32_t d = idrow ? idrow[i] : (int32_t)i;
-    key = d >= 0 ? score_key(row[i]) : 0u;
-    id = d;
+  __device__ __forceinline__ void load(int64_t i, float& v, int32_t& id) const {
+    v = row[i];
+    id = HAS_IDS ? idrow[i] : (int32_t)i;
   }
 };
 struct TileSrc {                  // tile maxima; ids = tile numbers
   const float* trow;
-  __device__ __forceinline__ void operator()(int64_t t, uint32_t& key,
-                                             int32_t& id) const {
-    key = score_key(trow[t]);
+  __device__ __forceinline__ void load(int64_t t, float& v, int32_t& id) const {
+    v = trow[t];
     id = (int32_t)t;
   }
 };
@@ -152,6 +156,7 @@ struct RowArgs {
   int32_t* out;             // [B][k * block]
 };
 
+template <bool HAS_IDS>
 __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
@@ -161,8 +166,8 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
     const int64_t nv = a.n_valid[b];
     len = nv < len ? (nv > 0 ? nv : 0) : len;
   }
-  const ScoreSrc from_scores{a.scores + (int64_t)b * a.ld,
-                             a.ids ? a.ids + (int64_t)b * a.ld : nullptr};
+  const ScoreSrc<HAS_IDS> from_scores{
+      a.scores + (int64_t)b * a.ld, HAS_IDS ? a.ids + (int64_t)b * a.ld : nullptr};
   const int64_t n_t = (len + 31) >> 5;
   int count = 0;
   bool pruned = a.tmax != nullptr && n_t > a.k;
@@ -198,18 +203,21 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
       int n_c = 0;
       for (int l0 = 0; l0 < n_list; l0 += kNT) {
         const int l = l0 + tid;
-        uint32_t kk[32];
+        const bool have = l < n_list;
+        const int64_t base = (int64_t)(have ? sm.tiles[l] : 0) * 32;
+        float vv[32];
         int32_t ii[32];
-        uint32_t fl = 0;
-        if (l < n_list) {
-          const int64_t base = (int64_t)sm.tiles[l] * 32;
 #pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            kk[j] = 0;
-            ii[j] = -1;
-            if (base + j < len) from_scores(base + j, kk[j], ii[j]);
-            if (kk[j] >= mk) fl |= 1u << j;
-          }
+        for (int j = 0; j < 32; ++j) {
+          const int64_t pos = base + j < len ? base + j : len - 1;   // len >= 1
+          from_scores.load(pos, vv[j], ii[j]);
+        }
+        uint32_t kk[32];
+        uint32_t fl = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          kk[j] = ii[j] >= 0 ? score_key(vv[j]) : 0u;
+          if (have && base + j < len && kk[j] >= mk) fl |= 1u << j;
         }
         int tot;
         int p = sel_excl_scan<kNT, kNB>(__popc(fl), tot, sm.sel);
@@ -279,10 +287,13 @@ hipError_t launch_row_select(const float* scores, const float* tmax,
                              const int32_t* limit, int32_t* out,
                              hipStream_t s) {
   if (B == 0) return hipSuccess;
-  static std::atomic<uint64_t> lds_set{0};
+  static std::atomic<uint64_t> lds_set0{0}, lds_set1{0};
   hipError_t e = ensure_lds_limit(
-      reinterpret_cast<const void*>(row_select_kernel), (int)sizeof(RowSmem),
-      lds_set);
+      reinterpret_cast<const void*>(row_select_kernel<false>),
+      (int)sizeof(RowSmem), lds_set0);
+  if (e != hipSuccess) return e;
+  e = ensure_lds_limit(reinterpret_cast<const void*>(row_select_kernel<true>),
+                       (int)sizeof(RowSmem), lds_set1);
   if (e != hipSuccess) return e;
   RowArgs a{};
   a.scores = scores;
@@ -294,8 +305,12 @@ hipError_t launch_row_select(const float* scores, const float* tmax,
   a.block = block;
   a.limit = limit;
   a.out = out;
-  hipLaunchKernelGGL(row_select_kernel, dim3((unsigned)B), dim3(kNT),
-                     sizeof(RowSmem), s, a);
+  if (ids)
+    hipLaunchKernelGGL(row_select_kernel<true>, dim3((unsigned)B), dim3(kNT),
+                       sizeof(RowSmem), s, a);
+  else
+    hipLaunchKernelGGL(row_select_kernel<false>, dim3((unsigned)B), dim3(kNT),
+                       sizeof(RowSmem), s, a);
   return hipGetLastError();
 }
 
