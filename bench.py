@@ -36,6 +36,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="counter-collection run: plain indexer launches on "
+                         "rotated cache replicas, then a float32 copy kernel "
+                         "of known size (read 256 MiB, write 256 MiB) to "
+                         "calibrate FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -199,6 +204,40 @@ def run_gpu(args, wl):
                 steps_run=steps_run)
 
 
+COPY_ELEMS = 64 << 20          # float32 elements of the calibration copy
+
+
+def run_pmc_pass(args, wl):
+    """Launch sequence for rocprofv3 --pmc: M plain indexer launches (the
+    roofline kernel, same arguments as the timed ones), then 4 copies
+    y = x * 1 over COPY_ELEMS float32 (a kernel whose HBM bytes are known:
+    4 * COPY_ELEMS read and written)."""
+    import torch
+    from fp4_kv_cache_amd import csa2, workload
+
+    dev = "cuda:0"
+    st = workload.build(wl, dev)
+    per_call = wl.B * algorithmic_bytes(wl)
+    R = args.replicas or max(1, math.ceil(2 * 256e6 / per_call) + 1)
+    reps, keep = replicate(st, R)
+    planes = [(st.idx_codes, st.idx_scales)] + [(t[2], t[3]) for t in keep]
+    scores = torch.empty((wl.B, wl.n), dtype=torch.float32, device=dev)
+    M = max(8, min(args.steps, 64))
+    for i in range(M):
+        c, sc = planes[i % R]
+        csa2.indexer_score(csa2.KEYS_MXFP4, c, sc, st.n_entries, st.q_idx,
+                           st.w, out=scores)
+    torch.cuda.synchronize()
+    x = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(4):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_pass": True, "indexer_launches": M,
+                      "indexer_algorithmic_bytes": indexer_bytes(wl),
+                      "copy_bytes_each_way": 4 * COPY_ELEMS}))
+
+
 def run_cpu(wl, budget_s):
     """The oracle as it stands, on a bounded sample of the same workload:
     whole sequences (indexer over all entries, exact top-k, gather and
@@ -252,6 +291,9 @@ def main():
         sys.exit(2)
     from fp4_kv_cache_amd.inputs import WORKLOADS
     wl = WORKLOADS[args.workload]
+    if args.pmc_pass:
+        run_pmc_pass(args, wl)
+        return
     g = run_gpu(args, wl)
     step_s = g["graph_s"] if g["graph_s"] is not None else g["eager_s"]
     value = wl.B / step_s

@@ -51,6 +51,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 constexpr int kMaxK = 2048;
 constexpr int kMaxBlock = 64;
 constexpr int64_t kMaxCap = INT32_MAX;
+// Attention gathers address rows by 32-bit byte offsets within a sequence.
+constexpr int64_t kMaxAttnCap = int64_t(1) << 24;
 
 // Workspace layout of csa2_sparse_attn_decode.
 struct DecodeLayout {
@@ -116,6 +118,9 @@ csa2_status check_attn_common(const uint8_t* main_codes,
     return fail(CSA2_ERR_UNSUPPORTED, "k must be in 1..%d (got %d)", kMaxK, k);
   if (n_cap < 0 || n_cap > kMaxCap)
     return fail(CSA2_ERR_INVALID_ARG, "n_cap must be in 0..2^31-1");
+  if (n_cap > kMaxAttnCap)
+    return fail(CSA2_ERR_UNSUPPORTED,
+                "attention needs n_cap <= 2^24 (got %lld)", (long long)n_cap);
   if (!(scale == scale) || scale == 0.0f)
     return fail(CSA2_ERR_INVALID_ARG, "scale must be a finite nonzero float");
   if (B == 0) return CSA2_OK;

@@ -92,48 +92,72 @@ struct AttnArgs {
 };
 
 // Raw gather registers for the 8 slots this lane dequantises in one tile.
+// They hold the loaded words untouched, so nothing waits for the loads
+// before the dequantisation that consumes them.
 struct Raw {
   uint32_t a[8];
   uint32_t c[8];
 };
 
-// Gather the raw bytes of the 8 slots this lane dequantises in one tile
-// (wavefront `quarter` owns slots {4q..4q+3, 16+4q..16+4q+3}, lane g owns
-// dims 8g..8g+7).  All top-k ids are loaded first; then every slot issues the
-// same two unconditional dword loads from a clamped (always valid) address:
+// Slot (within a tile) of this lane's e-th element: wavefront `quarter`
+// owns slots {4q..4q+3, 16+4q..16+4q+3}, lane g owns dims 8g..8g+7.
+__device__ __forceinline__ int slot_of(int quarter, int e) {
+  return e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
+}
+
+// Top-k ids of this wavefront's slots, loaded by every lane with a
+// per-lane (vector) load: a scalar load would share its wait counter with the
+// LDS reads of the products and stall them.  Lane l fetches slot (l & 7) of
+// tile `ta` (l < 8) or `tb` (l >= 8).  Slots past the chosen entries read a
+// clamped, always valid address; their value is unused.
+__device__ __forceinline__ int32_t load_ids(const AttnArgs& p, int b, int ta,
+                                            int tb, int quarter, int lane) {
+  const int slot = ((lane & 8) ? tb : ta) * kTile + slot_of(quarter, lane & 7);
+  return p.topk[(int64_t)b * p.k + (slot < p.k ? slot : 0)];
+}
+
+// Per-sequence bases of the gathered planes (wavefront-uniform).
+struct Bases {
+  const uint8_t* codes;    // main codes of the sequence
+  const uint8_t* scales;   // main scales of the sequence
+  const uint8_t* swa;      // window rows of the sequence
+};
+
+// Issue the two dword loads of each of this wavefront's 8 slots of `tile`:
 // main entry -> code dword + the dword holding its scale byte, window row ->
-// its 8 bytes.  With no load under a branch, loads of a tile stay in flight
-// together.  `kinds` records per slot 0 = empty, 1 = main entry, 2 = window.
-__device__ __forceinline__ void gather(const AttnArgs& p, int b, int tile,
-                                       int quarter, int g, int nswa, Raw& raw,
-                                       uint32_t& kinds) {
-  int32_t idv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
-    const int slot = tile * kTile + j;
-    idv[e] = p.topk[(int64_t)b * p.k + (slot < p.k ? slot : 0)];
-  }
+// its 8 bytes; `kinds` records per slot 0 = empty, 1 = main entry, 2 =
+// window row (empty slots read row 0).  Lane off+e (e < 8) holds slot e's
+// id in `idl` and works out that slot's byte offsets and kind with vector
+// arithmetic; each load then takes a uniform base plus a 32-bit lane offset
+// (row offsets within one sequence stay below 2^32 since n_cap <= 2^24).
+__device__ __forceinline__ void load_rows(const AttnArgs& p, const Bases& bs,
+                                          int tile, int quarter, int lane,
+                                          int nswa, int32_t idl, int off,
+                                          Raw& raw, uint32_t& kinds) {
+  const int g = lane;
+  const int slot_l = tile * kTile + slot_of(quarter, lane & 7);
+  const bool main_l = slot_l < p.k;
+  const bool ok_main = main_l && (uint32_t)idl < (uint32_t)p.n_cap;
+  const int rr = slot_l - p.k;
+  const bool ok_swa = !main_l && rr < nswa;
+  const uint32_t row = ok_main ? (uint32_t)idl : 0u;
+  const uint32_t srow = ok_swa ? (uint32_t)rr : 0u;
+  const uint32_t offa = main_l ? row * 256u : srow * 512u;
+  const uint32_t offc = main_l ? row * 32u : srow * 512u + 4u;
+  const uint32_t kind = ok_main ? 1u : (ok_swa ? 2u : 0u);
+  const uint32_t g4 = 4u * (uint32_t)g, g8 = 8u * (uint32_t)g;
+  const uint32_t gs = (uint32_t)((g >> 1) & ~3);
   kinds = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
-    const int slot = tile * kTile + j;
-    const bool is_main = slot < p.k;
-    const bool ok_main = is_main && idv[e] >= 0 && idv[e] < p.n_cap;
-    const int rr = slot - p.k;
-    const bool ok_swa = !is_main && rr < nswa;
-    const int64_t mrow = (int64_t)b * p.n_cap + (ok_main ? idv[e] : 0);
-    const int64_t srow = (int64_t)b * kWindow + (ok_swa ? rr : 0);
-    const uint8_t* pa = is_main ? p.main_codes + mrow * 256 + 4 * g
-                                : p.swa + srow * 512 + 8 * g;
-    const uint8_t* pc = is_main ? p.main_scales + mrow * 32 + ((g >> 1) & ~3)
-                                : pa + 4;
-    const uint32_t va = *reinterpret_cast<const uint32_t*>(pa);
-    const uint32_t vc = *reinterpret_cast<const uint32_t*>(pc);
-    raw.a[e] = va;
-    raw.c[e] = is_main ? (vc >> (8 * ((g >> 1) & 3))) & 0xFFu : vc;
-    kinds |= (ok_main ? 1u : (ok_swa ? 2u : 0u)) << (2 * e);
+    const bool is_main = tile * kTile + slot_of(quarter, e) < p.k;
+    const uint32_t oa = __builtin_amdgcn_readlane(offa, off + e);
+    const uint32_t oc = __builtin_amdgcn_readlane(offc, off + e);
+    kinds |= (uint32_t)__builtin_amdgcn_readlane(kind, off + e) << (2 * e);
+    const uint8_t* ba = is_main ? bs.codes : bs.swa;
+    const uint8_t* bc = is_main ? bs.scales : bs.swa;
+    raw.a[e] = *reinterpret_cast<const uint32_t*>(ba + (oa + (is_main ? g4 : g8)));
+    raw.c[e] = *reinterpret_cast<const uint32_t*>(bc + (oc + (is_main ? gs : g8)));
   }
 }
 
@@ -148,8 +172,9 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
     const uint32_t kind = (kinds >> (2 * e)) & 3u;
     if (kind == 1) {
       // (s, s) in fp16 from the E4M3 scale byte duplicated into two lanes.
+      const uint32_t sb = (raw.c[e] >> (8 * ((g >> 1) & 3))) & 0xFFu;
       const f16x2_t ss = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-          raw.c[e] * 0x101u, 1.0f, false);
+          sb * 0x101u, 1.0f, false);
       const uint32_t cw = raw.a[e];
       kd[e][0] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ss);
       kd[e][1] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ss);
@@ -169,7 +194,7 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
   _Float16* kt = buf;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
+    const int j = slot_of(quarter, e);
     u32x4 v = {kd[e][0], kd[e][1], kd[e][2], kd[e][3]};
     *reinterpret_cast<u32x4*>(kt + j * kKtStride + 8 * g) = v;
   }
@@ -191,7 +216,7 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
   if (g == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int j = e < 4 ? 4 * quarter + e : 16 + 4 * quarter + (e - 4);
+      const int j = slot_of(quarter, e);
       valid[j] = ((kinds >> (2 * e)) & 3u) != 0;
     }
   }
@@ -206,6 +231,127 @@ __device__ __forceinline__ bool map_workgroup(int id, int B, int S, int& b,
   b = xcd + 8 * (slot / S);
   split = slot % S;
   return b < B;
+}
+
+struct TileState {
+  f32x4 acc[32];           // O^T accumulators: dims 16*blk + 4*q4 + r
+  float m_run;             // exp2 reference point (log2 units)
+  float l_run;             // running sum of this lane's weights
+};
+
+// One key tile of the split.  P = parity of the tile within the split: LDS
+// buffer P holds its dequantised keys, raw[P] is free again (its rows went
+// to LDS at the end of the previous step) and receives the rows of tile
+// t+2, and raw[P^1] (rows of t+1) is dequantised into buffer P^1 once the
+// products have read buffer P.
+template <int P>
+__device__ __forceinline__ void tile_step(
+    const AttnArgs& p, const Bases& bs, int b, int t, int t1, int wave,
+    int lane, int nswa, int col, int q4, _Float16* bufs, int32_t* valid_base,
+    const f16x8_t (&qb)[16], Raw (&raw)[2], uint32_t (&kinds)[2],
+    int32_t& idn, TileState& st) {
+  // The ids of t+3 are issued before the rows of t+2: wait counts retire in
+  // order, so reading them next step does not wait for these rows.
+  const int tl = t1 - 1;
+  const int t3 = t + 3 < t1 ? t + 3 : tl;
+  const int32_t id3 = load_ids(p, b, t3, t3, wave, lane);
+  load_rows(p, bs, t + 2 < t1 ? t + 2 : tl, wave, lane, nswa, idn, 0, raw[P],
+            kinds[P]);
+  idn = id3;
+
+  const _Float16* kt = bufs + P * kBufElems;
+  const _Float16* vs = kt + kKtElems;
+  const int32_t* valid = valid_base + P * kTile;
+
+  // S^T = K Q^T for the 32 slots of this tile, as four independent
+  // accumulation chains (slot halves x even/odd k-steps).  Operands are read
+  // kAhead steps before their products, so LDS latency overlaps the
+  // matrix-core work (the scheduling barriers keep that order).
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  {
+    f32x4 s0b = {0.f, 0.f, 0.f, 0.f}, s1b = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kAhead = 3;
+    const _Float16* k0 = kt + col * kKtStride + 8 * q4;
+    const _Float16* k1 = k0 + 16 * kKtStride;
+    f16x8_t a0[kAhead], a1[kAhead];
+#pragma unroll
+    for (int s = 0; s < kAhead; ++s) {
+      a0[s] = *reinterpret_cast<const f16x8_t*>(k0 + 32 * s);
+      a1[s] = *reinterpret_cast<const f16x8_t*>(k1 + 32 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const f16x8_t c0 = a0[s % kAhead], c1 = a1[s % kAhead];
+      if (s + kAhead < 16) {
+        a0[s % kAhead] = *reinterpret_cast<const f16x8_t*>(k0 + 32 * (s + kAhead));
+        a1[s % kAhead] = *reinterpret_cast<const f16x8_t*>(k1 + 32 * (s + kAhead));
+      }
+      if (s & 1) {
+        s0b = __builtin_amdgcn_mfma_f32_16x16x32_f16(c0, qb[s], s0b, 0, 0, 0);
+        s1b = __builtin_amdgcn_mfma_f32_16x16x32_f16(c1, qb[s], s1b, 0, 0, 0);
+      } else {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(c0, qb[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(c1, qb[s], s1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s0 += s0b;
+    s1 += s1b;
+  }
+  // Logits in log2 units; lane holds slots 4*q4 + r and 16 + 4*q4 + r.
+  float x[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = valid[4 * q4 + r] ? s0[r] * p.scale_log2 : -__builtin_inff();
+    x[4 + r] = valid[16 + 4 * q4 + r] ? s1[r] * p.scale_log2 : -__builtin_inff();
+  }
+  float mt = x[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const bool bump = mt > st.m_run + kRescaleSlack;   // also true from -inf
+  if (__any(bump)) {
+    if (bump) {
+      const float alpha = (st.m_run == -__builtin_inff()) ? 0.0f
+                                                          : exp2f(st.m_run - mt);
+      st.l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) st.acc[i] *= alpha;
+      st.m_run = mt;
+    }
+  }
+  const float mref = st.m_run == -__builtin_inff() ? 0.0f : st.m_run;
+  f16x8_t pb;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pb[r] = (_Float16)exp2f(x[r] - mref);
+  // The running sum takes the same rounded weights the product uses.
+#pragma unroll
+  for (int r = 0; r < 8; ++r) st.l_run += (float)pb[r];
+
+  // O^T += V^T P^T.
+  {
+    constexpr int kAhead = 4;
+    const _Float16* v0 = vs + q4 * (512 * 8);
+    f16x8_t va[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+      va[i] = *reinterpret_cast<const f16x8_t*>(v0 + vs_phys(16 * i + col) * 8);
+#pragma unroll
+    for (int blk = 0; blk < 32; ++blk) {
+      const f16x8_t c = va[blk % kAhead];
+      if (blk + kAhead < 32)
+        va[blk % kAhead] = *reinterpret_cast<const f16x8_t*>(
+            v0 + vs_phys(16 * (blk + kAhead) + col) * 8);
+      st.acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c, pb, st.acc[blk], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (t + 1 < t1)
+    dequant_store(raw[P ^ 1], kinds[P ^ 1], wave, lane,
+                  bufs + (P ^ 1) * kBufElems, valid_base + (P ^ 1) * kTile);
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
@@ -227,95 +373,57 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   int t1 = t0 + p.tiles_per_split;
   if (t1 > p.n_tiles) t1 = p.n_tiles;
 
-  Raw raw;
-  uint32_t kinds = 0;
-  if (t0 < t1) gather(p, b, t0, wave, lane, nswa, raw, kinds);
-
+  // Gather pipeline: while tile t runs on the matrix cores, the rows of
+  // tiles t+1 and t+2 are in flight (a two-slot register ring, slot =
+  // parity of the tile within the split) and the ids of tile t+3 behind
+  // them.  Tile indices past the split are clamped to its last tile, so every
+  // load is unconditional and valid.
+  const Bases bs{p.main_codes + (int64_t)b * p.n_cap * 256,
+                 p.main_scales + (int64_t)b * p.n_cap * 32,
+                 p.swa + (int64_t)b * kWindow * 512};
+  const int tl = t1 - 1;
+  const int ta = t0 < t1 ? t0 : tl < 0 ? 0 : tl;
+  const int tb = t0 + 1 < t1 ? t0 + 1 : ta;
+  Raw raw[2];
+  uint32_t kinds[2] = {0u, 0u};
+  const int32_t id01 = load_ids(p, b, ta, tb, wave, lane);
+  int32_t idn = load_ids(p, b, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
+  // Loads are issued in the order they are consumed (wait counts retire in
+  // order): ids, rows of the first tile, the query, rows of the second.
+  load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
   // Q^T operand: head `head`, dims 32s + 8*q4 .. +7, converted to fp16.
-  f16x8_t qb[16];
+  bf16x8_t qraw[16];
   {
     const bf16x8_t* qr = reinterpret_cast<const bf16x8_t*>(
         p.q + ((int64_t)b * kHeads + head) * 512 + 8 * q4);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const bf16x8_t v = qr[4 * s];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)(float)v[j];
-    }
+    for (int s = 0; s < 16; ++s) qraw[s] = qr[4 * s];
   }
-  f32x4 acc[32];
+  load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
+  f16x8_t qb[16];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
+  for (int s = 0; s < 16; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)(float)qraw[s][j];
+  TileState st;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -__builtin_inff();
+  st.l_run = 0.0f;
 
-  if (t0 < t1) dequant_store(raw, kinds, wave, lane, bufs, valid_base);
+  if (t0 < t1) dequant_store(raw[0], kinds[0], wave, lane, bufs, valid_base);
   __syncthreads();
 
-  for (int t = t0; t < t1; ++t) {
-    const int cur = (t - t0) & 1;
-    const bool has_next = t + 1 < t1;
-    if (has_next) gather(p, b, t + 1, wave, lane, nswa, raw, kinds);
-
-    const _Float16* kt = bufs + cur * kBufElems;
-    const _Float16* vs = kt + kKtElems;
-    const int32_t* valid = valid_base + cur * kTile;
-
-    // S^T = K Q^T for the 32 slots of this tile.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const f16x8_t a0 = *reinterpret_cast<const f16x8_t*>(
-          kt + col * kKtStride + 32 * s + 8 * q4);
-      const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(
-          kt + (16 + col) * kKtStride + 32 * s + 8 * q4);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[s], s1, 0, 0, 0);
-    }
-    // Logits in log2 units; lane holds slots 4*q4 + r and 16 + 4*q4 + r.
-    float x[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = valid[4 * q4 + r] ? s0[r] * p.scale_log2 : -__builtin_inff();
-      x[4 + r] = valid[16 + 4 * q4 + r] ? s1[r] * p.scale_log2 : -__builtin_inff();
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool bump = mt > m_run + kRescaleSlack;   // also true from -inf
-    if (__any(bump)) {
-      if (bump) {
-        const float alpha = (m_run == -__builtin_inff()) ? 0.0f
-                                                         : exp2f(m_run - mt);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-        m_run = mt;
-      }
-    }
-    const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
-    f16x8_t pb;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) pb[r] = (_Float16)exp2f(x[r] - mref);
-    // The running sum takes the same rounded weights the product uses.
-#pragma unroll
-    for (int r = 0; r < 8; ++r) l_run += (float)pb[r];
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int blk = 0; blk < 32; ++blk) {
-      const f16x8_t va = *reinterpret_cast<const f16x8_t*>(
-          vs + q4 * (512 * 8) + vs_phys(16 * blk + col) * 8);
-      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[blk], 0, 0, 0);
-    }
-
-    if (has_next)
-      dequant_store(raw, kinds, wave, lane, bufs + (cur ^ 1) * kBufElems,
-                    valid_base + (cur ^ 1) * kTile);
-    __syncthreads();
+  for (int t = t0; t < t1; t += 2) {
+    tile_step<0>(p, bs, b, t, t1, wave, lane, nswa, col, q4, bufs, valid_base,
+                 qb, raw, kinds, idn, st);
+    if (t + 1 < t1)
+      tile_step<1>(p, bs, b, t + 1, t1, wave, lane, nswa, col, q4, bufs,
+                   valid_base, qb, raw, kinds, idn, st);
   }
+  f32x4 (&acc)[32] = st.acc;
+  const float m_run = st.m_run;
+  const float l_run = st.l_run;
 
   // Fold the running sums of the four lanes that share a head.
   float l_tot = l_run + __shfl_xor(l_run, 16);

@@ -42,6 +42,31 @@ struct RowSmem {
   SelSmem<kNT, kNB> sel;
 };
 
+// Lanes below this one in the wavefront.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// Exclusive prefix of a per-wavefront count over the wavefronts of the
+// block (the count is uniform within each wavefront); returns the total.
+__device__ __forceinline__ int wave_offset(int wcount, int& total,
+                                           SelSmem<kNT, kNB>& sm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) sm.red[0][wv] = (uint32_t)wcount;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kNT / 64; ++i) {
+    const int t = (int)sm.red[0][i];
+    before += i < wv ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return before;
+}
+
 // Top-k of the `count` (key, id) pairs held in sm.key/sm.id (ids in
 // order): the winners are compacted, still in id order, to the front.
 // Returns their number.  PER keys per thread; count <= kNT * PER.
@@ -55,11 +80,11 @@ __device__ __forceinline__ int select_dense(RowSmem& sm, int count, int k) {
     key[j] = pos < count ? sm.key[pos] : 0u;
   }
   const SelResult r = block_select<kNT, PER, kNB>(key, k, sm.sel);
-  int tot;
-  int p = sel_excl_scan<kNT, kNB>(__popc(r.mask), tot, sm.sel);
-  // In-order compaction of the winners (at most k <= kNB): keys come from
-  // registers; ids are staged through the histogram buffer (free after the
-  // selection) so no thread overwrites an id another has yet to read.
+  // In-order compaction of the winners (at most k <= kNB).  Every read of
+  // sm.key finished inside the selection, so keys go straight to their
+  // place; ids are staged through the (zero) histogram, which is cleared
+  // again behind them.
+  int p = r.pos;
 #pragma unroll
   for (int j = 0; j < PER; ++j)
     if (r.mask & (1u << j)) {
@@ -68,9 +93,12 @@ __device__ __forceinline__ int select_dense(RowSmem& sm, int count, int k) {
       ++p;
     }
   __syncthreads();
-  for (int q = tid; q < tot; q += kNT) sm.id[q] = sm.sel.hist[q];
+  for (int q = tid; q < r.total; q += kNT) {
+    sm.id[q] = sm.sel.hist[q];
+    sm.sel.hist[q] = 0;
+  }
   __syncthreads();
-  return tot;
+  return r.total;
 }
 
 __device__ __forceinline__ int select_any(RowSmem& sm, int count, int k) {
@@ -79,9 +107,9 @@ __device__ __forceinline__ int select_any(RowSmem& sm, int count, int k) {
   return select_dense<kPer>(sm, count, k);
 }
 
-// Streaming top-k into LDS: feeds src.load(i, value, id) for i < n (ids ascending
-// in i) through passes of up to kCap keys; afterwards key/id[0..count) hold
-// the winners in id order.
+// Streaming top-k into LDS: feeds src.load(i, value, id) for i < n (ids
+// ascending in i) through passes of up to kCap keys; afterwards
+// key/id[0..count) hold the winners in id order.
 template <typename Src>
 __device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
                                              Src src) {
@@ -156,11 +184,140 @@ struct RowArgs {
   int32_t* out;             // [B][k * block]
 };
 
+// Write chosen id `id` as output entry p (expanded by `block`, clipped).
+__device__ __forceinline__ void put(const RowArgs& a, int64_t ob, int64_t lim,
+                                    int p, int64_t id) {
+  for (int t = 0; t < a.block; ++t) {
+    const int64_t q = id * a.block + t;
+    a.out[ob + (int64_t)p * a.block + t] = q < lim ? (int32_t)q : -1;
+  }
+}
+
+// Final selection over the `count` candidates in sm.key/sm.id (ids in
+// order), written straight to the output at the positions the selection
+// gives.  Returns the number chosen.
+template <int PER>
+__device__ __forceinline__ int select_out(RowSmem& sm, int count,
+                                          const RowArgs& a, int64_t ob,
+                                          int64_t lim) {
+  const int tid = threadIdx.x;
+  uint32_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int pos = tid * PER + j;
+    key[j] = pos < count ? sm.key[pos] : 0u;
+  }
+  const SelResult r = block_select<kNT, PER, kNB>(key, a.k, sm.sel);
+  int p = r.pos;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (r.mask & (1u << j)) put(a, ob, lim, p++, sm.id[tid * PER + j]);
+  return r.total;
+}
+
+// Tile-pruned candidates (see the file comment), with the tile maxima held
+// in registers: thread t owns tiles TP*t .. TP*t+TP-1.  Leaves the
+// candidates (elements >= M of the tiles whose maximum is >= M) in
+// sm.key/sm.id in id order and returns their number, or -1 when they do
+// not fit (then the caller streams the whole row).
+template <int TP, bool HAS_IDS>
+__device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
+                                                 int64_t n_t, int64_t len,
+                                                 const ScoreSrc<HAS_IDS>& src,
+                                                 int k) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // (1) M = the k-th largest tile maximum (or a lower bound of it that no
+  // selected tile maximum undercuts).
+  uint32_t tk[TP];
+  {
+    float tv[TP];
+#pragma unroll
+    for (int j = 0; j < TP; ++j) {
+      const int64_t t = (int64_t)tid * TP + j;
+      tv[j] = trow[t < n_t ? t : n_t - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < TP; ++j)
+      tk[j] = (int64_t)tid * TP + j < n_t ? score_key(tv[j]) : 0u;
+  }
+  const uint32_t M = block_select<kNT, TP, kNB>(tk, k, sm.sel).thr;
+  if (M == 0) return 0;                       // no valid score at all
+  // (2) the tiles whose maximum is >= M, in order.
+  uint32_t fl = 0;
+#pragma unroll
+  for (int j = 0; j < TP; ++j)
+    if (tk[j] >= M) fl |= 1u << j;
+  int n_list;
+  int p = sel_excl_scan<kNT, kNB>(__popc(fl), n_list, sm.sel);
+  if (n_list > kTileList) return -1;
+#pragma unroll
+  for (int j = 0; j < TP; ++j)
+    if (fl & (1u << j)) sm.tiles[p++] = tid * TP + j;
+  __syncthreads();
+  // (3) their elements >= M.  A wavefront reads two listed tiles per load
+  // (lanes 0-31 and 32-63), kSteps loads in flight, and places its
+  // candidates in lane order, which is id order.
+  constexpr int kSteps = 16;
+  constexpr int kChunk = kNT / 64 * 2 * kSteps;     // listed tiles per round
+  int n_c = 0;
+  for (int c0 = 0; c0 < n_list; c0 += kChunk) {
+    float v[kSteps];
+    int32_t ii[kSteps];
+    int pos[kSteps];                                  // < 2^19 here
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int li = c0 + wv * 2 * kSteps + 2 * s + (lane >> 5);
+      const int tile = li < n_list ? sm.tiles[li] : 0;
+      pos[s] = tile * 32 + (lane & 31);
+      src.load(pos[s] < len ? pos[s] : len - 1, v[s], ii[s]);
+      if (li >= n_list) pos[s] = (int)len;            // marks "no element"
+    }
+    uint32_t kk[kSteps];
+    int wcount = 0;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const uint32_t key = pos[s] < len && ii[s] >= 0 ? score_key(v[s]) : 0u;
+      kk[s] = key >= M ? key : 0u;
+      wcount += __popcll(__ballot(kk[s] != 0));
+    }
+    int total;
+    int run = n_c + wave_offset(wcount, total, sm.sel);
+    if (n_c + total <= kCap) {
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const uint64_t m = __ballot(kk[s] != 0);
+        if (kk[s]) {
+          const int q = run + __popcll(m & lanemask_lt());
+          sm.key[q] = kk[s];
+          sm.id[q] = ii[s];
+        }
+        run += __popcll(m);
+      }
+    }
+    n_c += total;
+  }
+  __syncthreads();
+  return n_c <= kCap ? n_c : -1;
+}
+
+template <int TP, bool HAS_IDS>
+__device__ __forceinline__ int pruned_dispatch(RowSmem& sm, const float* trow,
+                                               int64_t n_t, int64_t len,
+                                               const ScoreSrc<HAS_IDS>& src,
+                                               int k) {
+  if constexpr (TP < kPer) {
+    if (n_t > (int64_t)kNT * TP)
+      return pruned_dispatch<TP * 2, HAS_IDS>(sm, trow, n_t, len, src, k);
+  }
+  return pruned_candidates<TP, HAS_IDS>(sm, trow, n_t, len, src, k);
+}
+
 template <bool HAS_IDS>
 __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
   const int b = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < kNB; i += kNT) sm.sel.hist[i] = 0;
   int64_t len = a.ld;
   if (a.n_valid) {
     const int64_t nv = a.n_valid[b];
@@ -168,87 +325,25 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   }
   const ScoreSrc<HAS_IDS> from_scores{
       a.scores + (int64_t)b * a.ld, HAS_IDS ? a.ids + (int64_t)b * a.ld : nullptr};
-  const int64_t n_t = (len + 31) >> 5;
-  int count = 0;
-  bool pruned = a.tmax != nullptr && n_t > a.k;
-  if (pruned) {
-    const float* trow = a.tmax + (int64_t)b * ((a.ld + 31) >> 5);
-    // (1) M = the k-th largest tile maximum.
-    const int ct = stream_select(sm, n_t, a.k, TileSrc{trow});
-    uint32_t mk = 0xFFFFFFFFu, dummy = 0u;
-    for (int p = tid; p < ct; p += kNT) mk = min(mk, sm.key[p]);
-    sel_minmax<kNT, kNB>(mk, dummy, sm.sel);
-    // (2) every tile whose maximum is >= M, in order (each thread scans a
-    // run of kPer tiles).
-    int n_list = 0;
-    for (int64_t t0 = 0; t0 < n_t; t0 += kCap) {
-      const int64_t tb = t0 + (int64_t)tid * kPer;
-      uint32_t fl = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (tb + j < n_t && score_key(trow[tb + j]) >= mk) fl |= 1u << j;
-      int tot;
-      int p = sel_excl_scan<kNT, kNB>(__popc(fl), tot, sm.sel);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (fl & (1u << j)) {
-          if (n_list + p < kTileList) sm.tiles[n_list + p] = (int32_t)(tb + j);
-          ++p;
-        }
-      n_list += tot;
-    }
-    __syncthreads();
-    // (3) the elements >= M of the listed tiles, densely, in id order.
-    if (n_list <= kTileList) {
-      int n_c = 0;
-      for (int l0 = 0; l0 < n_list; l0 += kNT) {
-        const int l = l0 + tid;
-        const bool have = l < n_list;
-        const int64_t base = (int64_t)(have ? sm.tiles[l] : 0) * 32;
-        float vv[32];
-        int32_t ii[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const int64_t pos = base + j < len ? base + j : len - 1;   // len >= 1
-          from_scores.load(pos, vv[j], ii[j]);
-        }
-        uint32_t kk[32];
-        uint32_t fl = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          kk[j] = ii[j] >= 0 ? score_key(vv[j]) : 0u;
-          if (have && base + j < len && kk[j] >= mk) fl |= 1u << j;
-        }
-        int tot;
-        int p = sel_excl_scan<kNT, kNB>(__popc(fl), tot, sm.sel);
-        if (n_c + tot <= kCap) {
-#pragma unroll
-          for (int j = 0; j < 32; ++j)
-            if (fl & (1u << j)) {
-              sm.key[n_c + p] = kk[j];
-              sm.id[n_c + p] = ii[j];
-              ++p;
-            }
-        }
-        n_c += tot;
-      }
-      __syncthreads();
-      if (n_c <= kCap) count = select_any(sm, n_c, a.k);
-      else pruned = false;     // (massive ties) fall back to a full pass
-    } else {
-      pruned = false;
-    }
-  }
-  if (!pruned) count = stream_select(sm, len, a.k, from_scores);
-  // Winners in id order -> out[b], expanded by `block` and clipped.
   const int64_t ob = (int64_t)b * a.k * a.block;
   const int64_t lim = a.limit ? (int64_t)a.limit[b] : INT64_MAX;
-  for (int p = tid; p < count; p += kNT) {
-    const int64_t id = sm.id[p];
-    for (int t = 0; t < a.block; ++t) {
-      const int64_t q = id * a.block + t;
-      a.out[ob + (int64_t)p * a.block + t] = q < lim ? (int32_t)q : -1;
+  const int64_t n_t = (len + 31) >> 5;
+  int count = -1;
+  if (a.tmax != nullptr && n_t > a.k && n_t <= (int64_t)kNT * kPer) {
+    const float* trow = a.tmax + (int64_t)b * ((a.ld + 31) >> 5);
+    const int n_c = pruned_dispatch<2, HAS_IDS>(sm, trow, n_t, len,
+                                                from_scores, a.k);
+    if (n_c >= 0) {
+      if (n_c <= kNT * 2) count = select_out<2>(sm, n_c, a, ob, lim);
+      else if (n_c <= kNT * 8) count = select_out<8>(sm, n_c, a, ob, lim);
+      else count = select_out<kPer>(sm, n_c, a, ob, lim);
     }
+  }
+  if (count < 0) {
+    // Whole-row streaming (short rows, or candidates that overflow).
+    __syncthreads();
+    count = stream_select(sm, len, a.k, from_scores);
+    for (int p = tid; p < count; p += kNT) put(a, ob, lim, p, sm.id[p]);
   }
   for (int64_t p = (int64_t)count * a.block + tid; p < (int64_t)a.k * a.block;
        p += kNT)

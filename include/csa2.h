@@ -190,8 +190,9 @@ csa2_status csa2_topk(const float *scores, int64_t ld, const int32_t *n_valid,
  *   k         1..2048 (512 in the pages)
  *   out       [B][64][512] bf16 (16-byte aligned)
  *   topk_out  [B][k] chosen ids ascending, -1 padded (for Reuse layers)
- * Softmax and accumulation are float32; probabilities enter the P.V
- * product as bf16. */
+ *   n_cap     <= 2^24 here (CSA2_ERR_UNSUPPORTED beyond)
+ * Keys/values are dequantised exactly (to fp16); logits, softmax and
+ * accumulation are float32; probabilities enter the P.V product as fp16. */
 csa2_status csa2_sparse_attn_decode(const csa2_cache *kv,
                                     const uint16_t *q_idx, const float *w,
                                     const uint16_t *q, const uint8_t *swa,
