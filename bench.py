@@ -44,19 +44,29 @@ def parse():
     return ap.parse_args()
 
 
+def n_blocks(wl):
+    return -(-wl.n // wl.pool[1]) if wl.pool else 0
+
+
 def algorithmic_bytes(wl):
     """Bytes the method must move for one query through a Full layer:
-    68 n (indexer keys) + 288 k (chosen main entries) + 512 n_swa (window)
-    + 8192 (bf16 indexer query) + 128 (head weights) + 65536 (bf16 query)
-    + 65536 (bf16 output) + 4 k (top-k ids written)."""
-    return (68 * wl.n + 288 * wl.k + 512 * wl.n_swa + 8192 + 128 + 65536
+    the indexer keys scanned (68 n; hierarchically 256 per bf16 block key
+    plus 68 per pool member), 288 k (chosen main entries), 512 n_swa
+    (window), 8192 (bf16 indexer query) + 128 (head weights), 65536 (bf16
+    query), 65536 (bf16 output) and 4 k (top-k ids written)."""
+    scan = (256 * n_blocks(wl) + 68 * wl.pool[0] * wl.pool[1] if wl.pool
+            else 68 * wl.n)
+    return (scan + 288 * wl.k + 512 * wl.n_swa + 8192 + 128 + 65536
             + 65536 + 4 * wl.k)
 
 
 def indexer_bytes(wl):
-    """Algorithmic bytes of one indexer launch: the MXFP4 keys of every
-    visible entry plus the per-sequence query and weights."""
-    return wl.B * (68 * wl.n + 8192 + 128)
+    """Algorithmic bytes of one launch of the scan kernel the roofline is
+    quoted on: the MXFP4 keys of every visible entry (hierarchically: the
+    bf16 block keys of every block) plus the per-sequence query and
+    weights."""
+    per = 256 * n_blocks(wl) if wl.pool else 68 * wl.n
+    return wl.B * (per + 8192 + 128)
 
 
 def source_hash():
@@ -81,18 +91,22 @@ def traffic_from_profile(launch_bytes_alg):
 
 
 def replicate(st, R):
-    """R independent copies of the caches (same contents)."""
+    """R independent copies of the caches (same contents); each entry of
+    `planes` is (main codes, main scales, idx codes, idx scales, block keys
+    or None)."""
     import torch
     from fp4_kv_cache_amd import csa2
     reps = [st.cache]
-    keep = []
+    planes = [(st.main_codes, st.main_scales, st.idx_codes, st.idx_scales,
+               st.block_keys)]
     for _ in range(R - 1):
-        t = [st.main_codes.clone(), st.main_scales.clone(),
-             st.idx_codes.clone(), st.idx_scales.clone()]
-        keep.append(t)
-        reps.append(csa2.cache_desc(*t, st.n_entries))
+        t = (st.main_codes.clone(), st.main_scales.clone(),
+             st.idx_codes.clone(), st.idx_scales.clone(),
+             None if st.block_keys is None else st.block_keys.clone())
+        planes.append(t)
+        reps.append(csa2.cache_desc(*t[:4], st.n_entries, block_keys=t[4]))
     torch.cuda.synchronize()
-    return reps, keep
+    return reps, planes
 
 
 def run_gpu(args, wl):
@@ -103,16 +117,17 @@ def run_gpu(args, wl):
     st = workload.build(wl, dev)
     per_call = wl.B * algorithmic_bytes(wl)
     R = args.replicas or max(1, math.ceil(2 * 256e6 / per_call) + 1)
-    reps, keep = replicate(st, R)
+    reps, planes = replicate(st, R)
     k = wl.k
     out = torch.empty((wl.B, 64, 512), dtype=torch.bfloat16, device=dev)
     ids = torch.empty((wl.B, k), dtype=torch.int32, device=dev)
-    ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, wl.B, wl.n, k), dev)
+    ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, wl.B, wl.n, k,
+                                            wl.pool), dev)
 
     def step(i):
         csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
-                                st.swa[0], st.n_swa, k, st.scale, out=out,
-                                topk_out=ids, ws=ws)
+                                st.swa[0], st.n_swa, k, st.scale,
+                                pool=wl.pool, out=out, topk_out=ids, ws=ws)
 
     # -- eager
     for i in range(args.warmup):
@@ -163,21 +178,36 @@ def run_gpu(args, wl):
     # kernels through the component calls, M back-to-back launches of one
     # kernel queued behind a spin kernel (so host enqueue time is hidden),
     # rotated over the replicas.
-    scores = torch.empty((wl.B, wl.n), dtype=torch.float32, device=dev)
-    tk_ws = csa2.workspace(csa2.workspace_size(csa2.OP_TOPK, wl.B, wl.n, k), dev)
+    # The scan kernel: the MXFP4 indexer over every entry, or, for the
+    # hierarchical workload, the bf16 block-key scan (its top-k keeps
+    # n_keep blocks expanded by the block size).
+    if wl.pool:
+        ld = n_blocks(wl)
+        nvalid = torch.full((wl.B,), ld, dtype=torch.int32, device=dev)
+        tk_k, tk_block = min(wl.pool[0], ld), wl.pool[1]
+    else:
+        ld, nvalid, tk_k, tk_block = wl.n, st.n_entries, k, 1
+    scores = torch.empty((wl.B, ld), dtype=torch.float32, device=dev)
+    tk_out = torch.empty((wl.B, tk_k * tk_block), dtype=torch.int32, device=dev)
+    tk_ws = csa2.workspace(csa2.workspace_size(csa2.OP_TOPK, wl.B, ld, tk_k), dev)
     at_ws = csa2.workspace(csa2.workspace_size(csa2.OP_REUSE, wl.B, wl.n, k), dev)
-    idx_planes = [(st.idx_codes, st.idx_scales)] + [(t[2], t[3]) for t in keep]
-    main_planes = [(st.main_codes, st.main_scales)] + [(t[0], t[1]) for t in keep]
 
     def k_idx(r):
-        csa2.indexer_score(csa2.KEYS_MXFP4, idx_planes[r][0], idx_planes[r][1],
-                           st.n_entries, st.q_idx, st.w, out=scores)
+        pl = planes[r]
+        if wl.pool:
+            csa2.indexer_score(csa2.KEYS_BF16, pl[4], None, nvalid, st.q_idx,
+                               st.w, out=scores)
+        else:
+            csa2.indexer_score(csa2.KEYS_MXFP4, pl[2], pl[3], nvalid,
+                               st.q_idx, st.w, out=scores)
 
     def k_topk(r):
-        csa2.topk(scores, k, n_valid=st.n_entries, out=ids, ws=tk_ws)
+        csa2.topk(scores, tk_k, n_valid=nvalid, block=tk_block,
+                  limit=st.n_entries if wl.pool else None, out=tk_out,
+                  ws=tk_ws)
 
     def k_attn(r):
-        csa2.reuse_attn(main_planes[r][0], main_planes[r][1], ids, st.q[0],
+        csa2.reuse_attn(planes[r][0], planes[r][1], ids, st.q[0],
                         st.swa[0], st.n_swa, st.scale, out=out, ws=at_ws)
 
     def timed(fn, M):
@@ -219,14 +249,13 @@ def run_pmc_pass(args, wl):
     st = workload.build(wl, dev)
     per_call = wl.B * algorithmic_bytes(wl)
     R = args.replicas or max(1, math.ceil(2 * 256e6 / per_call) + 1)
-    reps, keep = replicate(st, R)
-    planes = [(st.idx_codes, st.idx_scales)] + [(t[2], t[3]) for t in keep]
+    reps, planes = replicate(st, R)
     scores = torch.empty((wl.B, wl.n), dtype=torch.float32, device=dev)
     M = max(8, min(args.steps, 64))
     for i in range(M):
-        c, sc = planes[i % R]
-        csa2.indexer_score(csa2.KEYS_MXFP4, c, sc, st.n_entries, st.q_idx,
-                           st.w, out=scores)
+        pl = planes[i % R]
+        csa2.indexer_score(csa2.KEYS_MXFP4, pl[2], pl[3], st.n_entries,
+                           st.q_idx, st.w, out=scores)
     torch.cuda.synchronize()
     x = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
@@ -262,16 +291,30 @@ def run_cpu(wl, budget_s):
             qi, w = bits(qi), w.cpu().numpy()
             # Packing is the write path (untimed); only the main rows this
             # query will read need packing, found by an untimed oracle pass.
-            sel = O.topk(O.indexer_scores(qi, w, O.unpack_idx(ic, isc)), wl.k)
+            if wl.pool:
+                bk = O.block_keys(ic, isc, wl.n, wl.pool[1])
+                sel = O.hier_layer(np.zeros((wl.n, 256), np.uint8),
+                                   np.zeros((wl.n, 32), np.uint8), ic, isc, bk,
+                                   wl.n, qi, w, q, sw, wl.n_swa, wl.k, 1.0,
+                                   n_keep=wl.pool[0], block=wl.pool[1])[0]
+            else:
+                sel = O.topk(O.indexer_scores(qi, w, O.unpack_idx(ic, isc)),
+                             wl.k)
             sel = sel[sel >= 0]
             lat = inputs.main_latents(wl, b, 0, wl.n, dev)[
                 torch.from_numpy(sel).to(dev)].cpu().numpy()
             mc = np.zeros((wl.n, 256), np.uint8)
             ms = np.zeros((wl.n, 32), np.uint8)
             mc[sel], ms[sel] = O.pack_main(lat)
+            scale = float(np.float32(1 / math.sqrt(512)))
             t0 = time.perf_counter()
-            O.full_layer(mc, ms, ic, isc, wl.n, qi, w, q, sw, wl.n_swa, wl.k,
-                         float(np.float32(1 / math.sqrt(512))))
+            if wl.pool:
+                O.hier_layer(mc, ms, ic, isc, bk, wl.n, qi, w, q, sw,
+                             wl.n_swa, wl.k, scale, n_keep=wl.pool[0],
+                             block=wl.pool[1])
+            else:
+                O.full_layer(mc, ms, ic, isc, wl.n, qi, w, q, sw, wl.n_swa,
+                             wl.k, scale)
             spent += time.perf_counter() - t0
             done += 1
             if spent >= budget_s:
@@ -279,7 +322,7 @@ def run_cpu(wl, budget_s):
     return dict(value=done / spent, unit="query-tokens/s", cores=cores,
                 kind="oracle",
                 sample=f"{done} of {wl.B} sequences of {wl.name} "
-                       f"(full layer each, {spent:.1f} s, float64 NumPy, "
+                       f"({'hierarchical' if wl.pool else 'full'} layer each, {spent:.1f} s, float64 NumPy, "
                        f"BLAS threads={cores}, cpu={platform.processor() or 'x86_64'})")
 
 
@@ -299,7 +342,9 @@ def main():
     value = wl.B / step_s
     idx_alg = indexer_bytes(wl)
     achieved = idx_alg / g["t_idx"] / 1e9
-    traffic = traffic_from_profile(idx_alg)
+    traffic = traffic_from_profile(idx_alg) if args.workload == 1 else None
+    scan = ("indexer_kernel<1> (bf16 block-key scan)" if wl.pool
+            else "indexer_kernel<0> (MXFP4 scan)")
     line = {
         "metric": "CSA2 decode query-tokens/s per layer at 64K ctx; "
                   "achieved HBM GB/s vs peak",
@@ -318,13 +363,14 @@ def main():
                    "entries_per_seq": wl.n, "context": wl.ctx, "m": wl.m,
                    "k": wl.k, "n_swa": wl.n_swa, "heads": 64,
                    "head_dim": 512, "indexer": "32 heads x 128, MXFP4",
+                   "pool": list(wl.pool) if wl.pool else None,
                    "cache_replicas": g["replicas"],
                    "launch": "hip-graph" if g["graph_s"] else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "indexer_kernel<0> (MXFP4 scan)",
+                     "kernel": scan,
                      "algorithmic_bytes_per_launch": idx_alg,
                      "avg_launch_us": g["t_idx"] * 1e6},
         "step_hbm": {"algorithmic_bytes": g["per_call"],

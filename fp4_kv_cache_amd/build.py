@@ -28,11 +28,16 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
+# Per-source additions.  The indexer keeps its matrix-core accumulators in
+# ordinary VGPRs (no accumulator-register copies before the per-lane
+# epilogue), which also brings it to 128 VGPRs: four waves per SIMD.
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _compile(src):
     out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src),
-                             "-o", out]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + [
+        "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

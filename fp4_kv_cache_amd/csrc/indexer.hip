@@ -97,6 +97,24 @@ __device__ __forceinline__ bf16x8 key_operand<1>(const RawKey<1>& r, int s,
   return bits_to_bf8(r.v[s]);
 }
 
+// Largest value over the wavefront (DPP row shifts and broadcasts; lanes
+// without a source keep their own value), read from lane 63.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                      __float_as_int(v), __float_as_int(v), CTRL, RMASK, 0xf,
+                      false)));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = dpp_fmax<0x111, 0xf>(v);     // row_shr:1
+  v = dpp_fmax<0x112, 0xf>(v);     // row_shr:2
+  v = dpp_fmax<0x114, 0xf>(v);     // row_shr:4
+  v = dpp_fmax<0x118, 0xf>(v);     // row_shr:8
+  v = dpp_fmax<0x142, 0xa>(v);     // row_bcast:15
+  v = dpp_fmax<0x143, 0xc>(v);     // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Tiles of loads kept in flight ahead of the matrix work.
 template <int KEYFMT> struct Depth { static constexpr int value = 2; };
 template <> struct Depth<1> { static constexpr int value = 1; };
@@ -170,10 +188,19 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       for (int s = 0; s < 8; ++s)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             qa[s], key_operand<KEYFMT>(cur, s, half), acc, 0, 0, 0);
-      float part = 0.0f;
+      // ReLU as an integer max on the float bits (negatives and -0 go to
+      // +0; the dots are finite), weights, and the head sum in two chains.
+      float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) part += wr[j] * fmaxf(acc[j], 0.0f);
-      const float sum = part + __shfl_xor(part, 32);
+      for (int j = 0; j < 16; j += 2) {
+        p0 += wr[j] * __int_as_float(max(__float_as_int(acc[j]), 0));
+        p1 += wr[j + 1] * __int_as_float(max(__float_as_int(acc[j + 1]), 0));
+      }
+      // Fold the lane halves (dims 0-63 and 64-127 of the same entry):
+      // the swap gives every lane both halves, added in the same order.
+      const auto hv = __builtin_amdgcn_permlane32_swap(
+          __float_as_uint(p0 + p1), __float_as_uint(p0 + p1), false, false);
+      const float sum = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
       if (vmask & (1u << t)) total[t] = sum;
     }
   }
@@ -185,9 +212,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
     if constexpr (TMAX) {
       // Largest score of the tile (both lane halves hold the same 32).
-      float mx = total[t];
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float mx = wave_max_f32(total[t]);
       if (lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
     }

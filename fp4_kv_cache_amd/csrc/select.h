@@ -6,14 +6,16 @@
 // score_key() canonicalises -0 to +0 so that equal scores have equal keys.
 //
 // The k-th key is found by narrowing a key interval [lo, hi] that holds it.
-// The keys inside are binned by (hi - key) >> shift, with the shift chosen so
-// the interval fits NB bins; one wavefront scans the bin counts for the bin
-// where the running count from the top reaches the number still needed (and
-// clears the bins for the next pass), and the interval becomes exactly that
-// bin's key range.  With NB = 2048 a 32-bit range needs at most three passes
-// (21, then 10, then 0 bits left).  The search ends with the bin holding
-// exactly the number needed (take every key >= lo) or with a one-key
-// interval (keys above it, plus the first `need` keys equal to it in
+// Each pass bins the keys inside by (hi - key) >> shift into NB = 256 bins,
+// with the shift chosen so the interval fits; every wavefront counts into a
+// histogram of its own (spreading the LDS atomics), and wavefront 0 sums the
+// per-wave counts (one 16-byte read per lane and wave), finds with one
+// prefix scan the bin where the running count from the top reaches the
+// number still needed, clears the histograms for the next pass, and the
+// interval becomes exactly that bin's key range.  A 32-bit range needs at
+// most four passes (24, 16, 8, then 0 bits left).  The search ends with the
+// bin holding exactly the number needed (take every key >= lo) or with a
+// one-key interval (keys above it, plus the first `need` keys equal to it in
 // position order).  One packed prefix sum then yields every selected
 // element's output position.  Reductions and scans inside a wavefront use
 // DPP row shifts and broadcasts.
@@ -24,8 +26,9 @@ namespace csa2 {
 
 template <int NT, int NB>
 struct SelSmem {
-  static_assert((NB & (NB - 1)) == 0 && NB >= 256, "NB is a power of two");
-  int32_t hist[NB];
+  static_assert(NB == 256, "the bin scan assumes 4 bins per lane");
+  int32_t hist[NT / 64][NB];      // per-wavefront bin counts (all zero
+                                  // between calls)
   uint32_t red[4][NT / 64];
   int32_t bstar, cum_before, bcount;
 };
@@ -85,30 +88,38 @@ __device__ __forceinline__ int sel_excl_scan(int x, int& total,
 }
 
 // Canonical key of a score: NaN and -inf -> 0 (invalid), -0 -> key(+0).
+// Written with selects only (no branches), so unrolled uses stay
+// straight-line code.
 __device__ __forceinline__ uint32_t score_key(float v) {
-  if (!(v > -__builtin_inff())) return 0u;
-  if (v == 0.0f) v = 0.0f;
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  uint32_t u = __float_as_uint(v);
+  u = (u << 1) ? u : 0u;                                   // -0 -> +0
+  const uint32_t key = (int32_t)u < 0 ? ~u : (u | 0x80000000u);
+  return v > -__builtin_inff() ? key : 0u;
 }
 
 struct SelResult {
   uint32_t mask;      // selected elements of this thread (bit j)
   int pos;            // selected elements before this thread
   int total;          // selected in the block: min(k, valid keys)
-  uint32_t thr;       // every selected key is >= thr, and thr is <= the
-                      // smallest selected key (0 when nothing is selected)
+  uint32_t thr;       // every selected key is >= thr, thr is <= the
+                      // smallest selected key, and at least min(k, valid)
+                      // keys are >= thr (0 when no key is valid)
 };
 
 // Select the top-k (k >= 1) of the NT * PER keys held as key[j] by each
-// thread.  The histogram must be all zero on entry; it is all zero again on
-// return, and every shared-memory access of the call has completed.
-template <int NT, int PER, int NB>
+// thread.  The histograms must be all zero on entry; they are all zero again
+// on return, and every shared-memory access of the call has completed.
+// BOUND_ONLY: stop after `passes` passes and return only `thr` (a lower bound
+// of the k-th key with at least k keys at or above it); mask, pos and total
+// are then not set.
+template <int NT, int PER, int NB, bool BOUND_ONLY = false>
 __device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
-                                                  int k, SelSmem<NT, NB>& sm) {
+                                                  int k, SelSmem<NT, NB>& sm,
+                                                  int passes = 4) {
   static_assert(PER <= 32, "selection mask is 32 bits");
   static_assert(NT * PER < 65536, "packed counts are 16 bits");
-  constexpr int kLogNB = __builtin_ctz(NB);
+  constexpr int kLogNB = 8;
+  constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   // Valid count, min and max in one reduction.
@@ -129,7 +140,7 @@ __device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
     __syncthreads();
     nval = 0;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) {
+    for (int i = 0; i < kWaves; ++i) {
       nval += (int)sm.red[1][i];
       mn = min(mn, sm.red[2][i]);
       mx = max(mx, sm.red[3][i]);
@@ -140,39 +151,40 @@ __device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
   int need = k;
   bool take_all = nval <= k;              // select every valid key >= lo
   if (!take_all) {
-    for (int it = 0; it < 3 && lo < hi; ++it) {
+    int32_t* H = sm.hist[wv];
+    for (int it = 0; it < passes && lo < hi; ++it) {
       const int bits = 32 - __builtin_clz(hi - lo);
       const int shift = bits > kLogNB ? bits - kLogNB : 0;
 #pragma unroll
       for (int j = 0; j < PER; ++j)
-        if (key[j] >= lo && key[j] <= hi)
-          atomicAdd(&sm.hist[(hi - key[j]) >> shift], 1);
+        if ((key[j] >= lo) & (key[j] <= hi))
+          atomicAdd(&H[(hi - key[j]) >> shift], 1);
       __syncthreads();
       if (wv == 0) {
-        // Wavefront 0 reads the bins (lane L owns bins 32L .. 32L+31, in
-        // key order from the top), clears them and finds the crossing.
-        constexpr int BPL = NB / 64;
-        int cnt[BPL];
-        int s = 0;
+        // Lane L sums bins 4L .. 4L+3 over the per-wave histograms (bins
+        // in key order from the top) and clears them.
+        int4 c = make_int4(0, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < BPL; i += 4) {
-          int4* p = reinterpret_cast<int4*>(&sm.hist[lane * BPL + i]);
+        for (int w = 0; w < kWaves; ++w) {
+          int4* p = reinterpret_cast<int4*>(&sm.hist[w][4 * lane]);
           const int4 v = *p;
-          cnt[i] = v.x; cnt[i + 1] = v.y; cnt[i + 2] = v.z; cnt[i + 3] = v.w;
-          s += v.x + v.y + v.z + v.w;
+          c.x += v.x; c.y += v.y; c.z += v.z; c.w += v.w;
           *p = make_int4(0, 0, 0, 0);
         }
-        int run = wave_incl_scan(s) - s;
+        const int s = c.x + c.y + c.z + c.w;
+        const int run = wave_incl_scan(s) - s;
         if (run < need && run + s >= need) {
-#pragma unroll
-          for (int i = 0; i < BPL; ++i) {
-            if (run < need && run + cnt[i] >= need) {
-              sm.bstar = lane * BPL + i;
-              sm.cum_before = run;
-              sm.bcount = cnt[i];
+          int b = 0, before = run, cnt = c.x;
+          if (before + c.x < need) {
+            before += c.x; b = 1; cnt = c.y;
+            if (before + c.y < need) {
+              before += c.y; b = 2; cnt = c.z;
+              if (before + c.z < need) { before += c.z; b = 3; cnt = c.w; }
             }
-            run += cnt[i];
           }
+          sm.bstar = 4 * lane + b;
+          sm.cum_before = before;
+          sm.bcount = cnt;
         }
       }
       __syncthreads();
@@ -187,38 +199,43 @@ __device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
       if (exact) { take_all = true; break; }
     }
   }
-  // Selected: take_all -> key >= lo; else key > hi (= lo) plus the first
-  // `need` keys equal to lo.  One packed scan (ties << 16 | greater) gives
-  // both counts before this thread.
-  int ngt = 0, ntie = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (!key[j]) continue;
-    if (take_all) ngt += key[j] >= lo;
-    else { ngt += key[j] > hi; ntie += key[j] == lo; }
-  }
-  int tot;
-  const int ex = sel_excl_scan<NT, NB>((ntie << 16) | ngt, tot, sm);
-  const int gt_before = ex & 0xFFFF, tie_before = ex >> 16;
-  int tie_rank = tie_before;
-  uint32_t mask = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    bool s = false;
-    if (key[j]) {
-      if (take_all) s = key[j] >= lo;
-      else if (key[j] > hi) s = true;
-      else if (key[j] == lo) { s = tie_rank < need; ++tie_rank; }
-    }
-    if (s) mask |= 1u << j;
-  }
   SelResult res;
-  res.mask = mask;
-  res.pos = gt_before + (take_all ? 0 : min(tie_before, need));
-  const int tot_gt = tot & 0xFFFF, tot_tie = tot >> 16;
-  res.total = tot_gt + (take_all ? 0 : min(tot_tie, need));
   res.thr = nval ? lo : 0u;
-  return res;
+  if constexpr (BOUND_ONLY) {
+    res.mask = 0; res.pos = 0; res.total = 0;
+    return res;
+  } else {
+    // Selected: take_all -> key >= lo; else key > hi (= lo) plus the first
+    // `need` keys equal to lo.  One packed scan (ties << 16 | greater)
+    // gives both counts before this thread.
+    int ngt = 0, ntie = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (!key[j]) continue;
+      if (take_all) ngt += key[j] >= lo;
+      else { ngt += key[j] > hi; ntie += key[j] == lo; }
+    }
+    int tot;
+    const int ex = sel_excl_scan<NT, NB>((ntie << 16) | ngt, tot, sm);
+    const int gt_before = ex & 0xFFFF, tie_before = ex >> 16;
+    int tie_rank = tie_before;
+    uint32_t mask = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      bool s = false;
+      if (key[j]) {
+        if (take_all) s = key[j] >= lo;
+        else if (key[j] > hi) s = true;
+        else if (key[j] == lo) { s = tie_rank < need; ++tie_rank; }
+      }
+      if (s) mask |= 1u << j;
+    }
+    res.mask = mask;
+    res.pos = gt_before + (take_all ? 0 : min(tie_before, need));
+    const int tot_gt = tot & 0xFFFF, tot_tie = tot >> 16;
+    res.total = tot_gt + (take_all ? 0 : min(tot_tie, need));
+    return res;
+  }
 }
 
 }  // namespace csa2

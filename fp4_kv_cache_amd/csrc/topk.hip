@@ -31,9 +31,10 @@ namespace {
 constexpr int kNT = 512;                    // threads per row
 constexpr int kPer = 32;                    // keys per thread
 constexpr int kCap = kNT * kPer;            // 16384 keys per pass
-constexpr int kNB = 2048;
+constexpr int kNB = 256;                    // bins per selection pass
 constexpr int kTileList = 4096;             // candidate tiles held in LDS
-static_assert(kNB >= 2048, "winners (k <= 2048) are staged in the histogram");
+// Winners (k <= 2048) are staged in the histograms between selections.
+static_assert(kNT / 64 * kNB >= 2048, "staging room for 2048 winners");
 
 struct RowSmem {
   uint32_t key[kCap];
@@ -75,27 +76,32 @@ __device__ __forceinline__ int select_dense(RowSmem& sm, int count, int k) {
   const int tid = threadIdx.x;
   uint32_t key[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
+  for (int j = 0; j < PER; ++j) {       // unconditional reads, then masks
     const int pos = tid * PER + j;
-    key[j] = pos < count ? sm.key[pos] : 0u;
+    const uint32_t kv = sm.key[pos];
+    key[j] = pos < count ? kv : 0u;
   }
   const SelResult r = block_select<kNT, PER, kNB>(key, k, sm.sel);
   // In-order compaction of the winners (at most k <= kNB).  Every read of
   // sm.key finished inside the selection, so keys go straight to their
   // place; ids are staged through the (zero) histogram, which is cleared
   // again behind them.
+  int32_t* stage = &sm.sel.hist[0][0];
+  int32_t idv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) idv[j] = sm.id[tid * PER + j];
   int p = r.pos;
 #pragma unroll
   for (int j = 0; j < PER; ++j)
     if (r.mask & (1u << j)) {
-      sm.sel.hist[p] = sm.id[tid * PER + j];
+      stage[p] = idv[j];
       sm.key[p] = key[j];
       ++p;
     }
   __syncthreads();
   for (int q = tid; q < r.total; q += kNT) {
-    sm.id[q] = sm.sel.hist[q];
-    sm.sel.hist[q] = 0;
+    sm.id[q] = stage[q];
+    stage[q] = 0;
   }
   __syncthreads();
   return r.total;
@@ -203,46 +209,58 @@ __device__ __forceinline__ int select_out(RowSmem& sm, int count,
   const int tid = threadIdx.x;
   uint32_t key[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
+  for (int j = 0; j < PER; ++j) {       // unconditional reads, then masks
     const int pos = tid * PER + j;
-    key[j] = pos < count ? sm.key[pos] : 0u;
+    const uint32_t kv = sm.key[pos];
+    key[j] = pos < count ? kv : 0u;
   }
   const SelResult r = block_select<kNT, PER, kNB>(key, a.k, sm.sel);
+  int32_t idv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) idv[j] = sm.id[tid * PER + j];
   int p = r.pos;
 #pragma unroll
   for (int j = 0; j < PER; ++j)
-    if (r.mask & (1u << j)) put(a, ob, lim, p++, sm.id[tid * PER + j]);
+    if (r.mask & (1u << j)) put(a, ob, lim, p++, idv[j]);
   return r.total;
 }
 
 // Tile-pruned candidates (see the file comment), with the tile maxima held
 // in registers: thread t owns tiles TP*t .. TP*t+TP-1.  Leaves the
-// candidates (elements >= M of the tiles whose maximum is >= M) in
-// sm.key/sm.id in id order and returns their number, or -1 when they do
-// not fit (then the caller streams the whole row).
+// candidates (elements >= M' of the tiles whose maximum is >= M', M' a lower
+// bound of the k-th largest tile maximum with at least k tile maxima at or
+// above it) in sm.key/sm.id in id order and returns their number, or -1
+// when they do not fit (then the caller streams the whole row).
 template <int TP, bool HAS_IDS>
 __device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
                                                  int64_t n_t, int64_t len,
                                                  const ScoreSrc<HAS_IDS>& src,
                                                  int k) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // (1) M = the k-th largest tile maximum (or a lower bound of it that no
-  // selected tile maximum undercuts).
-  uint32_t tk[TP];
+  // (1) The tile maxima, read coalesced and staged as keys in sm.key, then
+  // taken back as each thread's contiguous run; M' after two binning
+  // passes (a bound is enough: the candidates only grow by the few tiles
+  // that share M's bin).
   {
     float tv[TP];
 #pragma unroll
-    for (int j = 0; j < TP; ++j) {
-      const int64_t t = (int64_t)tid * TP + j;
-      tv[j] = trow[t < n_t ? t : n_t - 1];
+    for (int r = 0; r < TP; ++r) {
+      const int t = r * kNT + tid;
+      tv[r] = trow[t < n_t ? t : n_t - 1];
     }
 #pragma unroll
-    for (int j = 0; j < TP; ++j)
-      tk[j] = (int64_t)tid * TP + j < n_t ? score_key(tv[j]) : 0u;
+    for (int r = 0; r < TP; ++r) {
+      const int t = r * kNT + tid;
+      sm.key[t] = t < n_t ? score_key(tv[r]) : 0u;
+    }
   }
-  const uint32_t M = block_select<kNT, TP, kNB>(tk, k, sm.sel).thr;
+  __syncthreads();
+  uint32_t tk[TP];
+#pragma unroll
+  for (int j = 0; j < TP; ++j) tk[j] = sm.key[tid * TP + j];
+  const uint32_t M = block_select<kNT, TP, kNB, true>(tk, k, sm.sel, 2).thr;
   if (M == 0) return 0;                       // no valid score at all
-  // (2) the tiles whose maximum is >= M, in order.
+  // (2) the tiles whose maximum is >= M', in order.
   uint32_t fl = 0;
 #pragma unroll
   for (int j = 0; j < TP; ++j)
@@ -254,40 +272,54 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
   for (int j = 0; j < TP; ++j)
     if (fl & (1u << j)) sm.tiles[p++] = tid * TP + j;
   __syncthreads();
-  // (3) their elements >= M.  A wavefront reads two listed tiles per load
+  const int len32 = (int)len;                 // < 2^19 here (n_t <= 16384)
+  // (3) their elements >= M'.  A wavefront reads two listed tiles per load
   // (lanes 0-31 and 32-63), kSteps loads in flight, and places its
   // candidates in lane order, which is id order.
-  constexpr int kSteps = 16;
+  constexpr int kSteps = 32;
   constexpr int kChunk = kNT / 64 * 2 * kSteps;     // listed tiles per round
   int n_c = 0;
   for (int c0 = 0; c0 < n_list; c0 += kChunk) {
-    float v[kSteps];
-    int32_t ii[kSteps];
-    int pos[kSteps];                                  // < 2^19 here
+    // Tile numbers first (unconditional reads from a clamped slot, so the
+    // LDS reads are issued together), then every score load.
+    int tl[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int li = c0 + wv * 2 * kSteps + 2 * s + (lane >> 5);
-      const int tile = li < n_list ? sm.tiles[li] : 0;
-      pos[s] = tile * 32 + (lane & 31);
-      src.load(pos[s] < len ? pos[s] : len - 1, v[s], ii[s]);
-      if (li >= n_list) pos[s] = (int)len;            // marks "no element"
+      tl[s] = sm.tiles[li < n_list ? li : 0];
     }
-    uint32_t kk[kSteps];
-    int wcount = 0;
+    float v[kSteps];
+    int32_t ii[kSteps];
+    uint32_t ok = 0;                                  // element exists
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const uint32_t key = pos[s] < len && ii[s] >= 0 ? score_key(v[s]) : 0u;
-      kk[s] = key >= M ? key : 0u;
-      wcount += __popcll(__ballot(kk[s] != 0));
+      const int li = c0 + wv * 2 * kSteps + 2 * s + (lane >> 5);
+      const int pos = tl[s] * 32 + (lane & 31);
+      src.load(pos < len32 ? pos : len32 - 1, v[s], ii[s]);
+      ok |= (uint32_t)((li < n_list) & (pos < len32)) << s;
     }
+    // Bitwise (not short-circuit) tests keep this straight-line code.
+    // The wavefront's count comes from per-lane counts and one reduction;
+    // the order-giving ballots are taken only while placing.
+    uint32_t kk[kSteps];
+    int lcount = 0;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const uint32_t key = score_key(v[s]);
+      const bool keep = (((ok >> s) & 1u) != 0) & (ii[s] >= 0) & (key >= M);
+      kk[s] = keep ? key : 0u;
+      lcount += keep ? 1 : 0;
+    }
+    const int wcount = __builtin_amdgcn_readlane(wave_incl_scan(lcount), 63);
     int total;
     int run = n_c + wave_offset(wcount, total, sm.sel);
     if (n_c + total <= kCap) {
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         const uint64_t m = __ballot(kk[s] != 0);
+        const int q = run + (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         if (kk[s]) {
-          const int q = run + __popcll(m & lanemask_lt());
           sm.key[q] = kk[s];
           sm.id[q] = ii[s];
         }
@@ -317,7 +349,7 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
   const int b = blockIdx.x, tid = threadIdx.x;
-  for (int i = tid; i < kNB; i += kNT) sm.sel.hist[i] = 0;
+  for (int i = tid; i < kNT / 64 * kNB; i += kNT) (&sm.sel.hist[0][0])[i] = 0;
   int64_t len = a.ld;
   if (a.n_valid) {
     const int64_t nv = a.n_valid[b];
