@@ -28,10 +28,13 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
-# Per-source additions.  The indexer keeps its matrix-core accumulators in
-# ordinary VGPRs (no accumulator-register copies before the per-lane
-# epilogue), which also brings it to 128 VGPRs: four waves per SIMD.
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions: matrix-core accumulators in ordinary VGPRs.  The
+# indexer then needs no accumulator-register copies before its per-lane
+# epilogue (and fits 128 VGPRs: four waves per SIMD); the attention kernel
+# no longer copies its 128 output accumulators out of accumulator registers
+# around the conditional softmax rescale.
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):

@@ -310,17 +310,20 @@ __device__ __forceinline__ void tile_step(
   for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
   mt = fmaxf(mt, __shfl_xor(mt, 16));
   mt = fmaxf(mt, __shfl_xor(mt, 32));
-  const bool bump = mt > st.m_run + kRescaleSlack;   // also true from -inf
-  if (__any(bump)) {
-    if (bump) {
-      const float alpha = (st.m_run == -__builtin_inff()) ? 0.0f
-                                                          : exp2f(st.m_run - mt);
+  // Move the reference point when the tile maximum rises by more than the
+  // slack (also from -inf).  Nothing has been accumulated while it is still
+  // -inf, so only a head with history rescales its accumulators.
+  const bool bump = mt > st.m_run + kRescaleSlack;
+  const bool rescale = bump & (st.m_run != -__builtin_inff());
+  if (__any(rescale)) {
+    if (rescale) {
+      const float alpha = exp2f(st.m_run - mt);
       st.l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 32; ++i) st.acc[i] *= alpha;
-      st.m_run = mt;
     }
   }
+  if (bump) st.m_run = mt;
   const float mref = st.m_run == -__builtin_inff() ? 0.0f : st.m_run;
   f16x8_t pb;
 #pragma unroll
