@@ -50,6 +50,8 @@ constexpr int kKtElems = kTile * kKtStride;
 constexpr int kVsElems = 4 * 512 * 8;
 constexpr int kBufElems = kKtElems + kVsElems;
 constexpr int kSmemBytes = 2 * kBufElems * 2 + 2 * kTile * 4;
+// The epilogue stages 4 waves x 16 heads x (512 + 8) halfs in the same LDS.
+static_assert(4 * 16 * (512 + 8) * 2 <= kSmemBytes, "output staging fits");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;       // log2 units
 
@@ -433,27 +435,38 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   l_tot += __shfl_xor(l_tot, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 
-  if (p.splits == 1) {
-    uint16_t* orow = p.out + ((int64_t)b * kHeads + head) * 512 + 4 * q4;
-#pragma unroll
-    for (int blk = 0; blk < 32; ++blk) {
-      const uint32_t lo = pack_bf16(acc[blk][0] * inv, acc[blk][1] * inv);
-      const uint32_t hi = pack_bf16(acc[blk][2] * inv, acc[blk][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * blk) = make_uint2(lo, hi);
-    }
-    return;
-  }
-  // Partial of this split, normalised by its own sum (a convex combination
-  // of keys, so |value| <= 2688 fits fp16 with 11 significant bits).
-  const int64_t ps = ((int64_t)b * p.splits + split) * kHeads + head;
-  uint16_t* orow = p.part_o + ps * 512 + 4 * q4;
+  // The output (final bf16, or this split's fp16 partial normalised by its
+  // own sum -- a convex combination of keys, so |value| <= 2688 fits fp16
+  // with 11 significant bits) is staged through LDS (free after the last
+  // tile's barrier) so that every store writes 16 contiguous bytes per lane
+  // and whole 1 KB head rows per instruction.
+  constexpr int kRowH = 512 + 8;                 // staged row, +16 B pad
+  uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + wave * 16 * kRowH;
+  const bool final_out = p.splits == 1;
 #pragma unroll
   for (int blk = 0; blk < 32; ++blk) {
-    const f16x2_t lo = {(_Float16)(acc[blk][0] * inv), (_Float16)(acc[blk][1] * inv)};
-    const f16x2_t hi = {(_Float16)(acc[blk][2] * inv), (_Float16)(acc[blk][3] * inv)};
-    *reinterpret_cast<uint2*>(orow + 16 * blk) = make_uint2(f16x2_bits(lo), f16x2_bits(hi));
+    uint32_t lo, hi;
+    if (final_out) {
+      lo = pack_bf16(acc[blk][0] * inv, acc[blk][1] * inv);
+      hi = pack_bf16(acc[blk][2] * inv, acc[blk][3] * inv);
+    } else {
+      lo = f16x2_bits(f16x2_t{(_Float16)(acc[blk][0] * inv), (_Float16)(acc[blk][1] * inv)});
+      hi = f16x2_bits(f16x2_t{(_Float16)(acc[blk][2] * inv), (_Float16)(acc[blk][3] * inv)});
+    }
+    *reinterpret_cast<uint2*>(stg + col * kRowH + 16 * blk + 4 * q4) =
+        make_uint2(lo, hi);
   }
-  if (q4 == 0) {
+  __syncthreads();
+  const int64_t row0 = final_out
+      ? ((int64_t)b * kHeads + 16 * wave)
+      : (((int64_t)b * p.splits + split) * kHeads + 16 * wave);
+  uint16_t* dst = (final_out ? p.out : p.part_o) + row0 * 512 + 8 * lane;
+#pragma unroll
+  for (int h = 0; h < 16; ++h)
+    *reinterpret_cast<u32x4*>(dst + h * 512) =
+        *reinterpret_cast<const u32x4*>(stg + h * kRowH + 8 * lane);
+  if (!final_out && q4 == 0) {
+    const int64_t ps = ((int64_t)b * p.splits + split) * kHeads + head;
     p.part_ml[ps * 2 + 0] = m_run;
     p.part_ml[ps * 2 + 1] = l_tot;
   }
