@@ -51,7 +51,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 constexpr int kMaxK = 2048;
 constexpr int kMaxBlock = 64;
 constexpr int64_t kMaxCap = INT32_MAX;
-// Attention gathers address rows by 32-bit byte offsets within a sequence.
+// The indexer and attention address rows by 32-bit byte offsets within a
+// sequence (up to 256 bytes per row).
 constexpr int64_t kMaxAttnCap = int64_t(1) << 24;
 
 // Workspace layout of csa2_sparse_attn_decode.
@@ -268,6 +269,9 @@ csa2_status csa2_indexer_score(int32_t keyfmt, const void* k_codes,
     return fail(CSA2_ERR_INVALID_ARG, "unknown key format %d", keyfmt);
   if (B < 0 || n_cap < 0 || n_cap > kMaxCap || (cand && n_cand < 0))
     return fail(CSA2_ERR_INVALID_ARG, "bad B, n_cap or n_cand");
+  if (n_cap > kMaxAttnCap)
+    return fail(CSA2_ERR_UNSUPPORTED,
+                "the indexer needs n_cap <= 2^24 (got %lld)", (long long)n_cap);
   const int64_t rows = cand ? n_cand : n_cap;
   if (B == 0 || rows == 0) return CSA2_OK;
   if (!k_codes || !n_entries || !q_idx || !w || !scores)

@@ -45,29 +45,31 @@ template <> struct RawKey<1> {       // bf16: 64 dims = 128 bytes
 
 // Loads are unconditional (the caller clamps `row` to a row that exists), so
 // no load sits inside a branch and the compiler can keep several tiles of
-// loads in flight with exact wait counts.
+// loads in flight with exact wait counts.  `codes`/`scales` point at the
+// sequence's first row and `row` is the row within it: byte offsets stay
+// below 2^32 (n_cap <= 2^24), one uniform base plus a 32-bit lane offset.
 template <int KEYFMT>
 __device__ __forceinline__ void load_key(RawKey<KEYFMT>& r, const void* codes,
-                                         const uint8_t* scales, int64_t row,
+                                         const uint8_t* scales, uint32_t row,
                                          int half);
 
 template <>
 __device__ __forceinline__ void load_key<0>(RawKey<0>& r, const void* codes,
-                                            const uint8_t* scales, int64_t row,
-                                            int half) {
+                                            const uint8_t* scales,
+                                            uint32_t row, int half) {
   const u32x4* p = reinterpret_cast<const u32x4*>(
-      static_cast<const uint8_t*>(codes) + row * 64 + 32 * half);
+      static_cast<const uint8_t*>(codes) + (row * 64u + 32u * half));
   r.c0 = p[0];
   r.c1 = p[1];
-  r.sc = *reinterpret_cast<const uint32_t*>(scales + row * 4);
+  r.sc = *reinterpret_cast<const uint32_t*>(scales + row * 4u);
 }
 
 template <>
 __device__ __forceinline__ void load_key<1>(RawKey<1>& r, const void* codes,
-                                            const uint8_t*, int64_t row,
+                                            const uint8_t*, uint32_t row,
                                             int half) {
   const u32x4* p = reinterpret_cast<const u32x4*>(
-      static_cast<const uint16_t*>(codes) + row * 128 + 64 * half);
+      static_cast<const uint8_t*>(codes) + (row * 256u + 128u * half));
 #pragma unroll
   for (int s = 0; s < 8; ++s) r.v[s] = p[s];
 }
@@ -138,22 +140,26 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   if (base >= n_rows) return;                  // wave-uniform; no barriers
   int64_t n = n_entries[b];
   n = n < 0 ? 0 : (n > n_cap ? n_cap : n);     // never past the cache
-  const int64_t seq_base = (int64_t)b * n_cap;
+  const void* seq_codes = static_cast<const uint8_t*>(k_codes) +
+                          (int64_t)b * n_cap * (KEYFMT == 0 ? 64 : 256);
+  const uint8_t* seq_scales =
+      KEYFMT == 0 ? k_scales + (int64_t)b * n_cap * 4 : nullptr;
   const int nt = (int)((n_rows - base + 31) >> 5) < T
                      ? (int)((n_rows - base + 31) >> 5) : T;
 
-  // Row of every tile position this lane will read (candidate ids first,
-  // all in one round), with validity; invalid rows are clamped to row 0.
-  int64_t row[T];
+  // Row (within the sequence) of every tile position this lane will read
+  // (candidate ids first, all in one round), with validity; invalid rows
+  // are clamped to row 0.
+  uint32_t row[T];
   uint32_t vmask = 0;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int64_t i = base + 32 * t + col;
     int64_t e = i;
     if (cand) e = cand[(int64_t)b * n_rows + (i < n_rows ? i : n_rows - 1)];
-    const bool v = i < n_rows && e >= 0 && e < n;
+    const bool v = (i < n_rows) & (e >= 0) & (e < n);
     vmask |= (v ? 1u : 0u) << t;
-    row[t] = seq_base + (v ? e : 0);
+    row[t] = v ? (uint32_t)e : 0u;
   }
 
   // A operand: head `col`, dims 64*half + 8*s .. +7 for step s.
@@ -173,13 +179,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   RawKey<KEYFMT> buf[D + 1];
 #pragma unroll
   for (int t = 0; t < D; ++t)
-    load_key<KEYFMT>(buf[t], k_codes, k_scales, row[t], half);
+    load_key<KEYFMT>(buf[t], seq_codes, seq_scales, row[t], half);
   float total[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (t + D < T)
-      load_key<KEYFMT>(buf[(t + D) % (D + 1)], k_codes, k_scales, row[t + D],
-                       half);
+      load_key<KEYFMT>(buf[(t + D) % (D + 1)], seq_codes, seq_scales,
+                       row[t + D], half);
     total[t] = -__builtin_inff();
     if (t < nt && base + 32 * t < (cand ? n_rows : n)) {   // wave-uniform
       const RawKey<KEYFMT>& cur = buf[t % (D + 1)];

@@ -147,6 +147,7 @@ csa2_status csa2_build_block_keys(const uint8_t *idx_codes,
  *   cand      NULL: score rows 0..n_cap-1 into scores[B][n_cap];
  *             else [B][n_cand] row ids to score into scores[B][n_cand]
  *   q_idx     [B][32][128] bf16; w [B][32] float32
+ *   n_cap     <= 2^24 (CSA2_ERR_UNSUPPORTED beyond)
  * Rows >= n_entries[b] (or ids outside [0, n_entries[b])) get -inf.
  * Products are exact (bf16 x dequantised FP4); accumulation is float32. */
 csa2_status csa2_indexer_score(int32_t keyfmt, const void *k_codes,
