@@ -186,8 +186,10 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     if (t + D < T)
       load_key<KEYFMT>(buf[(t + D) % (D + 1)], seq_codes, seq_scales,
                        row[t + D], half);
-    total[t] = -__builtin_inff();
-    if (t < nt && base + 32 * t < (cand ? n_rows : n)) {   // wave-uniform
+    // No branch around the tile: a conditional block would let the
+    // compiler sink this tile's loads into it (and serialise them).  Tiles
+    // past the end compute on clamped rows and are masked out.
+    {
       const RawKey<KEYFMT>& cur = buf[t % (D + 1)];
       f32x16 acc = {};
 #pragma unroll
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       const auto hv = __builtin_amdgcn_permlane32_swap(
           __float_as_uint(p0 + p1), __float_as_uint(p0 + p1), false, false);
       const float sum = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
-      if (vmask & (1u << t)) total[t] = sum;
+      total[t] = (vmask & (1u << t)) ? sum : -__builtin_inff();
     }
   }
   // Stores after the loop keep the loads' wait counts static.
