@@ -382,14 +382,15 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   hipError_t e;
-  float* tmax = reinterpret_cast<float*>(base + L.off_tmax);
+  // Decode-internal buffers hold selection keys (uint32), not scores.
+  uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
   if (!pool) {
     float* scores = reinterpret_cast<float*>(base + L.off_scores);
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, nullptr, kv->n_cap,
                              q_idx, w, B, scores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
-    e = csa2::launch_row_select(scores, tmax, kv->n_cap, kv->n_entries,
+    e = csa2::launch_row_select(scores, tmax, true, kv->n_cap, kv->n_entries,
                                 nullptr, B, k, 1, nullptr, topk_out, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
   } else {
@@ -403,15 +404,15 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
                              nblk, nullptr, L.nb, q_idx, w, B, bscores, s,
                              tmax);
     if (e != hipSuccess) return hip_fail(e, "block indexer launch");
-    e = csa2::launch_row_select(bscores, tmax, L.nb, nblk, nullptr, B, L.kb,
-                                pool->block, kv->n_entries, pool_ids, s);
+    e = csa2::launch_row_select(bscores, tmax, true, L.nb, nblk, nullptr, B,
+                                L.kb, pool->block, kv->n_entries, pool_ids, s);
     if (e != hipSuccess) return hip_fail(e, "block top-k launch");
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, pool_ids, L.n_cand,
                              q_idx, w, B, pscores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
-    e = csa2::launch_row_select(pscores, tmax, L.n_cand, nullptr, pool_ids,
-                                B, k, 1, nullptr, topk_out, s);
+    e = csa2::launch_row_select(pscores, tmax, true, L.n_cand, nullptr,
+                                pool_ids, B, k, 1, nullptr, topk_out, s);
     if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
   }
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,

@@ -41,13 +41,15 @@ __device__ __forceinline__ bf16x8 bits_to_bf8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Order-preserving map float32 -> uint32 (larger float -> larger key).
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = f2u(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return u2f((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+// Selection key of a score: an order-preserving map float32 -> uint32
+// (larger score -> larger key) with NaN and -inf -> 0 (never chosen) and
+// -0 -> key(+0), so equal scores have equal keys.  Selects only, no
+// branches.
+__device__ __forceinline__ uint32_t score_key(float v) {
+  uint32_t u = f2u(v);
+  u = (u << 1) ? u : 0u;                                   // -0 -> +0
+  const uint32_t key = (int32_t)u < 0 ? ~u : (u | 0x80000000u);
+  return v > -__builtin_inff() ? key : 0u;
 }
 
 // Raise a kernel's dynamic-LDS limit once per device (host side).

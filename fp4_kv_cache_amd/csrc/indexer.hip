@@ -25,6 +25,7 @@
 // only the tiles that can hold a winner.
 #include "common.h"
 #include "internal.h"
+#include "select.h"
 
 namespace csa2 {
 namespace {
@@ -99,35 +100,19 @@ __device__ __forceinline__ bf16x8 key_operand<1>(const RawKey<1>& r, int s,
   return bits_to_bf8(r.v[s]);
 }
 
-// Largest value over the wavefront (DPP row shifts and broadcasts; lanes
-// without a source keep their own value), read from lane 63.
-template <int CTRL, int RMASK>
-__device__ __forceinline__ float dpp_fmax(float v) {
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
-                      __float_as_int(v), __float_as_int(v), CTRL, RMASK, 0xf,
-                      false)));
-}
-__device__ __forceinline__ float wave_max_f32(float v) {
-  v = dpp_fmax<0x111, 0xf>(v);     // row_shr:1
-  v = dpp_fmax<0x112, 0xf>(v);     // row_shr:2
-  v = dpp_fmax<0x114, 0xf>(v);     // row_shr:4
-  v = dpp_fmax<0x118, 0xf>(v);     // row_shr:8
-  v = dpp_fmax<0x142, 0xa>(v);     // row_bcast:15
-  v = dpp_fmax<0x143, 0xc>(v);     // row_bcast:31
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
 // Tiles of loads kept in flight ahead of the matrix work.
 template <int KEYFMT> struct Depth { static constexpr int value = 2; };
 template <> struct Depth<1> { static constexpr int value = 1; };
 
-template <int KEYFMT, bool TMAX>
+// KEYS: write selection keys (see score_key) instead of float scores, and
+// each 32-row tile's largest key to tmax[B][ceil(n_rows/32)].
+template <int KEYFMT, bool KEYS>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ cand, int64_t n_rows,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    float* __restrict__ scores, float* __restrict__ tmax) {
+    float* __restrict__ scores, uint32_t* __restrict__ tmax) {
   constexpr int D = Depth<KEYFMT>::value;
   constexpr int T = kTilesPerWave;
   const int b = blockIdx.y;
@@ -186,10 +171,12 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     if (t + D < T)
       load_key<KEYFMT>(buf[(t + D) % (D + 1)], seq_codes, seq_scales,
                        row[t + D], half);
-    // No branch around the tile: a conditional block would let the
-    // compiler sink this tile's loads into it (and serialise them).  Tiles
-    // past the end compute on clamped rows and are masked out.
-    {
+    // MXFP4 keys: no branch around the tile -- a conditional block would
+    // let the compiler sink this tile's loads into it (and serialise them);
+    // tiles past the end compute on clamped rows and are masked out.  The
+    // bf16 block keys (one tile of loads ahead) keep the per-tile test,
+    // which schedules better there.
+    if (KEYFMT == 0 || (t < nt && base + 32 * t < (cand ? n_rows : n))) {
       const RawKey<KEYFMT>& cur = buf[t % (D + 1)];
       f32x16 acc = {};
 #pragma unroll
@@ -210,6 +197,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
           __float_as_uint(p0 + p1), __float_as_uint(p0 + p1), false, false);
       const float sum = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
       total[t] = (vmask & (1u << t)) ? sum : -__builtin_inff();
+    } else {
+      total[t] = -__builtin_inff();
     }
   }
   // Stores after the loop keep the loads' wait counts static.
@@ -217,12 +206,17 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   for (int t = 0; t < T; ++t) {
     if (t >= nt) break;
     const int64_t i = base + 32 * t + col;
-    if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
-    if constexpr (TMAX) {
-      // Largest score of the tile (both lane halves hold the same 32).
-      const float mx = wave_max_f32(total[t]);
+    if constexpr (KEYS) {
+      // Selection keys, and each tile's largest key (both lane halves hold
+      // the same 32 entries) by an integer wavefront maximum.
+      const uint32_t key = score_key(total[t]);
+      if (half == 0 && i < n_rows)
+        reinterpret_cast<uint32_t*>(scores)[(int64_t)b * n_rows + i] = key;
+      const uint32_t mx = wave_max_u32(key);
       if (lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
+    } else {
+      if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
     }
   }
 }
@@ -234,7 +228,7 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const int32_t* n_entries, const int32_t* cand,
                           int64_t n_rows, const uint16_t* q_idx,
                           const float* w, int B, float* scores, hipStream_t s,
-                          float* tmax) {
+                          uint32_t* tmax) {
   if (n_rows == 0 || B == 0) return hipSuccess;
   const dim3 grid((unsigned)((n_rows + kEntriesPerBlock - 1) / kEntriesPerBlock),
                   (unsigned)B);

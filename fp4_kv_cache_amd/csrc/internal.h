@@ -23,20 +23,22 @@ hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
                           int32_t* nblk, hipStream_t s);
 
 // indexer.hip
-// Scores rows (all n_rows, or the n_rows candidate ids `cand`) into
-// scores[B][n_rows]; with `tmax`, also each 32-row tile's largest score into
-// tmax[B][ceil(n_rows/32)].
+// Scores rows (all n_rows, or the n_rows candidate ids `cand`) into float
+// scores[B][n_rows].  With `tmax` (the decode path) it writes selection keys
+// (score_key, as uint32 in the same buffer) instead, and each 32-row tile's
+// largest key into tmax[B][ceil(n_rows/32)].
 hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,
                           const int32_t* n_entries, const int32_t* cand,
                           int64_t n_rows, const uint16_t* q_idx,
                           const float* w, int B, float* scores, hipStream_t s,
-                          float* tmax = nullptr);
+                          uint32_t* tmax = nullptr);
 
 // topk.hip
-// Exact per-row top-k (see topk.hip); `tmax` (tile maxima, nullable)
-// enables tile pruning.
-hipError_t launch_row_select(const float* scores, const float* tmax,
+// Exact per-row top-k (see topk.hip) of float scores (keys == false) or of
+// selection keys (keys == true); `tmax` (tile maxima in the same form,
+// nullable) enables tile pruning.
+hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
                              int64_t ld, const int32_t* n_valid,
                              const int32_t* ids, int B, int k, int block,
                              const int32_t* limit, int32_t* out,

@@ -87,16 +87,6 @@ __device__ __forceinline__ int sel_excl_scan(int x, int& total,
   return before + incl - x;
 }
 
-// Canonical key of a score: NaN and -inf -> 0 (invalid), -0 -> key(+0).
-// Written with selects only (no branches), so unrolled uses stay
-// straight-line code.
-__device__ __forceinline__ uint32_t score_key(float v) {
-  uint32_t u = __float_as_uint(v);
-  u = (u << 1) ? u : 0u;                                   // -0 -> +0
-  const uint32_t key = (int32_t)u < 0 ? ~u : (u | 0x80000000u);
-  return v > -__builtin_inff() ? key : 0u;
-}
-
 struct SelResult {
   uint32_t mask;      // selected elements of this thread (bit j)
   int pos;            // selected elements before this thread

@@ -132,7 +132,7 @@ __device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       constexpr int kH = kCap / kNT / 2;
-      float fv[kH];
+      uint32_t fv[kH];
       int32_t fi[kH];
 #pragma unroll
       for (int j = 0; j < kH; ++j) {
@@ -147,7 +147,7 @@ __device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
       for (int j = 0; j < kH; ++j) {
         const int s = (h * kH + j) * kNT + tid;
         if (s >= count && s < count + fill) {
-          sm.key[s] = fi[j] >= 0 ? score_key(fv[j]) : 0u;
+          sm.key[s] = fi[j] >= 0 ? Src::key(fv[j]) : 0u;
           sm.id[s] = fi[j];
         }
       }
@@ -159,28 +159,42 @@ __device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
   return count;
 }
 
-// Element sources for stream_select (ids ascending in i): load(i, v, id)
-// reads the raw value and id of element i (always a valid index).
-template <bool HAS_IDS>
+// Element sources (ids ascending in i): load(i, r, id) reads the raw
+// 32-bit word and id of element i (always a valid index); key(r) turns the
+// word into a selection key -- it already is one when KEYS, else it is a
+// float score.
+template <bool KEYS>
+__device__ __forceinline__ uint32_t word_key(uint32_t r) {
+  if constexpr (KEYS) return r;
+  else return score_key(__uint_as_float(r));
+}
+template <bool HAS_IDS, bool KEYS>
 struct ScoreSrc {                 // a score row; ids = positions or ids[]
-  const float* row;
+  const uint32_t* row;
   const int32_t* idrow;
-  __device__ __forceinline__ void load(int64_t i, float& v, int32_t& id) const {
-    v = row[i];
+  __device__ __forceinline__ void load(int64_t i, uint32_t& r, int32_t& id) const {
+    r = row[i];
     id = HAS_IDS ? idrow[i] : (int32_t)i;
   }
+  __device__ static __forceinline__ uint32_t key(uint32_t r) {
+    return word_key<KEYS>(r);
+  }
 };
+template <bool KEYS>
 struct TileSrc {                  // tile maxima; ids = tile numbers
-  const float* trow;
-  __device__ __forceinline__ void load(int64_t t, float& v, int32_t& id) const {
-    v = trow[t];
+  const uint32_t* trow;
+  __device__ __forceinline__ void load(int64_t t, uint32_t& r, int32_t& id) const {
+    r = trow[t];
     id = (int32_t)t;
+  }
+  __device__ static __forceinline__ uint32_t key(uint32_t r) {
+    return word_key<KEYS>(r);
   }
 };
 
 struct RowArgs {
-  const float* scores;      // row stride ld
-  const float* tmax;        // nullable; row stride ceil(ld / 32)
+  const void* scores;       // float scores or keys; row stride ld
+  const void* tmax;         // nullable, same form; row stride ceil(ld / 32)
   int64_t ld;
   const int32_t* n_valid;   // nullable
   const int32_t* ids;       // nullable
@@ -231,10 +245,11 @@ __device__ __forceinline__ int select_out(RowSmem& sm, int count,
 // bound of the k-th largest tile maximum with at least k tile maxima at or
 // above it) in sm.key/sm.id in id order and returns their number, or -1
 // when they do not fit (then the caller streams the whole row).
-template <int TP, bool HAS_IDS>
-__device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
+template <int TP, bool HAS_IDS, bool KEYS>
+__device__ __forceinline__ int pruned_candidates(RowSmem& sm,
+                                                 const uint32_t* trow,
                                                  int64_t n_t, int64_t len,
-                                                 const ScoreSrc<HAS_IDS>& src,
+                                                 const ScoreSrc<HAS_IDS, KEYS>& src,
                                                  int k) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // (1) The tile maxima, read coalesced and staged as keys in sm.key, then
@@ -242,7 +257,7 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
   // passes (a bound is enough: the candidates only grow by the few tiles
   // that share M's bin).
   {
-    float tv[TP];
+    uint32_t tv[TP];
 #pragma unroll
     for (int r = 0; r < TP; ++r) {
       const int t = r * kNT + tid;
@@ -251,7 +266,7 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
 #pragma unroll
     for (int r = 0; r < TP; ++r) {
       const int t = r * kNT + tid;
-      sm.key[t] = t < n_t ? score_key(tv[r]) : 0u;
+      sm.key[t] = t < n_t ? word_key<KEYS>(tv[r]) : 0u;
     }
   }
   __syncthreads();
@@ -288,7 +303,7 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
       const int li = c0 + wv * 2 * kSteps + 2 * s + (lane >> 5);
       tl[s] = sm.tiles[li < n_list ? li : 0];
     }
-    float v[kSteps];
+    uint32_t v[kSteps];
     int32_t ii[kSteps];
     uint32_t ok = 0;                                  // element exists
 #pragma unroll
@@ -305,7 +320,7 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
     int lcount = 0;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const uint32_t key = score_key(v[s]);
+      const uint32_t key = word_key<KEYS>(v[s]);
       const bool keep = (((ok >> s) & 1u) != 0) & (ii[s] >= 0) & (key >= M);
       kk[s] = keep ? key : 0u;
       lcount += keep ? 1 : 0;
@@ -332,19 +347,20 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm, const float* trow,
   return n_c <= kCap ? n_c : -1;
 }
 
-template <int TP, bool HAS_IDS>
-__device__ __forceinline__ int pruned_dispatch(RowSmem& sm, const float* trow,
+template <int TP, bool HAS_IDS, bool KEYS>
+__device__ __forceinline__ int pruned_dispatch(RowSmem& sm,
+                                               const uint32_t* trow,
                                                int64_t n_t, int64_t len,
-                                               const ScoreSrc<HAS_IDS>& src,
+                                               const ScoreSrc<HAS_IDS, KEYS>& src,
                                                int k) {
   if constexpr (TP < kPer) {
     if (n_t > (int64_t)kNT * TP)
-      return pruned_dispatch<TP * 2, HAS_IDS>(sm, trow, n_t, len, src, k);
+      return pruned_dispatch<TP * 2, HAS_IDS, KEYS>(sm, trow, n_t, len, src, k);
   }
-  return pruned_candidates<TP, HAS_IDS>(sm, trow, n_t, len, src, k);
+  return pruned_candidates<TP, HAS_IDS, KEYS>(sm, trow, n_t, len, src, k);
 }
 
-template <bool HAS_IDS>
+template <bool HAS_IDS, bool KEYS>
 __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
@@ -355,16 +371,18 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
     const int64_t nv = a.n_valid[b];
     len = nv < len ? (nv > 0 ? nv : 0) : len;
   }
-  const ScoreSrc<HAS_IDS> from_scores{
-      a.scores + (int64_t)b * a.ld, HAS_IDS ? a.ids + (int64_t)b * a.ld : nullptr};
+  const ScoreSrc<HAS_IDS, KEYS> from_scores{
+      static_cast<const uint32_t*>(a.scores) + (int64_t)b * a.ld,
+      HAS_IDS ? a.ids + (int64_t)b * a.ld : nullptr};
   const int64_t ob = (int64_t)b * a.k * a.block;
   const int64_t lim = a.limit ? (int64_t)a.limit[b] : INT64_MAX;
   const int64_t n_t = (len + 31) >> 5;
   int count = -1;
   if (a.tmax != nullptr && n_t > a.k && n_t <= (int64_t)kNT * kPer) {
-    const float* trow = a.tmax + (int64_t)b * ((a.ld + 31) >> 5);
-    const int n_c = pruned_dispatch<2, HAS_IDS>(sm, trow, n_t, len,
-                                                from_scores, a.k);
+    const uint32_t* trow =
+        static_cast<const uint32_t*>(a.tmax) + (int64_t)b * ((a.ld + 31) >> 5);
+    const int n_c = pruned_dispatch<2, HAS_IDS, KEYS>(sm, trow, n_t, len,
+                                                      from_scores, a.k);
     if (n_c >= 0) {
       if (n_c <= kNT * 2) count = select_out<2>(sm, n_c, a, ob, lim);
       else if (n_c <= kNT * 8) count = select_out<8>(sm, n_c, a, ob, lim);
@@ -408,20 +426,24 @@ size_t topk_workspace(int B, int64_t ld) {
   return (((size_t)B * ((ld + 31) >> 5) * 4) + 255) & ~size_t(255);
 }
 
-hipError_t launch_row_select(const float* scores, const float* tmax,
+template <bool HAS_IDS, bool KEYS>
+hipError_t launch_rows(const RowArgs& a, int B, hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(
+      reinterpret_cast<const void*>(row_select_kernel<HAS_IDS, KEYS>),
+      (int)sizeof(RowSmem), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((row_select_kernel<HAS_IDS, KEYS>), dim3((unsigned)B),
+                     dim3(kNT), sizeof(RowSmem), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
                              int64_t ld, const int32_t* n_valid,
                              const int32_t* ids, int B, int k, int block,
                              const int32_t* limit, int32_t* out,
                              hipStream_t s) {
   if (B == 0) return hipSuccess;
-  static std::atomic<uint64_t> lds_set0{0}, lds_set1{0};
-  hipError_t e = ensure_lds_limit(
-      reinterpret_cast<const void*>(row_select_kernel<false>),
-      (int)sizeof(RowSmem), lds_set0);
-  if (e != hipSuccess) return e;
-  e = ensure_lds_limit(reinterpret_cast<const void*>(row_select_kernel<true>),
-                       (int)sizeof(RowSmem), lds_set1);
-  if (e != hipSuccess) return e;
   RowArgs a{};
   a.scores = scores;
   a.tmax = tmax;
@@ -432,13 +454,10 @@ hipError_t launch_row_select(const float* scores, const float* tmax,
   a.block = block;
   a.limit = limit;
   a.out = out;
-  if (ids)
-    hipLaunchKernelGGL(row_select_kernel<true>, dim3((unsigned)B), dim3(kNT),
-                       sizeof(RowSmem), s, a);
-  else
-    hipLaunchKernelGGL(row_select_kernel<false>, dim3((unsigned)B), dim3(kNT),
-                       sizeof(RowSmem), s, a);
-  return hipGetLastError();
+  if (ids) return keys ? launch_rows<true, true>(a, B, s)
+                       : launch_rows<true, false>(a, B, s);
+  return keys ? launch_rows<false, true>(a, B, s)
+              : launch_rows<false, false>(a, B, s);
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
@@ -455,8 +474,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_row_select(scores, tmax, ld, n_valid, ids, B, k, block, limit,
-                           out, s);
+  return launch_row_select(scores, tmax, false, ld, n_valid, ids, B, k, block,
+                           limit, out, s);
 }
 
 }  // namespace csa2
