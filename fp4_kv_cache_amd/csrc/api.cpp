@@ -66,6 +66,9 @@ struct DecodeLayout {
 
 inline size_t tiles_of(int64_t rows) { return (size_t)((rows + 31) / 32); }
 
+// Key rows in the decode workspace are padded to a multiple of 32 entries.
+int64_t round32(int64_t n) { return (n + 31) & ~(int64_t)31; }
+
 DecodeLayout decode_layout(int B, int64_t n_cap, int k,
                            const csa2_pool_opts* pool) {
   DecodeLayout L;
@@ -73,7 +76,7 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
   size_t off = 0;
   if (!L.pool) {
     L.off_scores = off;
-    off += align256((size_t)B * n_cap * 4);
+    off += align256((size_t)B * round32(n_cap) * 4);
     L.off_tmax = off;
     off += align256((size_t)B * tiles_of(n_cap) * 4);
   } else {
@@ -84,11 +87,11 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     L.off_nblk = off;
     off += align256((size_t)B * 4);
     L.off_bscores = off;
-    off += align256((size_t)B * L.nb * 4);
+    off += align256((size_t)B * round32(L.nb) * 4);
     L.off_pool = off;
     off += align256((size_t)B * L.n_cand * 4);
     L.off_pscores = off;
-    off += align256((size_t)B * L.n_cand * 4);
+    off += align256((size_t)B * round32(L.n_cand) * 4);
     L.off_tmax = off;
     off += align256((size_t)B * std::max(tiles_of(L.nb), tiles_of(L.n_cand)) * 4);
   }
@@ -390,8 +393,9 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
                              kv->n_cap, kv->n_entries, nullptr, kv->n_cap,
                              q_idx, w, B, scores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
-    e = csa2::launch_row_select(scores, tmax, true, kv->n_cap, kv->n_entries,
-                                nullptr, B, k, 1, nullptr, topk_out, s);
+    e = csa2::launch_row_select(scores, tmax, true, round32(kv->n_cap),
+                                kv->n_cap, kv->n_entries, nullptr, B, k, 1,
+                                nullptr, topk_out, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
   } else {
     int32_t* nblk = reinterpret_cast<int32_t*>(base + L.off_nblk);
@@ -404,15 +408,17 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
                              nblk, nullptr, L.nb, q_idx, w, B, bscores, s,
                              tmax);
     if (e != hipSuccess) return hip_fail(e, "block indexer launch");
-    e = csa2::launch_row_select(bscores, tmax, true, L.nb, nblk, nullptr, B,
-                                L.kb, pool->block, kv->n_entries, pool_ids, s);
+    e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb, nblk,
+                                nullptr, B, L.kb, pool->block, kv->n_entries,
+                                pool_ids, s);
     if (e != hipSuccess) return hip_fail(e, "block top-k launch");
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, pool_ids, L.n_cand,
                              q_idx, w, B, pscores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
-    e = csa2::launch_row_select(pscores, tmax, true, L.n_cand, nullptr,
-                                pool_ids, B, k, 1, nullptr, topk_out, s);
+    e = csa2::launch_row_select(pscores, tmax, true, round32(L.n_cand),
+                                L.n_cand, nullptr, pool_ids, B, k, 1, nullptr,
+                                topk_out, s);
     if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
   }
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,

@@ -207,11 +207,14 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     if (t >= nt) break;
     const int64_t i = base + 32 * t + col;
     if constexpr (KEYS) {
-      // Selection keys, and each tile's largest key (both lane halves hold
-      // the same 32 entries) by an integer wavefront maximum.
+      // Selection keys (rows padded to a multiple of 32 entries, so whole
+      // tiles can be read as aligned 16-byte vectors), and each tile's
+      // largest key (both lane halves hold the same 32 entries) by an
+      // integer wavefront maximum.
       const uint32_t key = score_key(total[t]);
+      const int64_t ld32 = (n_rows + 31) & ~(int64_t)31;
       if (half == 0 && i < n_rows)
-        reinterpret_cast<uint32_t*>(scores)[(int64_t)b * n_rows + i] = key;
+        reinterpret_cast<uint32_t*>(scores)[(int64_t)b * ld32 + i] = key;
       const uint32_t mx = wave_max_u32(key);
       if (lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;

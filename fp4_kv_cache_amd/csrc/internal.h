@@ -25,8 +25,9 @@ hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
 // indexer.hip
 // Scores rows (all n_rows, or the n_rows candidate ids `cand`) into float
 // scores[B][n_rows].  With `tmax` (the decode path) it writes selection keys
-// (score_key, as uint32 in the same buffer) instead, and each 32-row tile's
-// largest key into tmax[B][ceil(n_rows/32)].
+// (score_key, as uint32) instead, rows padded to a multiple of 32 entries
+// (scores[B][round_up(n_rows, 32)]), and each 32-row tile's largest key into
+// tmax[B][ceil(n_rows/32)].
 hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,
                           const int32_t* n_entries, const int32_t* cand,
@@ -36,10 +37,11 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
 
 // topk.hip
 // Exact per-row top-k (see topk.hip) of float scores (keys == false) or of
-// selection keys (keys == true); `tmax` (tile maxima in the same form,
-// nullable) enables tile pruning.
+// selection keys (keys == true); rows of n_cols entries at stride ld (keys:
+// ld a multiple of 32), ids (nullable) at stride n_cols; `tmax` (tile maxima
+// [B][ceil(n_cols/32)] in the same form, nullable) enables tile pruning.
 hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
-                             int64_t ld, const int32_t* n_valid,
+                             int64_t ld, int64_t n_cols, const int32_t* n_valid,
                              const int32_t* ids, int B, int k, int block,
                              const int32_t* limit, int32_t* out,
                              hipStream_t s);

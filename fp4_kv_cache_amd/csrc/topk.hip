@@ -194,8 +194,9 @@ struct TileSrc {                  // tile maxima; ids = tile numbers
 
 struct RowArgs {
   const void* scores;       // float scores or keys; row stride ld
-  const void* tmax;         // nullable, same form; row stride ceil(ld / 32)
-  int64_t ld;
+  const void* tmax;         // nullable, same form; row stride ceil(n_cols/32)
+  int64_t ld;               // keys without ids: a multiple of 32
+  int64_t n_cols;           // row length (<= ld); ids row stride
   const int32_t* n_valid;   // nullable
   const int32_t* ids;       // nullable
   int k;
@@ -288,57 +289,87 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm,
     if (fl & (1u << j)) sm.tiles[p++] = tid * TP + j;
   __syncthreads();
   const int len32 = (int)len;                 // < 2^19 here (n_t <= 16384)
-  // (3) their elements >= M'.  A wavefront reads two listed tiles per load
-  // (lanes 0-31 and 32-63), kSteps loads in flight, and places its
-  // candidates in lane order, which is id order.
-  constexpr int kSteps = 32;
-  constexpr int kChunk = kNT / 64 * 2 * kSteps;     // listed tiles per round
+  // (3) their elements >= M'.  A wavefront covers 8 listed tiles per step:
+  // lanes 8j..8j+7 take tile j, four consecutive elements each, so a lane's
+  // elements, then the lanes, then the steps run in id order.  Counts are
+  // per lane (a 3-bit field per step); one prefix scan per step places them.
+  // Key rows without ids are padded to whole tiles (the row stride is a
+  // multiple of 32 entries), so each lane's four entries are one aligned
+  // 16-byte load; otherwise four single loads, moved back at the row's end.
+  constexpr bool kVec = KEYS && !HAS_IDS;
+  constexpr int kSteps = HAS_IDS ? 8 : 16;           // steps per wave
+  constexpr int kChunk = kNT / 64 * 8 * kSteps;      // listed tiles per round
+  const int sub = 4 * (lane & 7);                    // first element in tile
   int n_c = 0;
   for (int c0 = 0; c0 < n_list; c0 += kChunk) {
-    // Tile numbers first (unconditional reads from a clamped slot, so the
-    // LDS reads are issued together), then every score load.
-    int tl[kSteps];
+    int pos[kSteps];
+    uint32_t w[kSteps][4];
+    int32_t id[kSteps][4];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int li = c0 + wv * 2 * kSteps + 2 * s + (lane >> 5);
-      tl[s] = sm.tiles[li < n_list ? li : 0];
-    }
-    uint32_t v[kSteps];
-    int32_t ii[kSteps];
-    uint32_t ok = 0;                                  // element exists
+      const int li = c0 + (wv * kSteps + s) * 8 + (lane >> 3);
+      if constexpr (kVec) {
+        // An unlisted slot reads listed tile 0 and is masked out by pos.
+        const int t = sm.tiles[li < n_list ? li : 0];
+        pos[s] = li < n_list ? t * 32 + sub : len32;
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(src.row + (t * 32 + sub));
+        w[s][0] = v.x; w[s][1] = v.y; w[s][2] = v.z; w[s][3] = v.w;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int li = c0 + wv * 2 * kSteps + 2 * s + (lane >> 5);
-      const int pos = tl[s] * 32 + (lane & 31);
-      src.load(pos < len32 ? pos : len32 - 1, v[s], ii[s]);
-      ok |= (uint32_t)((li < n_list) & (pos < len32)) << s;
+        for (int e = 0; e < 4; ++e) id[s][e] = pos[s] + e;   // the position
+      } else {
+        pos[s] = li < n_list ? sm.tiles[li] * 32 + sub : len32;  // len: none
+      }
     }
-    // Bitwise (not short-circuit) tests keep this straight-line code.
-    // The wavefront's count comes from per-lane counts and one reduction;
-    // the order-giving ballots are taken only while placing.
-    uint32_t kk[kSteps];
+    if constexpr (!kVec) {
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        // Four loads from one address: at the row's end the run is moved
+        // back to stay inside it (len >= 33 here) and shifted into place.
+        const int pc = pos[s] < len32 - 4 ? pos[s] : len32 - 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) src.load(pc + e, w[s][e], id[s][e]);
+        const int d = pos[s] - pc;                   // 0 except at the end
+        if (d > 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int f = e + d < 4 ? e + d : 3;
+            w[s][e] = f == 1 ? w[s][1] : f == 2 ? w[s][2] : w[s][3];
+            id[s][e] = f == 1 ? id[s][1] : f == 2 ? id[s][2] : id[s][3];
+          }
+        }
+      }
+    }
+    uint64_t keepbits = 0;                           // 4 bits per step
     int lcount = 0;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const uint32_t key = word_key<KEYS>(v[s]);
-      const bool keep = (((ok >> s) & 1u) != 0) & (ii[s] >= 0) & (key >= M);
-      kk[s] = keep ? key : 0u;
-      lcount += keep ? 1 : 0;
-    }
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = word_key<KEYS>(w[s][e]);
+        // Past the row's end (padding, or an unlisted slot) nothing is kept.
+        const bool keep = (pos[s] + e < len32) & (id[s][e] >= 0) & (key >= M);
+        keepbits |= (uint64_t)(keep ? 1u : 0u) << (4 * s + e);
+        lcount += keep ? 1 : 0;
+      }
     const int wcount = __builtin_amdgcn_readlane(wave_incl_scan(lcount), 63);
     int total;
     int run = n_c + wave_offset(wcount, total, sm.sel);
     if (n_c + total <= kCap) {
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
-        const uint64_t m = __ballot(kk[s] != 0);
-        const int q = run + (int)__builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (kk[s]) {
-          sm.key[q] = kk[s];
-          sm.id[q] = ii[s];
-        }
-        run += __popcll(m);
+        const uint32_t kb = (uint32_t)(keepbits >> (4 * s)) & 15u;
+        const int c = __popc(kb);
+        const int incl = wave_incl_scan(c);
+        int q = run + incl - c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (kb & (1u << e)) {
+            sm.key[q] = word_key<KEYS>(w[s][e]);
+            sm.id[q] = id[s][e];
+            ++q;
+          }
+        run += __builtin_amdgcn_readlane(incl, 63);
       }
     }
     n_c += total;
@@ -366,21 +397,21 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
   const int b = blockIdx.x, tid = threadIdx.x;
   for (int i = tid; i < kNT / 64 * kNB; i += kNT) (&sm.sel.hist[0][0])[i] = 0;
-  int64_t len = a.ld;
+  int64_t len = a.n_cols;
   if (a.n_valid) {
     const int64_t nv = a.n_valid[b];
     len = nv < len ? (nv > 0 ? nv : 0) : len;
   }
   const ScoreSrc<HAS_IDS, KEYS> from_scores{
       static_cast<const uint32_t*>(a.scores) + (int64_t)b * a.ld,
-      HAS_IDS ? a.ids + (int64_t)b * a.ld : nullptr};
+      HAS_IDS ? a.ids + (int64_t)b * a.n_cols : nullptr};
   const int64_t ob = (int64_t)b * a.k * a.block;
   const int64_t lim = a.limit ? (int64_t)a.limit[b] : INT64_MAX;
   const int64_t n_t = (len + 31) >> 5;
   int count = -1;
   if (a.tmax != nullptr && n_t > a.k && n_t <= (int64_t)kNT * kPer) {
     const uint32_t* trow =
-        static_cast<const uint32_t*>(a.tmax) + (int64_t)b * ((a.ld + 31) >> 5);
+        static_cast<const uint32_t*>(a.tmax) + (int64_t)b * ((a.n_cols + 31) >> 5);
     const int n_c = pruned_dispatch<2, HAS_IDS, KEYS>(sm, trow, n_t, len,
                                                       from_scores, a.k);
     if (n_c >= 0) {
@@ -439,15 +470,17 @@ hipError_t launch_rows(const RowArgs& a, int B, hipStream_t s) {
 }
 
 hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
-                             int64_t ld, const int32_t* n_valid,
-                             const int32_t* ids, int B, int k, int block,
-                             const int32_t* limit, int32_t* out,
-                             hipStream_t s) {
+                             int64_t ld, int64_t n_cols,
+                             const int32_t* n_valid, const int32_t* ids, int B,
+                             int k, int block, const int32_t* limit,
+                             int32_t* out, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (n_cols > ld || (keys && !ids && (ld & 31))) return hipErrorInvalidValue;
   RowArgs a{};
   a.scores = scores;
   a.tmax = tmax;
   a.ld = ld;
+  a.n_cols = n_cols;
   a.n_valid = n_valid;
   a.ids = ids;
   a.k = k;
@@ -474,8 +507,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_row_select(scores, tmax, false, ld, n_valid, ids, B, k, block,
-                           limit, out, s);
+  return launch_row_select(scores, tmax, false, ld, ld, n_valid, ids, B, k,
+                           block, limit, out, s);
 }
 
 }  // namespace csa2
