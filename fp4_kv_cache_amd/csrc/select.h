@@ -66,6 +66,14 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return ~wave_max_u32(~v);
 }
 
+__device__ __forceinline__ uint64_t wave_ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+// Set bits of m in the lanes below this one, plus `add`.
+__device__ __forceinline__ int lanes_below(uint64_t m, int add = 0) {
+  return (int)__builtin_amdgcn_mbcnt_hi(
+      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)add));
+}
 // ------------------------------------------------------------ block ops --
 // Block-wide exclusive prefix sum over threads; returns the block total.
 template <int NT, int NB>

@@ -41,6 +41,8 @@ struct RowSmem {
   int32_t id[kCap];
   int32_t tiles[kTileList];
   SelSmem<kNT, kNB> sel;
+  int32_t n_list;                 // listed tiles (-1: the list overflowed)
+  uint32_t M;                     // the pruning bound M' (0: no valid score)
 };
 
 // Lanes below this one in the wavefront.
@@ -240,23 +242,18 @@ __device__ __forceinline__ int select_out(RowSmem& sm, int count,
   return r.total;
 }
 
-// Tile-pruned candidates (see the file comment), with the tile maxima held
-// in registers: thread t owns tiles TP*t .. TP*t+TP-1.  Leaves the
-// candidates (elements >= M' of the tiles whose maximum is >= M', M' a lower
-// bound of the k-th largest tile maximum with at least k tile maxima at or
-// above it) in sm.key/sm.id in id order and returns their number, or -1
-// when they do not fit (then the caller streams the whole row).
-template <int TP, bool HAS_IDS, bool KEYS>
-__device__ __forceinline__ int pruned_candidates(RowSmem& sm,
-                                                 const uint32_t* trow,
-                                                 int64_t n_t, int64_t len,
-                                                 const ScoreSrc<HAS_IDS, KEYS>& src,
-                                                 int k) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // (1) The tile maxima, read coalesced and staged as keys in sm.key, then
-  // taken back as each thread's contiguous run; M' after two binning
-  // passes (a bound is enough: the candidates only grow by the few tiles
-  // that share M's bin).
+// Pruning steps (1) and (2) of the file comment: M', a lower bound of the
+// k-th largest tile maximum with at least k tile maxima at or above it
+// (two binning passes: a bound is enough, the candidates only grow by the
+// few tiles that share M's bin), and the list of tiles whose maximum is
+// >= M', in order, in sm.tiles.  Both end in sm.n_list / sm.M (n_list is
+// -1 when the list does not fit).  TP tile maxima per thread (thread t owns
+// tiles TP*t .. TP*t+TP-1), read coalesced and staged as keys in sm.key.
+template <int TP, bool KEYS>
+__device__ __forceinline__ void block_tile_list(RowSmem& sm,
+                                                const uint32_t* trow,
+                                                int n_t, int k) {
+  const int tid = threadIdx.x;
   {
     uint32_t tv[TP];
 #pragma unroll
@@ -275,39 +272,60 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm,
 #pragma unroll
   for (int j = 0; j < TP; ++j) tk[j] = sm.key[tid * TP + j];
   const uint32_t M = block_select<kNT, TP, kNB, true>(tk, k, sm.sel, 2).thr;
-  if (M == 0) return 0;                       // no valid score at all
-  // (2) the tiles whose maximum is >= M', in order.
   uint32_t fl = 0;
 #pragma unroll
   for (int j = 0; j < TP; ++j)
-    if (tk[j] >= M) fl |= 1u << j;
+    if ((tk[j] >= M) & (M != 0)) fl |= 1u << j;
   int n_list;
   int p = sel_excl_scan<kNT, kNB>(__popc(fl), n_list, sm.sel);
-  if (n_list > kTileList) return -1;
+  if (n_list <= kTileList) {
 #pragma unroll
-  for (int j = 0; j < TP; ++j)
-    if (fl & (1u << j)) sm.tiles[p++] = tid * TP + j;
+    for (int j = 0; j < TP; ++j)
+      if (fl & (1u << j)) sm.tiles[p++] = tid * TP + j;
+  }
+  if (tid == 0) { sm.n_list = n_list <= kTileList ? n_list : -1; sm.M = M; }
+}
+
+// Leaves sm.n_list / sm.M / sm.tiles set and visible to every thread.
+template <int TP, bool KEYS>
+__device__ __forceinline__ void tile_list(RowSmem& sm, const uint32_t* trow,
+                                          int n_t, int k) {
+  if constexpr (TP < kPer) {
+    if (n_t > kNT * TP) return tile_list<TP * 2, KEYS>(sm, trow, n_t, k);
+  }
+  block_tile_list<TP, KEYS>(sm, trow, n_t, k);
   __syncthreads();
-  const int len32 = (int)len;                 // < 2^19 here (n_t <= 16384)
-  // (3) their elements >= M'.  A wavefront covers 8 listed tiles per step:
-  // lanes 8j..8j+7 take tile j, four consecutive elements each, so a lane's
-  // elements, then the lanes, then the steps run in id order.  Counts are
-  // per lane (a 3-bit field per step); one prefix scan per step places them.
+}
+
+// Pruning step (3): the elements >= M' of the listed tiles, into
+// sm.key/sm.id in id order; returns their number, or -1 when they do not
+// fit.  A wavefront covers 8 listed tiles per step: lanes 8j..8j+7 take tile
+// j, four consecutive elements each, so a lane's elements, then the lanes,
+// then the steps, then the wavefronts run in id order.  S steps per
+// wavefront and round (S chosen so one round usually covers the list).
+// Places are counted by ballots: an element's place is the kept elements of
+// lower lanes (the four per-element ballots' counts below this lane) plus
+// this lane's earlier ones.
+template <int S, bool HAS_IDS, bool KEYS>
+__device__ __forceinline__ int gather_candidates(
+    RowSmem& sm, int n_list, uint32_t M, int64_t len,
+    const ScoreSrc<HAS_IDS, KEYS>& src) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int len32 = (int)len;                 // < 2^20 here (n_t <= 16384)
   // Key rows without ids are padded to whole tiles (the row stride is a
   // multiple of 32 entries), so each lane's four entries are one aligned
   // 16-byte load; otherwise four single loads, moved back at the row's end.
   constexpr bool kVec = KEYS && !HAS_IDS;
-  constexpr int kSteps = HAS_IDS ? 8 : 16;           // steps per wave
-  constexpr int kChunk = kNT / 64 * 8 * kSteps;      // listed tiles per round
-  const int sub = 4 * (lane & 7);                    // first element in tile
+  constexpr int kChunk = kNT / 64 * 8 * S;    // listed tiles per round
+  const int sub = 4 * (lane & 7);             // first element in the tile
   int n_c = 0;
   for (int c0 = 0; c0 < n_list; c0 += kChunk) {
-    int pos[kSteps];
-    uint32_t w[kSteps][4];
-    int32_t id[kSteps][4];
+    int pos[S];
+    uint32_t w[S][4];
+    int32_t id[S][4];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int li = c0 + (wv * kSteps + s) * 8 + (lane >> 3);
+    for (int s = 0; s < S; ++s) {
+      const int li = c0 + (wv * S + s) * 8 + (lane >> 3);
       if constexpr (kVec) {
         // An unlisted slot reads listed tile 0 and is masked out by pos.
         const int t = sm.tiles[li < n_list ? li : 0];
@@ -323,7 +341,7 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm,
     }
     if constexpr (!kVec) {
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
+      for (int s = 0; s < S; ++s) {
         // Four loads from one address: at the row's end the run is moved
         // back to stay inside it (len >= 33 here) and shifted into place.
         const int pc = pos[s] < len32 - 4 ? pos[s] : len32 - 4;
@@ -340,36 +358,41 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm,
         }
       }
     }
-    uint64_t keepbits = 0;                           // 4 bits per step
+    uint32_t keep[S];                                // 4 bits per step
     int lcount = 0;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
+    for (int s = 0; s < S; ++s) {
+      keep[s] = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = word_key<KEYS>(w[s][e]);
         // Past the row's end (padding, or an unlisted slot) nothing is kept.
-        const bool keep = (pos[s] + e < len32) & (id[s][e] >= 0) & (key >= M);
-        keepbits |= (uint64_t)(keep ? 1u : 0u) << (4 * s + e);
-        lcount += keep ? 1 : 0;
+        const bool kp = (pos[s] + e < len32) & (id[s][e] >= 0) &
+                        (word_key<KEYS>(w[s][e]) >= M);
+        keep[s] |= (kp ? 1u : 0u) << e;
       }
+      lcount += __popc(keep[s]);
+    }
     const int wcount = __builtin_amdgcn_readlane(wave_incl_scan(lcount), 63);
     int total;
     int run = n_c + wave_offset(wcount, total, sm.sel);
     if (n_c + total <= kCap) {
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const uint32_t kb = (uint32_t)(keepbits >> (4 * s)) & 15u;
-        const int c = __popc(kb);
-        const int incl = wave_incl_scan(c);
-        int q = run + incl - c;
+      for (int s = 0; s < S; ++s) {
+        uint64_t m[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[e] = wave_ballot((keep[s] >> e) & 1u);
+        int q = run;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q = lanes_below(m[e], q);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (kb & (1u << e)) {
+          if ((keep[s] >> e) & 1u) {
             sm.key[q] = word_key<KEYS>(w[s][e]);
             sm.id[q] = id[s][e];
             ++q;
           }
-        run += __builtin_amdgcn_readlane(incl, 63);
+        run += __popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) +
+               __popcll(m[3]);
       }
     }
     n_c += total;
@@ -378,17 +401,18 @@ __device__ __forceinline__ int pruned_candidates(RowSmem& sm,
   return n_c <= kCap ? n_c : -1;
 }
 
-template <int TP, bool HAS_IDS, bool KEYS>
-__device__ __forceinline__ int pruned_dispatch(RowSmem& sm,
-                                               const uint32_t* trow,
-                                               int64_t n_t, int64_t len,
-                                               const ScoreSrc<HAS_IDS, KEYS>& src,
-                                               int k) {
-  if constexpr (TP < kPer) {
-    if (n_t > (int64_t)kNT * TP)
-      return pruned_dispatch<TP * 2, HAS_IDS, KEYS>(sm, trow, n_t, len, src, k);
-  }
-  return pruned_candidates<TP, HAS_IDS, KEYS>(sm, trow, n_t, len, src, k);
+template <bool HAS_IDS, bool KEYS>
+__device__ __forceinline__ int gather_dispatch(
+    RowSmem& sm, int n_list, uint32_t M, int64_t len,
+    const ScoreSrc<HAS_IDS, KEYS>& src) {
+  if (n_list <= kNT / 64 * 8 * 2)
+    return gather_candidates<2, HAS_IDS, KEYS>(sm, n_list, M, len, src);
+  if (n_list <= kNT / 64 * 8 * 4)
+    return gather_candidates<4, HAS_IDS, KEYS>(sm, n_list, M, len, src);
+  if (HAS_IDS || n_list <= kNT / 64 * 8 * 8)
+    return gather_candidates<8, HAS_IDS, KEYS>(sm, n_list, M, len, src);
+  return gather_candidates<HAS_IDS ? 8 : 16, HAS_IDS, KEYS>(sm, n_list, M,
+                                                           len, src);
 }
 
 template <bool HAS_IDS, bool KEYS>
@@ -410,10 +434,15 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
   const int64_t n_t = (len + 31) >> 5;
   int count = -1;
   if (a.tmax != nullptr && n_t > a.k && n_t <= (int64_t)kNT * kPer) {
-    const uint32_t* trow =
-        static_cast<const uint32_t*>(a.tmax) + (int64_t)b * ((a.n_cols + 31) >> 5);
-    const int n_c = pruned_dispatch<2, HAS_IDS, KEYS>(sm, trow, n_t, len,
-                                                      from_scores, a.k);
+    const uint32_t* trow = static_cast<const uint32_t*>(a.tmax) +
+                           (int64_t)b * ((a.n_cols + 31) >> 5);
+    tile_list<2, KEYS>(sm, trow, (int)n_t, a.k);
+    const int n_list = sm.n_list;
+    const uint32_t M = sm.M;
+    int n_c = -1;
+    if (M == 0) n_c = 0;                      // no valid score at all
+    else if (n_list >= 0)
+      n_c = gather_dispatch<HAS_IDS, KEYS>(sm, n_list, M, len, from_scores);
     if (n_c >= 0) {
       if (n_c <= kNT * 2) count = select_out<2>(sm, n_c, a, ob, lim);
       else if (n_c <= kNT * 8) count = select_out<8>(sm, n_c, a, ob, lim);
