@@ -7,18 +7,19 @@
 //
 // The k-th key is found by narrowing a key interval [lo, hi] that holds it.
 // Each pass bins the keys inside by (hi - key) >> shift into NB = 256 bins,
-// with the shift chosen so the interval fits; every wavefront counts into a
-// histogram of its own (spreading the LDS atomics), and wavefront 0 sums the
-// per-wave counts (one 16-byte read per lane and wave), finds with one
-// prefix scan the bin where the running count from the top reaches the
-// number still needed, clears the histograms for the next pass, and the
-// interval becomes exactly that bin's key range.  A 32-bit range needs at
-// most four passes (24, 16, 8, then 0 bits left).  The search ends with the
-// bin holding exactly the number needed (take every key >= lo) or with a
-// one-key interval (keys above it, plus the first `need` keys equal to it in
-// position order).  One packed prefix sum then yields every selected
-// element's output position.  Reductions and scans inside a wavefront use
-// DPP row shifts and broadcasts.
+// with the shift chosen so the interval fits, in a histogram of its own
+// (LDS atomics from every thread); after one barrier every wavefront reads
+// the whole histogram (one 16-byte read per lane), finds with one prefix
+// scan and a ballot the bin where the running count from the top reaches
+// the number still needed, and narrows the interval to exactly that bin's
+// key range -- the same decision in every wavefront, so nothing is
+// broadcast.  A 32-bit range needs at most four passes (24, 16, 8, then 0
+// bits left).  The search ends with the bin holding exactly the number
+// needed (take every key >= lo) or with a one-key interval (keys above it,
+// plus the first `need` keys equal to it in position order).  One packed
+// prefix sum then yields every selected element's output position.
+// Reductions and scans inside a wavefront use DPP row shifts and
+// broadcasts.
 #pragma once
 #include "common.h"
 
@@ -27,10 +28,19 @@ namespace csa2 {
 template <int NT, int NB>
 struct SelSmem {
   static_assert(NB == 256, "the bin scan assumes 4 bins per lane");
-  int32_t hist[NT / 64][NB];      // per-wavefront bin counts (all zero
-                                  // between calls)
+  static_assert(NT / 64 >= 4, "one histogram per pass, four passes");
+  int32_t hist[NT / 64][NB];      // histogram p serves pass p (all zero
+                                  // between calls); the rest is room for
+                                  // callers between calls
   uint32_t red[4][NT / 64];
-  int32_t bstar, cum_before, bcount;
+};
+
+// A key range known to hold every valid key, and the number of valid keys
+// (lets a selection skip its own min/max reduction).
+struct SelRange {
+  bool known;
+  uint32_t lo, hi;
+  int n;
 };
 
 // --------------------------------------------------------- wavefront ops --
@@ -102,31 +112,37 @@ struct SelResult {
   uint32_t thr;       // every selected key is >= thr, thr is <= the
                       // smallest selected key, and at least min(k, valid)
                       // keys are >= thr (0 when no key is valid)
+  uint32_t max;       // the largest key (the range's top when known)
 };
 
 // Select the top-k (k >= 1) of the NT * PER keys held as key[j] by each
-// thread.  The histograms must be all zero on entry; they are all zero again
-// on return, and every shared-memory access of the call has completed.
-// BOUND_ONLY: stop after `passes` passes and return only `thr` (a lower bound
-// of the k-th key with at least k keys at or above it); mask, pos and total
-// are then not set.
+// thread.  On entry the histograms must be zero, with a barrier since the
+// previous call returned.  BOUND_ONLY: stop after `passes` passes and return
+// only `thr` (a lower bound of the k-th key with at least k keys at or
+// above it) and `max`; mask, pos and total are then not set, and the
+// histograms are zero again once the caller has passed one more barrier.
+// Otherwise they are zero on return and every shared-memory access of the
+// call has completed.
 template <int NT, int PER, int NB, bool BOUND_ONLY = false>
-__device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
-                                                  int k, SelSmem<NT, NB>& sm,
-                                                  int passes = 4) {
+__device__ __forceinline__ SelResult block_select(
+    const uint32_t (&key)[PER], int k, SelSmem<NT, NB>& sm, int passes = 4,
+    SelRange range = SelRange{false, 0u, 0u, 0}) {
   static_assert(PER <= 32, "selection mask is 32 bits");
   static_assert(NT * PER < 65536, "packed counts are 16 bits");
   constexpr int kLogNB = 8;
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  // Valid count, min and max in one reduction.
-  int nval = 0;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  int nval;
+  uint32_t mn, mx;
+  if (range.known) {
+    nval = range.n; mn = range.lo; mx = range.hi;
+  } else {
+    // Valid count, min and max in one reduction.
+    nval = 0; mn = 0xFFFFFFFFu; mx = 0u;
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (key[j]) { ++nval; mn = min(mn, key[j]); mx = max(mx, key[j]); }
-  {
+    for (int j = 0; j < PER; ++j)
+      if (key[j]) { ++nval; mn = min(mn, key[j]); mx = max(mx, key[j]); }
     const int c = __builtin_amdgcn_readlane(wave_incl_scan(nval), 63);
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
@@ -148,47 +164,36 @@ __device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
   uint32_t lo = mn, hi = mx;
   int need = k;
   bool take_all = nval <= k;              // select every valid key >= lo
+  int used = 0;                           // histograms written
   if (!take_all) {
-    int32_t* H = sm.hist[wv];
     for (int it = 0; it < passes && lo < hi; ++it) {
+      int32_t* H = sm.hist[it];
       const int bits = 32 - __builtin_clz(hi - lo);
       const int shift = bits > kLogNB ? bits - kLogNB : 0;
 #pragma unroll
       for (int j = 0; j < PER; ++j)
         if ((key[j] >= lo) & (key[j] <= hi))
           atomicAdd(&H[(hi - key[j]) >> shift], 1);
+      used = it + 1;
       __syncthreads();
-      if (wv == 0) {
-        // Lane L sums bins 4L .. 4L+3 over the per-wave histograms (bins
-        // in key order from the top) and clears them.
-        int4 c = make_int4(0, 0, 0, 0);
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          int4* p = reinterpret_cast<int4*>(&sm.hist[w][4 * lane]);
-          const int4 v = *p;
-          c.x += v.x; c.y += v.y; c.z += v.z; c.w += v.w;
-          *p = make_int4(0, 0, 0, 0);
-        }
-        const int s = c.x + c.y + c.z + c.w;
-        const int run = wave_incl_scan(s) - s;
-        if (run < need && run + s >= need) {
-          int b = 0, before = run, cnt = c.x;
-          if (before + c.x < need) {
-            before += c.x; b = 1; cnt = c.y;
-            if (before + c.y < need) {
-              before += c.y; b = 2; cnt = c.z;
-              if (before + c.z < need) { before += c.z; b = 3; cnt = c.w; }
-            }
-          }
-          sm.bstar = 4 * lane + b;
-          sm.cum_before = before;
-          sm.bcount = cnt;
+      // Lane L holds bins 4L .. 4L+3 (bins in key order from the top).
+      const int4 c = reinterpret_cast<const int4*>(H)[lane];
+      const int s = c.x + c.y + c.z + c.w;
+      const int run = wave_incl_scan(s) - s;
+      // Exactly one lane holds the crossing: `need` >= 1 keys lie in range.
+      const bool hit = (run < need) & (run + s >= need);
+      const int hl = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(hit));
+      int b = 0, before = run, cnt = c.x;
+      if (before + c.x < need) {
+        before += c.x; b = 1; cnt = c.y;
+        if (before + c.y < need) {
+          before += c.y; b = 2; cnt = c.z;
+          if (before + c.z < need) { before += c.z; b = 3; cnt = c.w; }
         }
       }
-      __syncthreads();
-      const int bs = sm.bstar;
-      need -= sm.cum_before;
-      const bool exact = sm.bcount == need;
+      const int bs = __builtin_amdgcn_readlane(4 * lane + b, hl);
+      need -= __builtin_amdgcn_readlane(before, hl);
+      const bool exact = __builtin_amdgcn_readlane(cnt, hl) == need;
       // The bin's key range, clipped to [lo, hi].
       const uint32_t nhi = hi - ((uint32_t)bs << shift);
       const uint32_t width = (1u << shift) - 1u;
@@ -197,10 +202,20 @@ __device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
       if (exact) { take_all = true; break; }
     }
   }
+  // Clears the histograms this call wrote (after a barrier that follows
+  // every read of them).
+  auto clear_used = [&]() {
+    for (int i = tid; i < used * NB; i += NT) (&sm.hist[0][0])[i] = 0;
+  };
   SelResult res;
   res.thr = nval ? lo : 0u;
+  res.max = mx;
   if constexpr (BOUND_ONLY) {
     res.mask = 0; res.pos = 0; res.total = 0;
+    if (used) {
+      __syncthreads();
+      clear_used();
+    }
     return res;
   } else {
     // Selected: take_all -> key >= lo; else key > hi (= lo) plus the first
@@ -213,8 +228,20 @@ __device__ __forceinline__ SelResult block_select(const uint32_t (&key)[PER],
       if (take_all) ngt += key[j] >= lo;
       else { ngt += key[j] > hi; ntie += key[j] == lo; }
     }
-    int tot;
-    const int ex = sel_excl_scan<NT, NB>((ntie << 16) | ngt, tot, sm);
+    const int x = (ntie << 16) | ngt;
+    const int incl = wave_incl_scan(x);
+    if (lane == 63) sm.red[0][wv] = (uint32_t)incl;
+    __syncthreads();
+    clear_used();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const int t = (int)sm.red[0][i];
+      before += i < wv ? t : 0;
+      tot += t;
+    }
+    __syncthreads();
+    const int ex = before + incl - x;
     const int gt_before = ex & 0xFFFF, tie_before = ex >> 16;
     int tie_rank = tie_before;
     uint32_t mask = 0;

@@ -43,6 +43,7 @@ struct RowSmem {
   SelSmem<kNT, kNB> sel;
   int32_t n_list;                 // listed tiles (-1: the list overflowed)
   uint32_t M;                     // the pruning bound M' (0: no valid score)
+  uint32_t M_top;                 // the largest tile maximum
 };
 
 // Lanes below this one in the wavefront.
@@ -222,7 +223,7 @@ __device__ __forceinline__ void put(const RowArgs& a, int64_t ob, int64_t lim,
 template <int PER>
 __device__ __forceinline__ int select_out(RowSmem& sm, int count,
                                           const RowArgs& a, int64_t ob,
-                                          int64_t lim) {
+                                          int64_t lim, SelRange range) {
   const int tid = threadIdx.x;
   uint32_t key[PER];
 #pragma unroll
@@ -231,7 +232,7 @@ __device__ __forceinline__ int select_out(RowSmem& sm, int count,
     const uint32_t kv = sm.key[pos];
     key[j] = pos < count ? kv : 0u;
   }
-  const SelResult r = block_select<kNT, PER, kNB>(key, a.k, sm.sel);
+  const SelResult r = block_select<kNT, PER, kNB>(key, a.k, sm.sel, 4, range);
   int32_t idv[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) idv[j] = sm.id[tid * PER + j];
@@ -271,7 +272,8 @@ __device__ __forceinline__ void block_tile_list(RowSmem& sm,
   uint32_t tk[TP];
 #pragma unroll
   for (int j = 0; j < TP; ++j) tk[j] = sm.key[tid * TP + j];
-  const uint32_t M = block_select<kNT, TP, kNB, true>(tk, k, sm.sel, 2).thr;
+  const SelResult r = block_select<kNT, TP, kNB, true>(tk, k, sm.sel, 2);
+  const uint32_t M = r.thr;
   uint32_t fl = 0;
 #pragma unroll
   for (int j = 0; j < TP; ++j)
@@ -283,7 +285,11 @@ __device__ __forceinline__ void block_tile_list(RowSmem& sm,
     for (int j = 0; j < TP; ++j)
       if (fl & (1u << j)) sm.tiles[p++] = tid * TP + j;
   }
-  if (tid == 0) { sm.n_list = n_list <= kTileList ? n_list : -1; sm.M = M; }
+  if (tid == 0) {
+    sm.n_list = n_list <= kTileList ? n_list : -1;
+    sm.M = M;
+    sm.M_top = r.max;
+  }
 }
 
 // Leaves sm.n_list / sm.M / sm.tiles set and visible to every thread.
@@ -444,9 +450,11 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
     else if (n_list >= 0)
       n_c = gather_dispatch<HAS_IDS, KEYS>(sm, n_list, M, len, from_scores);
     if (n_c >= 0) {
-      if (n_c <= kNT * 2) count = select_out<2>(sm, n_c, a, ob, lim);
-      else if (n_c <= kNT * 8) count = select_out<8>(sm, n_c, a, ob, lim);
-      else count = select_out<kPer>(sm, n_c, a, ob, lim);
+      // Every candidate lies in [M', largest tile maximum].
+      const SelRange range{true, M, sm.M_top, n_c};
+      if (n_c <= kNT * 2) count = select_out<2>(sm, n_c, a, ob, lim, range);
+      else if (n_c <= kNT * 8) count = select_out<8>(sm, n_c, a, ob, lim, range);
+      else count = select_out<kPer>(sm, n_c, a, ob, lim, range);
     }
   }
   if (count < 0) {
