@@ -153,6 +153,20 @@ def indexer_scores(q_idx_bits, w, keys):
     return np.maximum(dots, 0.0) @ w
 
 
+def indexer_scores_fp4q(q_codes, q_scales, w, keys):
+    """The lightning-indexer score with the query itself in MXFP4: [ARCH]
+    2.4.4 (V4 trains the indexer query and key for FP4 scoring, in OCP
+    MXFP4; [KVC] 5 says the same).  The query heads are packed like an
+    indexer key (pack_idx of the 32 rows) and scored dequantised:
+        I_j = sum_h w_h * ReLU(deq(q_h) . K_j)
+    q_codes uint8 [32, 64], q_scales uint8 [32, 4]; w [32]; keys float64
+    [n, 128] (dequantised).  Returns float64 [n]."""
+    q = unpack_idx(q_codes, q_scales)
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    dots = keys @ q.T                                          # [n, 32]
+    return np.maximum(dots, 0.0) @ w
+
+
 def topk(scores, k, ids=None):
     """Exact top-k, [V4] CSA step 2 / [KVC] 4.1 (S_t = Top512 of I_t).
 

@@ -4,6 +4,7 @@ the identities the pages state (sparse = dense when top-k covers every
 entry; the hierarchical path = the flat path when the pool covers every
 block; a Reuse layer fed a Full layer's top-k reproduces its attention)."""
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -70,6 +71,65 @@ def test_scores_permutation_equivariant():
     a = O.indexer_scores(c["qi"], c["w"], keys)
     b = O.indexer_scores(c["qi"], c["w"], keys[perm])
     assert np.array_equal(a[perm], b)
+
+
+def _e2m1_table():
+    """E2M1 magnitudes of codes 0..7 from the cited golden table."""
+    import pathlib
+    rows = [l.split() for l in (pathlib.Path(__file__).parent / "golden" /
+                                "e2m1_values.txt").read_text().splitlines()
+            if l.strip() and not l.startswith("#")]
+    return {int(c): Fraction(v) for c, v in rows}
+
+
+def test_scores_fp4_query_bruteforce_exact():
+    """The FP4-query score against exact rational arithmetic written from
+    the format definitions alone: element 2i in the low nibble of byte i,
+    sign bit 8, E8M0 scale byte g = 2**(g - 127) for elements 32g..32g+31."""
+    mag = _e2m1_table()
+
+    def deq(codes, scales):
+        out = []
+        for e in range(128):
+            nib = (int(codes[e // 2]) >> (4 * (e % 2))) & 15
+            v = mag[nib & 7] * (-1 if nib & 8 else 1)
+            out.append(v * Fraction(2) ** (int(scales[e // 32]) - 127))
+        return out
+
+    rng = np.random.default_rng(11)
+    for trial in range(3):
+        qc, qs = O.pack_idx(rng.standard_normal((32, 128)).astype(np.float32)
+                            * rng.uniform(0.01, 50))
+        kc, ks = O.pack_idx(rng.standard_normal((5, 128)).astype(np.float32))
+        w = rng.uniform(0, 1, 32).astype(np.float32)
+        got = O.indexer_scores_fp4q(qc, qs, w, O.unpack_idx(kc, ks))
+        qv = [deq(qc[h], qs[h]) for h in range(32)]
+        for j in range(5):
+            kv = deq(kc[j], ks[j])
+            ref = Fraction(0)
+            for h in range(32):
+                dot = sum(a * b for a, b in zip(qv[h], kv))
+                ref += Fraction(float(w[h])) * max(dot, Fraction(0))
+            assert got[j] == pytest.approx(float(ref), rel=1e-14, abs=1e-300)
+
+
+def test_scores_fp4_query_reduces_to_bf16_query():
+    """A query already exact in MXFP4 (each 32-block: E2M1 values times one
+    power of two, with a largest magnitude of 4 or 6 so the MX exponent
+    rule returns that power) scores as the bf16-query path does."""
+    rng = np.random.default_rng(12)
+    vals = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    q = rng.choice(vals, size=(32, 4, 32)) * rng.choice([-1, 1], size=(32, 4, 32))
+    q[..., 0] = rng.choice([4.0, 6.0], size=(32, 4))   # pins the block max
+    q = q * np.exp2(rng.integers(-6, 6, size=(32, 4, 1)))
+    q = q.reshape(32, 128).astype(np.float32)
+    qc, qs = O.pack_idx(q)
+    assert np.array_equal(O.unpack_idx(qc, qs), q.astype(np.float64))
+    c = _case(40, 13)
+    keys = O.unpack_idx(c["ic"], c["is_"])
+    a = O.indexer_scores_fp4q(qc, qs, c["w"], keys)
+    b = O.indexer_scores(_bf16(q), c["w"], keys)     # q is exact in bf16
+    assert np.array_equal(a, b)
 
 
 # --------------------------------------------------------------- top-k ----
