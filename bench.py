@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--query", choices=("bf16", "mxfp4"), default="bf16",
+                    help="indexer query format of the headline step (the "
+                         "other is reported under variants)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="counter-collection run: plain indexer launches on "
                          "rotated cache replicas, then a float32 copy kernel "
@@ -48,25 +51,32 @@ def n_blocks(wl):
     return -(-wl.n // wl.pool[1]) if wl.pool else 0
 
 
-def algorithmic_bytes(wl):
+def query_bytes(query):
+    """Indexer query bytes per sequence: 32 x 128 bf16, or the 32 heads as
+    MXFP4 (64 code + 4 scale bytes each)."""
+    return 32 * 68 if query == "mxfp4" else 32 * 128 * 2
+
+
+def algorithmic_bytes(wl, query="bf16"):
     """Bytes the method must move for one query through a Full layer:
     the indexer keys scanned (68 n; hierarchically 256 per bf16 block key
     plus 68 per pool member), 288 k (chosen main entries), 512 n_swa
-    (window), 8192 (bf16 indexer query) + 128 (head weights), 65536 (bf16
-    query), 65536 (bf16 output) and 4 k (top-k ids written)."""
+    (window), the indexer query (8192 bf16 or 2176 MXFP4) + 128 (head
+    weights), 65536 (bf16 query), 65536 (bf16 output) and 4 k (top-k ids
+    written)."""
     scan = (256 * n_blocks(wl) + 68 * wl.pool[0] * wl.pool[1] if wl.pool
             else 68 * wl.n)
-    return (scan + 288 * wl.k + 512 * wl.n_swa + 8192 + 128 + 65536
-            + 65536 + 4 * wl.k)
+    return (scan + 288 * wl.k + 512 * wl.n_swa + query_bytes(query) + 128
+            + 65536 + 65536 + 4 * wl.k)
 
 
-def indexer_bytes(wl):
+def indexer_bytes(wl, query="bf16"):
     """Algorithmic bytes of one launch of the scan kernel the roofline is
     quoted on: the MXFP4 keys of every visible entry (hierarchically: the
     bf16 block keys of every block) plus the per-sequence query and
     weights."""
     per = 256 * n_blocks(wl) if wl.pool else 68 * wl.n
-    return wl.B * (per + 8192 + 128)
+    return wl.B * (per + query_bytes(query) + 128)
 
 
 def source_hash():
@@ -77,9 +87,10 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(launch_bytes_alg):
-    """HBM bytes per indexer launch from the committed rocprofv3 counter
-    summary, or None when it is absent or the kernel changed since."""
+def traffic_from_profile(query):
+    """HBM bytes per indexer launch (the scan with a bf16 or an MXFP4 query)
+    from the committed rocprofv3 counter summary, or None when it is absent
+    or the kernel changed since."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             prof = json.load(f)
@@ -87,7 +98,7 @@ def traffic_from_profile(launch_bytes_alg):
         return None
     if prof.get("source_hash") != source_hash():
         return None
-    return prof.get("hbm_bytes_per_launch")
+    return prof.get("kernels", {}).get(query, {}).get("hbm_bytes_per_launch")
 
 
 def replicate(st, R):
@@ -109,6 +120,54 @@ def replicate(st, R):
     return reps, planes
 
 
+def time_steps(step, args, R, out, ids):
+    """Eager and HIP-graph time per step of `step(i)` (i picks the cache
+    replica).  The graph holds one step per replica (R steps) and is
+    replayed until at least K steps have run; a replay must reproduce the
+    eager result bit for bit."""
+    import torch
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / args.steps
+    if args.no_graph:
+        return eager_s, None, args.steps
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in range(R):
+            step(r)          # warm the capture path on this stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            step(r)
+    reps_needed = max(1, math.ceil(args.steps / R))
+    steps_run = reps_needed * R
+    for _ in range(max(1, args.warmup // R)):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps_needed):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t0) / steps_run
+    step(R - 1)
+    torch.cuda.synchronize()
+    e_out, e_ids = out.clone(), ids.clone()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), e_out.view(torch.int16))
+    assert torch.equal(ids, e_ids)
+    del g
+    return eager_s, graph_s, steps_run
+
+
 def run_gpu(args, wl):
     import torch
     from fp4_kv_cache_amd import csa2, workload
@@ -123,56 +182,23 @@ def run_gpu(args, wl):
     ids = torch.empty((wl.B, k), dtype=torch.int32, device=dev)
     ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, wl.B, wl.n, k,
                                             wl.pool), dev)
+    # The MXFP4 indexer query (V4's FP4 indexer query): an input of the
+    # layer call like the bf16 one, packed once outside the timed steps.
+    qc, qs = csa2.pack_query_fp4(st.q_idx)
 
-    def step(i):
+    def step_bf16(i):
         csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
                                 st.swa[0], st.n_swa, k, st.scale,
                                 pool=wl.pool, out=out, topk_out=ids, ws=ws)
 
-    # -- eager
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    eager_s = (time.perf_counter() - t0) / args.steps
+    def step_mxfp4(i):
+        csa2.sparse_attn_decode_fp4q(reps[i % R], qc, qs, st.w, st.q[0],
+                                     st.swa[0], st.n_swa, k, st.scale,
+                                     pool=wl.pool, out=out, topk_out=ids,
+                                     ws=ws)
 
-    # -- HIP graph: one graph holding one step per replica (R steps),
-    # replayed until K steps have run.
-    graph_s = None
-    steps_run = args.steps
-    if not args.no_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for r in range(R):
-                step(r)          # warm the capture path on this stream
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in range(R):
-                step(r)
-        reps_needed = max(1, math.ceil(args.steps / R))
-        steps_run = reps_needed * R
-        for _ in range(max(1, args.warmup // R)):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps_needed):
-            g.replay()
-        torch.cuda.synchronize()
-        graph_s = (time.perf_counter() - t0) / steps_run
-        # a replay must reproduce the eager result bit for bit
-        step(R - 1)
-        torch.cuda.synchronize()
-        e_out, e_ids = out.clone(), ids.clone()
-        g.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), e_out.view(torch.int16))
-        assert torch.equal(ids, e_ids)
+    steps = {"bf16": step_bf16, "mxfp4": step_mxfp4}
+    timing = {q: time_steps(fn, args, R, out, ids) for q, fn in steps.items()}
 
     # -- per-kernel durations with HIP events on the launch stream: the same
     # kernels through the component calls, M back-to-back launches of one
@@ -192,14 +218,15 @@ def run_gpu(args, wl):
     tk_ws = csa2.workspace(csa2.workspace_size(csa2.OP_TOPK, wl.B, ld, tk_k), dev)
     at_ws = csa2.workspace(csa2.workspace_size(csa2.OP_REUSE, wl.B, wl.n, k), dev)
 
-    def k_idx(r):
+    def k_idx(r, query="bf16"):
         pl = planes[r]
-        if wl.pool:
-            csa2.indexer_score(csa2.KEYS_BF16, pl[4], None, nvalid, st.q_idx,
-                               st.w, out=scores)
+        kf, kc, ks = ((csa2.KEYS_BF16, pl[4], None) if wl.pool
+                      else (csa2.KEYS_MXFP4, pl[2], pl[3]))
+        if query == "mxfp4":
+            csa2.indexer_score_fp4q(kf, kc, ks, nvalid, qc, qs, st.w,
+                                    out=scores)
         else:
-            csa2.indexer_score(csa2.KEYS_MXFP4, pl[2], pl[3], nvalid,
-                               st.q_idx, st.w, out=scores)
+            csa2.indexer_score(kf, kc, ks, nvalid, st.q_idx, st.w, out=scores)
 
     def k_topk(r):
         csa2.topk(scores, tk_k, n_valid=nvalid, block=tk_block,
@@ -226,20 +253,21 @@ def run_gpu(args, wl):
 
     M = max(8, min(args.steps, 200))
     k_idx(0)
-    t_idx = timed(k_idx, M)
+    t_idx = {"bf16": timed(k_idx, M),
+             "mxfp4": timed(lambda r: k_idx(r, "mxfp4"), M)}
     t_tk = timed(k_topk, M)
     t_at = timed(k_attn, M)
-    return dict(eager_s=eager_s, graph_s=graph_s, t_idx=t_idx, t_topk=t_tk,
-                t_attn=t_at, replicas=R, per_call=per_call, st=st,
-                steps_run=steps_run)
+    return dict(timing=timing, t_idx=t_idx, t_topk=t_tk, t_attn=t_at,
+                replicas=R, st=st)
 
 
 COPY_ELEMS = 64 << 20          # float32 elements of the calibration copy
 
 
 def run_pmc_pass(args, wl):
-    """Launch sequence for rocprofv3 --pmc: M plain indexer launches (the
-    roofline kernel, same arguments as the timed ones), then 4 copies
+    """Launch sequence for rocprofv3 --pmc: M plain indexer launches with
+    the bf16 query, then M with the MXFP4 query (the roofline kernels, same
+    arguments as the timed ones), then 4 copies
     y = x * 1 over COPY_ELEMS float32 (a kernel whose HBM bytes are known:
     4 * COPY_ELEMS read and written)."""
     import torch
@@ -251,11 +279,16 @@ def run_pmc_pass(args, wl):
     R = args.replicas or max(1, math.ceil(2 * 256e6 / per_call) + 1)
     reps, planes = replicate(st, R)
     scores = torch.empty((wl.B, wl.n), dtype=torch.float32, device=dev)
+    qc, qs = csa2.pack_query_fp4(st.q_idx)
     M = max(8, min(args.steps, 64))
     for i in range(M):
         pl = planes[i % R]
         csa2.indexer_score(csa2.KEYS_MXFP4, pl[2], pl[3], st.n_entries,
                            st.q_idx, st.w, out=scores)
+    for i in range(M):
+        pl = planes[i % R]
+        csa2.indexer_score_fp4q(csa2.KEYS_MXFP4, pl[2], pl[3], st.n_entries,
+                                qc, qs, st.w, out=scores)
     torch.cuda.synchronize()
     x = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
@@ -263,7 +296,8 @@ def run_pmc_pass(args, wl):
         torch.mul(x, 1.0, out=y)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_pass": True, "indexer_launches": M,
-                      "indexer_algorithmic_bytes": indexer_bytes(wl),
+                      "indexer_algorithmic_bytes": {
+                          q: indexer_bytes(wl, q) for q in ("bf16", "mxfp4")},
                       "copy_bytes_each_way": 4 * COPY_ELEMS}))
 
 
@@ -338,20 +372,39 @@ def main():
         run_pmc_pass(args, wl)
         return
     g = run_gpu(args, wl)
-    step_s = g["graph_s"] if g["graph_s"] is not None else g["eager_s"]
-    value = wl.B / step_s
-    idx_alg = indexer_bytes(wl)
-    achieved = idx_alg / g["t_idx"] / 1e9
-    traffic = traffic_from_profile(idx_alg) if args.workload == 1 else None
-    scan = ("indexer_kernel<1> (bf16 block-key scan)" if wl.pool
-            else "indexer_kernel<0> (MXFP4 scan)")
+    scan_name = ("indexer_kernel<1, *, Q> (bf16 block-key scan)" if wl.pool
+                 else "indexer_kernel<0, *, Q> (MXFP4 scan)")
+
+    def summary(query):
+        eager_s, graph_s, steps_run = g["timing"][query]
+        step_s = graph_s if graph_s is not None else eager_s
+        idx_alg = indexer_bytes(wl, query)
+        achieved = idx_alg / g["t_idx"][query] / 1e9
+        per_call = wl.B * algorithmic_bytes(wl, query)
+        qf = "true" if query == "mxfp4" else "false"
+        return dict(
+            step_s=step_s, eager_s=eager_s, graph_s=graph_s,
+            steps_run=steps_run, per_call=per_call,
+            roofline={"bound": "hbm", "achieved": achieved,
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBS,
+                      "traffic": (traffic_from_profile(query)
+                                  if args.workload == 1 else None),
+                      "kernel": scan_name.replace("Q", qf),
+                      "algorithmic_bytes_per_launch": idx_alg,
+                      "avg_launch_us": g["t_idx"][query] * 1e6})
+
+    head = summary(args.query)
+    other = "mxfp4" if args.query == "bf16" else "bf16"
+    alt = summary(other)
+    step_s = head["step_s"]
     line = {
         "metric": "CSA2 decode query-tokens/s per layer at 64K ctx; "
                   "achieved HBM GB/s vs peak",
-        "value": value,
+        "value": wl.B / step_s,
         "unit": "query-tokens/s",
         "n_gpus": 1,
-        "steps": g["steps_run"],
+        "steps": head["steps_run"],
         "warmup": args.warmup,
         "ms_per_step": step_s * 1e3,
         "higher_is_better": True,
@@ -362,23 +415,22 @@ def main():
         "config": {"workload": wl.name, "global_batch": wl.B,
                    "entries_per_seq": wl.n, "context": wl.ctx, "m": wl.m,
                    "k": wl.k, "n_swa": wl.n_swa, "heads": 64,
-                   "head_dim": 512, "indexer": "32 heads x 128, MXFP4",
+                   "head_dim": 512, "indexer": "32 heads x 128, MXFP4 keys",
+                   "indexer_query": args.query,
                    "pool": list(wl.pool) if wl.pool else None,
                    "cache_replicas": g["replicas"],
-                   "launch": "hip-graph" if g["graph_s"] else "eager"},
-        "roofline": {"bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic,
-                     "kernel": scan,
-                     "algorithmic_bytes_per_launch": idx_alg,
-                     "avg_launch_us": g["t_idx"] * 1e6},
-        "step_hbm": {"algorithmic_bytes": g["per_call"],
-                     "achieved_GBs": g["per_call"] / step_s / 1e9,
-                     "frac": g["per_call"] / step_s / 1e9 / HBM_PEAK_GBS},
-        "kernels_us": {"indexer": g["t_idx"] * 1e6, "topk": g["t_topk"] * 1e6,
+                   "launch": "hip-graph" if head["graph_s"] else "eager"},
+        "roofline": head["roofline"],
+        "step_hbm": {"algorithmic_bytes": head["per_call"],
+                     "achieved_GBs": head["per_call"] / step_s / 1e9,
+                     "frac": head["per_call"] / step_s / 1e9 / HBM_PEAK_GBS},
+        "kernels_us": {"indexer": g["t_idx"][args.query] * 1e6,
+                       "topk": g["t_topk"] * 1e6,
                        "attention": g["t_attn"] * 1e6},
-        "eager_ms_per_step": g["eager_s"] * 1e3,
+        "eager_ms_per_step": head["eager_s"] * 1e3,
+        "variants": {f"indexer_query_{other}": {
+            "value": wl.B / alt["step_s"], "ms_per_step": alt["step_s"] * 1e3,
+            "roofline": alt["roofline"]}},
     }
     if not args.no_cpu:
         cpu = run_cpu(wl, args.cpu_seconds)

@@ -19,7 +19,8 @@ OP_TOPK, OP_DECODE, OP_REUSE = 0, 1, 2
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGNMENT",
           4: "WORKSPACE", 5: "HIP"}
 EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
-           "csa2_indexer_score", "csa2_topk", "csa2_sparse_attn_decode",
+           "csa2_indexer_score", "csa2_indexer_score_fp4q", "csa2_topk",
+           "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_fp4q",
            "csa2_reuse_attn", "csa2_workspace_size", "csa2_entry_bytes",
            "csa2_kv_bytes_per_token", "csa2_last_error", "csa2_version"]
 
@@ -66,11 +67,17 @@ def load(path=None):
         "csa2_build_block_keys": (I32, [P, P, I64, P, I32, I32, P, P]),
         "csa2_indexer_score": (I32, [I32, P, P, I64, P, P, I32, P, P, I32, P,
                                      P]),
+        "csa2_indexer_score_fp4q": (I32, [I32, P, P, I64, P, P, I32, P, P,
+                                          P, I32, P, P]),
         "csa2_topk": (I32, [P, I64, P, P, I32, I32, I32, P, P, P, SZ, P]),
         "csa2_sparse_attn_decode": (I32, [ctypes.POINTER(CacheDesc), P, P, P,
                                           P, P, I32, I32, F32,
                                           ctypes.POINTER(PoolOpts), P, P, P,
                                           SZ, P]),
+        "csa2_sparse_attn_decode_fp4q": (I32, [ctypes.POINTER(CacheDesc), P,
+                                               P, P, P, P, P, I32, I32, F32,
+                                               ctypes.POINTER(PoolOpts), P, P,
+                                               P, SZ, P]),
         "csa2_reuse_attn": (I32, [P, P, I64, P, I32, P, P, P, I32, F32, P, P,
                                   SZ, P]),
         "csa2_workspace_size": (SZ, [I32, I32, I64, I32,
@@ -192,6 +199,32 @@ def indexer_score(keyfmt, k_codes, k_scales, n_entries, q_idx, w, cand=None,
     return out
 
 
+def pack_query_fp4(q_idx):
+    """The MXFP4 planes of bf16 indexer queries [B, 32, 128]: codes
+    [B, 32, 64] u8 and scales [B, 32, 4] u8 (csa2_pack_kv, FMT_IDX)."""
+    B = q_idx.shape[0]
+    codes, scales = pack_kv(FMT_IDX, q_idx.reshape(B * 32, 128).float())
+    return codes.view(B, 32, 64), scales.view(B, 32, 4)
+
+
+def indexer_score_fp4q(keyfmt, k_codes, k_scales, n_entries, q_codes,
+                       q_scales, w, cand=None, out=None):
+    """indexer_score with an MXFP4 query (pack_query_fp4 planes)."""
+    B, n_cap = k_codes.shape[0], k_codes.shape[1]
+    rows = n_cap if cand is None else cand.shape[1]
+    if out is None:
+        out = torch.empty((B, rows), dtype=torch.float32,
+                          device=k_codes.device)
+    _need(out, torch.float32, (B, rows), "out")
+    _need(q_codes, torch.uint8, (B, 32, 64), "q_codes")
+    _need(q_scales, torch.uint8, (B, 32, 4), "q_scales")
+    _check(load().csa2_indexer_score_fp4q(
+        keyfmt, _ptr(k_codes), _ptr(k_scales), n_cap, _ptr(n_entries),
+        _ptr(cand), 0 if cand is None else cand.shape[1], _ptr(q_codes),
+        _ptr(q_scales), _ptr(w), B, _ptr(out), _stream()))
+    return out
+
+
 def topk(scores, k, n_valid=None, ids=None, block=1, limit=None, ws=None,
          out=None):
     B, ld = scores.shape
@@ -236,6 +269,32 @@ def sparse_attn_decode(cache, q_idx, w, q, swa, n_swa, k, scale, pool=None,
         ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
         _ptr(n_swa), B, k, float(scale), ctypes.byref(po) if po else None,
         _ptr(out), _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
+    return out, topk_out
+
+
+def sparse_attn_decode_fp4q(cache, q_codes, q_scales, w, q, swa, n_swa, k,
+                            scale, pool=None, out=None, topk_out=None,
+                            ws=None):
+    """sparse_attn_decode with an MXFP4 indexer query (pack_query_fp4
+    planes)."""
+    B = q.shape[0]
+    dev = q.device
+    _need(q_codes, torch.uint8, (B, 32, 64), "q_codes")
+    _need(q_scales, torch.uint8, (B, 32, 4), "q_scales")
+    if out is None:
+        out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
+    if topk_out is None:
+        topk_out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    po = PoolOpts(*pool) if pool is not None else None
+    if ws is None:
+        need = load().csa2_workspace_size(OP_DECODE, B, cache.n_cap, k,
+                                          ctypes.byref(po) if po else None)
+        ws = workspace(need, dev)
+    _check(load().csa2_sparse_attn_decode_fp4q(
+        ctypes.byref(cache), _ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(q),
+        _ptr(swa), _ptr(n_swa), B, k, float(scale),
+        ctypes.byref(po) if po else None, _ptr(out), _ptr(topk_out), _ptr(ws),
+        ws.numel(), _stream()))
     return out, topk_out
 
 

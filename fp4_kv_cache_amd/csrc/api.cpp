@@ -262,12 +262,25 @@ csa2_status csa2_build_block_keys(const uint8_t* idx_codes,
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_build_block_keys launch");
 }
 
-csa2_status csa2_indexer_score(int32_t keyfmt, const void* k_codes,
+namespace {
+// Checks the indexer query (bf16, or MXFP4 planes when q_scales is set).
+csa2_status check_query(const csa2::IndexQuery& iq) {
+  if (!iq.q || !iq.w) return fail(CSA2_ERR_INVALID_ARG, "null indexer query");
+  if (!aligned(iq.q, 16) || !aligned(iq.w, 4) ||
+      (iq.q_scales && !aligned(iq.q_scales, 4)))
+    return fail(CSA2_ERR_ALIGNMENT, "the indexer query needs 16-byte "
+                "(codes) and 4-byte (scales, w) alignment");
+  return CSA2_OK;
+}
+size_t query_bytes(const csa2::IndexQuery& iq, int32_t B) {
+  return (size_t)B * 32 * (iq.q_scales ? 64 : 256);
+}
+
+csa2_status indexer_score_impl(int32_t keyfmt, const void* k_codes,
                                const void* k_scales, int64_t n_cap,
                                const int32_t* n_entries, const int32_t* cand,
-                               int32_t n_cand, const uint16_t* q_idx,
-                               const float* w, int32_t B, float* scores,
-                               void* stream) {
+                               int32_t n_cand, const csa2::IndexQuery& iq,
+                               int32_t B, float* scores, void* stream) {
   if (keyfmt != CSA2_KEYS_MXFP4 && keyfmt != CSA2_KEYS_BF16)
     return fail(CSA2_ERR_INVALID_ARG, "unknown key format %d", keyfmt);
   if (B < 0 || n_cap < 0 || n_cap > kMaxCap || (cand && n_cand < 0))
@@ -277,27 +290,54 @@ csa2_status csa2_indexer_score(int32_t keyfmt, const void* k_codes,
                 "the indexer needs n_cap <= 2^24 (got %lld)", (long long)n_cap);
   const int64_t rows = cand ? n_cand : n_cap;
   if (B == 0 || rows == 0) return CSA2_OK;
-  if (!k_codes || !n_entries || !q_idx || !w || !scores)
+  if (!k_codes || !n_entries || !scores)
     return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  csa2_status qs = check_query(iq);
+  if (qs) return qs;
   if (keyfmt == CSA2_KEYS_MXFP4 && !k_scales)
     return fail(CSA2_ERR_INVALID_ARG, "MXFP4 keys need k_scales");
   if (keyfmt == CSA2_KEYS_BF16 && k_scales)
     return fail(CSA2_ERR_INVALID_ARG, "bf16 keys take no k_scales");
-  if (!aligned(k_codes, 16) || !aligned(q_idx, 16) || !aligned(w, 4) ||
-      !aligned(scores, 4) || (k_scales && !aligned(k_scales, 4)))
+  if (!aligned(k_codes, 16) || !aligned(scores, 4) ||
+      (k_scales && !aligned(k_scales, 4)))
     return fail(CSA2_ERR_ALIGNMENT,
-                "k_codes and q_idx need 16-byte, k_scales, w, scores 4-byte "
-                "alignment");
+                "k_codes needs 16-byte, k_scales and scores 4-byte alignment");
   const size_t kbytes = (size_t)B * n_cap * (keyfmt == CSA2_KEYS_MXFP4 ? 64 : 256);
   if (overlap(scores, (size_t)B * rows * 4, k_codes, kbytes) ||
-      overlap(scores, (size_t)B * rows * 4, q_idx, (size_t)B * 32 * 128 * 2))
+      overlap(scores, (size_t)B * rows * 4, iq.q, query_bytes(iq, B)))
     return fail(CSA2_ERR_INVALID_ARG, "scores overlap an input");
   csa2_status st = need_device();
   if (st) return st;
   hipError_t e = csa2::launch_indexer(
       keyfmt, k_codes, static_cast<const uint8_t*>(k_scales), n_cap, n_entries,
-      cand, rows, q_idx, w, B, scores, static_cast<hipStream_t>(stream));
+      cand, rows, iq, B, scores, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_indexer_score launch");
+}
+}  // namespace
+
+csa2_status csa2_indexer_score(int32_t keyfmt, const void* k_codes,
+                               const void* k_scales, int64_t n_cap,
+                               const int32_t* n_entries, const int32_t* cand,
+                               int32_t n_cand, const uint16_t* q_idx,
+                               const float* w, int32_t B, float* scores,
+                               void* stream) {
+  return indexer_score_impl(keyfmt, k_codes, k_scales, n_cap, n_entries, cand,
+                            n_cand, csa2::IndexQuery{q_idx, nullptr, w}, B,
+                            scores, stream);
+}
+
+csa2_status csa2_indexer_score_fp4q(int32_t keyfmt, const void* k_codes,
+                                    const void* k_scales, int64_t n_cap,
+                                    const int32_t* n_entries,
+                                    const int32_t* cand, int32_t n_cand,
+                                    const uint8_t* q_codes,
+                                    const uint8_t* q_scales, const float* w,
+                                    int32_t B, float* scores, void* stream) {
+  if (!q_scales && q_codes)
+    return fail(CSA2_ERR_INVALID_ARG, "an MXFP4 query needs q_scales");
+  return indexer_score_impl(keyfmt, k_codes, k_scales, n_cap, n_entries, cand,
+                            n_cand, csa2::IndexQuery{q_codes, q_scales, w}, B,
+                            scores, stream);
 }
 
 csa2_status csa2_topk(const float* scores, int64_t ld, const int32_t* n_valid,
@@ -351,13 +391,13 @@ csa2_status csa2_reuse_attn(const uint8_t* main_codes,
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_reuse_attn launch");
 }
 
-csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
-                                    const uint16_t* q_idx, const float* w,
-                                    const uint16_t* q, const uint8_t* swa,
-                                    const int32_t* n_swa, int32_t B, int32_t k,
-                                    float scale, const csa2_pool_opts* pool,
-                                    uint16_t* out, int32_t* topk_out, void* ws,
-                                    size_t ws_bytes, void* stream) {
+namespace {
+csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
+                        const uint16_t* q, const uint8_t* swa,
+                        const int32_t* n_swa, int32_t B, int32_t k,
+                        float scale, const csa2_pool_opts* pool,
+                        uint16_t* out, int32_t* topk_out, void* ws,
+                        size_t ws_bytes, void* stream) {
   if (!kv) return fail(CSA2_ERR_INVALID_ARG, "null cache descriptor");
   csa2_status st = check_attn_common(kv->main_codes, kv->main_scales,
                                      kv->n_cap, q, swa, n_swa, B, k, scale, out);
@@ -366,13 +406,14 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
   if (st) return st;
   if (B == 0) return CSA2_OK;
   if (kv->n_cap < 1) return fail(CSA2_ERR_INVALID_ARG, "n_cap must be >= 1");
-  if (!kv->idx_codes || !kv->idx_scales || !kv->n_entries || !q_idx || !w ||
-      !topk_out)
+  if (!kv->idx_codes || !kv->idx_scales || !kv->n_entries || !topk_out)
     return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  st = check_query(iq);
+  if (st) return st;
   if (pool && !kv->block_keys)
     return fail(CSA2_ERR_INVALID_ARG, "a pool needs kv->block_keys");
   if (!aligned(kv->idx_codes, 16) || !aligned(kv->idx_scales, 4) ||
-      !aligned(q_idx, 16) || !aligned(w, 4) || !aligned(topk_out, 4) ||
+      !aligned(topk_out, 4) ||
       (pool && !aligned(kv->block_keys, 16)))
     return fail(CSA2_ERR_ALIGNMENT, "misaligned indexer argument");
   const DecodeLayout L = decode_layout(B, kv->n_cap, k, pool);
@@ -391,7 +432,7 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
     float* scores = reinterpret_cast<float*>(base + L.off_scores);
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, nullptr, kv->n_cap,
-                             q_idx, w, B, scores, s, tmax);
+                             iq, B, scores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
     e = csa2::launch_row_select(scores, tmax, true, round32(kv->n_cap),
                                 kv->n_cap, kv->n_entries, nullptr, B, k, 1,
@@ -405,8 +446,7 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
     e = csa2::launch_nblocks(kv->n_entries, B, pool->block, nblk, s);
     if (e != hipSuccess) return hip_fail(e, "block count launch");
     e = csa2::launch_indexer(CSA2_KEYS_BF16, kv->block_keys, nullptr, L.nb,
-                             nblk, nullptr, L.nb, q_idx, w, B, bscores, s,
-                             tmax);
+                             nblk, nullptr, L.nb, iq, B, bscores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "block indexer launch");
     e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb, nblk,
                                 nullptr, B, L.kb, pool->block, kv->n_entries,
@@ -414,7 +454,7 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
     if (e != hipSuccess) return hip_fail(e, "block top-k launch");
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, pool_ids, L.n_cand,
-                             q_idx, w, B, pscores, s, tmax);
+                             iq, B, pscores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
     e = csa2::launch_row_select(pscores, tmax, true, round32(L.n_cand),
                                 L.n_cand, nullptr, pool_ids, B, k, 1, nullptr,
@@ -425,6 +465,31 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
                         k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return CSA2_OK;
+}
+}  // namespace
+
+csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
+                                    const uint16_t* q_idx, const float* w,
+                                    const uint16_t* q, const uint8_t* swa,
+                                    const int32_t* n_swa, int32_t B, int32_t k,
+                                    float scale, const csa2_pool_opts* pool,
+                                    uint16_t* out, int32_t* topk_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  return decode_impl(kv, csa2::IndexQuery{q_idx, nullptr, w}, q, swa, n_swa,
+                     B, k, scale, pool, out, topk_out, ws, ws_bytes, stream);
+}
+
+csa2_status csa2_sparse_attn_decode_fp4q(
+    const csa2_cache* kv, const uint8_t* q_codes, const uint8_t* q_scales,
+    const float* w, const uint16_t* q, const uint8_t* swa,
+    const int32_t* n_swa, int32_t B, int32_t k, float scale,
+    const csa2_pool_opts* pool, uint16_t* out, int32_t* topk_out, void* ws,
+    size_t ws_bytes, void* stream) {
+  if (!q_scales && q_codes)
+    return fail(CSA2_ERR_INVALID_ARG, "an MXFP4 query needs q_scales");
+  return decode_impl(kv, csa2::IndexQuery{q_codes, q_scales, w}, q, swa,
+                     n_swa, B, k, scale, pool, out, topk_out, ws, ws_bytes,
+                     stream);
 }
 
 }  // extern "C"

@@ -20,6 +20,21 @@
 // folded with one cross-half swap.  HBM traffic per entry: 64 + 4 bytes
 // read, 4 bytes of score written.
 //
+// FP4 query ("DeepSeek-V4.1-Flash, 2. Architecture" course notes, 2.4.4:
+// V4 trains the indexer query and key for FP4, OCP MXFP4, so that scoring
+// itself runs on FP4; the mer.run page, section 5, says the same).  With
+// the query also in MXFP4, an MXFP4 tile is two issues of the gfx950 scaled
+// matrix op v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 x E2M1 with one E8M0
+// scale per 32 values on each side) straight from the loaded code bytes:
+// no conversion at all.  Operand layout of that op: lane l holds row (or
+// column) l % 32 and the 32 consecutive K values 32*(l/32) .. +31, two per
+// byte, low nibble first -- exactly the stored order -- and the scale byte
+// picked by op_sel.  Lane half h feeds dims 64h .. 64h+31 to the first
+// issue and 64h+32 .. 64h+63 to the second (the query in the same order),
+// so its 32 code bytes are the two operands as loaded and its scale bytes
+// are 2h and 2h+1.  Every product is exact; the sums are float32.  The
+// bf16 block keys take the query dequantised to bf16, which is exact.
+//
 // Tile maxima (the decode path): each 32-row tile's largest score is also
 // written (one wave reduction per tile); the top-k stage uses them to read
 // only the tiles that can hold a winner.
@@ -49,26 +64,27 @@ template <> struct RawKey<1> {       // bf16: 64 dims = 128 bytes
 // loads in flight with exact wait counts.  `codes`/`scales` point at the
 // sequence's first row and `row` is the row within it: byte offsets stay
 // below 2^32 (n_cap <= 2^24), one uniform base plus a 32-bit lane offset.
-template <int KEYFMT>
-__device__ __forceinline__ void load_key(RawKey<KEYFMT>& r, const void* codes,
+// HALF_SCALES (scaled matrix op): only this lane half's two scale bytes
+// (2*half, 2*half+1), as bits 0-15, so the op reads the loaded register as
+// it is and nothing waits on the load before the op itself.
+template <int KEYFMT, bool HALF_SCALES>
+__device__ __forceinline__ void load_key(RawKey<0>& r, const void* codes,
                                          const uint8_t* scales, uint32_t row,
-                                         int half);
-
-template <>
-__device__ __forceinline__ void load_key<0>(RawKey<0>& r, const void* codes,
-                                            const uint8_t* scales,
-                                            uint32_t row, int half) {
+                                         int half) {
   const u32x4* p = reinterpret_cast<const u32x4*>(
       static_cast<const uint8_t*>(codes) + (row * 64u + 32u * half));
   r.c0 = p[0];
   r.c1 = p[1];
-  r.sc = *reinterpret_cast<const uint32_t*>(scales + row * 4u);
+  if constexpr (HALF_SCALES)
+    r.sc = *reinterpret_cast<const uint16_t*>(scales + (row * 4u + 2u * half));
+  else
+    r.sc = *reinterpret_cast<const uint32_t*>(scales + row * 4u);
 }
 
-template <>
-__device__ __forceinline__ void load_key<1>(RawKey<1>& r, const void* codes,
-                                            const uint8_t*, uint32_t row,
-                                            int half) {
+template <int KEYFMT, bool HALF_SCALES>
+__device__ __forceinline__ void load_key(RawKey<1>& r, const void* codes,
+                                         const uint8_t*, uint32_t row,
+                                         int half) {
   const u32x4* p = reinterpret_cast<const u32x4*>(
       static_cast<const uint8_t*>(codes) + (row * 256u + 128u * half));
 #pragma unroll
@@ -100,20 +116,36 @@ __device__ __forceinline__ bf16x8 key_operand<1>(const RawKey<1>& r, int s,
   return bits_to_bf8(r.v[s]);
 }
 
+// FP4 operand of the scaled matrix op: 32 E2M1 values in the low 16 bytes
+// (the upper half of the register group is not read for FP4).
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
+  i32x8 o;
+  o[0] = (int32_t)v[0]; o[1] = (int32_t)v[1];
+  o[2] = (int32_t)v[2]; o[3] = (int32_t)v[3];
+  o[4] = 0; o[5] = 0; o[6] = 0; o[7] = 0;
+  return o;
+}
+constexpr int kFmtFp4 = 4;          // E2M1 in the op's format fields
+
 // Tiles of loads kept in flight ahead of the matrix work.
 template <int KEYFMT> struct Depth { static constexpr int value = 2; };
 template <> struct Depth<1> { static constexpr int value = 1; };
 
 // KEYS: write selection keys (see score_key) instead of float scores, and
 // each 32-row tile's largest key to tmax[B][ceil(n_rows/32)].
-template <int KEYFMT, bool KEYS>
+// QFP4: the query is MXFP4 planes (codes q[B][32][64], scales
+// q_scales[B][32][4]) instead of bf16 q[B][32][128].
+template <int KEYFMT, bool KEYS, bool QFP4>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ cand, int64_t n_rows,
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    float* __restrict__ scores, uint32_t* __restrict__ tmax) {
+    const void* __restrict__ q_in, const uint8_t* __restrict__ q_scales,
+    const float* __restrict__ w, float* __restrict__ scores,
+    uint32_t* __restrict__ tmax) {
   constexpr int D = Depth<KEYFMT>::value;
+  constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int T = kTilesPerWave;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -137,22 +169,57 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   // are clamped to row 0.
   uint32_t row[T];
   uint32_t vmask = 0;
+  int64_t ent[T];
+  if (cand) {
+    // Every id load is issued before any is used (one wait, not one per
+    // tile).
+    int32_t cv[T];
+    const int32_t* crow = cand + (int64_t)b * n_rows;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t i = base + 32 * t + col;
+      cv[t] = crow[i < n_rows ? i : n_rows - 1];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) ent[t] = cv[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < T; ++t) ent[t] = base + 32 * t + col;
+  }
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int64_t i = base + 32 * t + col;
-    int64_t e = i;
-    if (cand) e = cand[(int64_t)b * n_rows + (i < n_rows ? i : n_rows - 1)];
+    const int64_t e = ent[t];
     const bool v = (i < n_rows) & (e >= 0) & (e < n);
     vmask |= (v ? 1u : 0u) << t;
     row[t] = v ? (uint32_t)e : 0u;
   }
 
-  // A operand: head `col`, dims 64*half + 8*s .. +7 for step s.
-  bf16x8 qa[8];
-  const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
-      q_idx + ((int64_t)b * kIdxHeads + col) * kIdxDim + 64 * half);
+  // A operand: head `col`, dims 64*half + 8*s .. +7 for step s (bf16), or
+  // the head's MXFP4 codes for dims 64*half .. +63 and its two scale bytes
+  // for them in bits 0-15 (scaled op).
+  bf16x8 qa[kScaledOp ? 1 : 8];
+  RawKey<0> q4;
+  if constexpr (QFP4) {
+    const int64_t head = (int64_t)b * kIdxHeads + col;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint8_t*>(q_in) + head * 64 + 32 * half);
+    q4.c0 = qp[0];
+    q4.c1 = qp[1];
+    q4.sc = *reinterpret_cast<const uint32_t*>(q_scales + head * 4);
+    if constexpr (kScaledOp) {
+      q4.sc >>= 16 * half;
+    } else {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) qa[s] = qrow[s];
+      for (int s = 0; s < 8; ++s) qa[s] = key_operand<0>(q4, s, half);
+    }
+  } else {
+    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
+        static_cast<const uint16_t*>(q_in) +
+        ((int64_t)b * kIdxHeads + col) * kIdxDim + 64 * half);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qa[s] = qrow[s];
+  }
   // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
   float wr[16];
 #pragma unroll
@@ -164,13 +231,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   RawKey<KEYFMT> buf[D + 1];
 #pragma unroll
   for (int t = 0; t < D; ++t)
-    load_key<KEYFMT>(buf[t], seq_codes, seq_scales, row[t], half);
+    load_key<KEYFMT, kScaledOp>(buf[t], seq_codes, seq_scales, row[t], half);
   float total[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (t + D < T)
-      load_key<KEYFMT>(buf[(t + D) % (D + 1)], seq_codes, seq_scales,
-                       row[t + D], half);
+      load_key<KEYFMT, kScaledOp>(buf[(t + D) % (D + 1)], seq_codes,
+                                  seq_scales, row[t + D], half);
     // MXFP4 keys: no branch around the tile -- a conditional block would
     // let the compiler sink this tile's loads into it (and serialise them);
     // tiles past the end compute on clamped rows and are masked out.  The
@@ -179,10 +246,20 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     if (KEYFMT == 0 || (t < nt && base + 32 * t < (cand ? n_rows : n))) {
       const RawKey<KEYFMT>& cur = buf[t % (D + 1)];
       f32x16 acc = {};
+      if constexpr (kScaledOp) {
+        const int32_t ks = (int32_t)cur.sc;   // bytes 2*half, 2*half+1
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fp4_operand(q4.c0), fp4_operand(cur.c0), acc, kFmtFp4, kFmtFp4,
+            0, (int32_t)q4.sc, 0, ks);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fp4_operand(q4.c1), fp4_operand(cur.c1), acc, kFmtFp4, kFmtFp4,
+            1, (int32_t)q4.sc, 1, ks);
+      } else {
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            qa[s], key_operand<KEYFMT>(cur, s, half), acc, 0, 0, 0);
+        for (int s = 0; s < 8; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              qa[s], key_operand<KEYFMT>(cur, s, half), acc, 0, 0, 0);
+      }
       // ReLU as an integer max on the float bits (negatives and -0 go to
       // +0; the dots are finite), weights, and the head sum in two chains.
       float p0 = 0.0f, p1 = 0.0f;
@@ -226,31 +303,50 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 
 }  // namespace
 
+namespace {
+template <int KEYFMT, bool KEYS, bool QFP4>
+void launch_one(dim3 grid, hipStream_t s, const void* k_codes,
+                const uint8_t* k_scales, int64_t n_cap,
+                const int32_t* n_entries, const int32_t* cand, int64_t n_rows,
+                const IndexQuery& iq, float* scores, uint32_t* tmax) {
+  hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256), 0,
+                     s, k_codes, k_scales, n_cap, n_entries, cand, n_rows,
+                     iq.q, iq.q_scales, iq.w, scores, tmax);
+}
+template <int KEYFMT, bool KEYS>
+void launch_q(dim3 grid, hipStream_t s, const void* k_codes,
+              const uint8_t* k_scales, int64_t n_cap, const int32_t* n_entries,
+              const int32_t* cand, int64_t n_rows, const IndexQuery& iq,
+              float* scores, uint32_t* tmax) {
+  if (iq.q_scales)
+    launch_one<KEYFMT, KEYS, true>(grid, s, k_codes, k_scales, n_cap,
+                                   n_entries, cand, n_rows, iq, scores, tmax);
+  else
+    launch_one<KEYFMT, KEYS, false>(grid, s, k_codes, k_scales, n_cap,
+                                    n_entries, cand, n_rows, iq, scores, tmax);
+}
+}  // namespace
+
 hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,
                           const int32_t* n_entries, const int32_t* cand,
-                          int64_t n_rows, const uint16_t* q_idx,
-                          const float* w, int B, float* scores, hipStream_t s,
-                          uint32_t* tmax) {
+                          int64_t n_rows, const IndexQuery& iq, int B,
+                          float* scores, hipStream_t s, uint32_t* tmax) {
   if (n_rows == 0 || B == 0) return hipSuccess;
   const dim3 grid((unsigned)((n_rows + kEntriesPerBlock - 1) / kEntriesPerBlock),
                   (unsigned)B);
   if (keyfmt == 0 && tmax)
-    hipLaunchKernelGGL((indexer_kernel<0, true>), grid, dim3(256), 0, s,
-                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
-                       q_idx, w, scores, tmax);
+    launch_q<0, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+                      n_rows, iq, scores, tmax);
   else if (keyfmt == 0)
-    hipLaunchKernelGGL((indexer_kernel<0, false>), grid, dim3(256), 0, s,
-                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
-                       q_idx, w, scores, tmax);
+    launch_q<0, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+                       n_rows, iq, scores, tmax);
   else if (tmax)
-    hipLaunchKernelGGL((indexer_kernel<1, true>), grid, dim3(256), 0, s,
-                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
-                       q_idx, w, scores, tmax);
+    launch_q<1, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+                      n_rows, iq, scores, tmax);
   else
-    hipLaunchKernelGGL((indexer_kernel<1, false>), grid, dim3(256), 0, s,
-                       k_codes, k_scales, n_cap, n_entries, cand, n_rows,
-                       q_idx, w, scores, tmax);
+    launch_q<1, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+                       n_rows, iq, scores, tmax);
   return hipGetLastError();
 }
 

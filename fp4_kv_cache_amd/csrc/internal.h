@@ -28,11 +28,18 @@ hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
 // (score_key, as uint32) instead, rows padded to a multiple of 32 entries
 // (scores[B][round_up(n_rows, 32)]), and each 32-row tile's largest key into
 // tmax[B][ceil(n_rows/32)].
+// The indexer query of every sequence: bf16 q[B][32][128] (q_scales null),
+// or MXFP4 planes q[B][32][64] codes + q_scales[B][32][4]; weights w[B][32].
+struct IndexQuery {
+  const void* q;
+  const uint8_t* q_scales;
+  const float* w;
+};
 hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,
                           const int32_t* n_entries, const int32_t* cand,
-                          int64_t n_rows, const uint16_t* q_idx,
-                          const float* w, int B, float* scores, hipStream_t s,
+                          int64_t n_rows, const IndexQuery& iq, int B,
+                          float* scores, hipStream_t s,
                           uint32_t* tmax = nullptr);
 
 // topk.hip

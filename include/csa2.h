@@ -157,6 +157,24 @@ csa2_status csa2_indexer_score(int32_t keyfmt, const void *k_codes,
                                const float *w, int32_t B, float *scores,
                                void *stream);
 
+/* csa2_indexer_score_fp4q -- the same scores with the indexer query itself
+ * in OCP MXFP4, as V4 trains it for FP4 scoring ([ARCH] 2.4.4; [KVC] 5):
+ *   q_codes   [B][32][64] E2M1 codes (16-byte aligned), q_scales [B][32][4]
+ *             E8M0: the CSA2_FMT_IDX planes of the 32 query heads (what
+ *             csa2_pack_kv(CSA2_FMT_IDX, q, 32 * B, ...) writes)
+ *   other arguments as in csa2_indexer_score.
+ * I_j = sum_h w_h * ReLU(deq(q_h) . K_j).  MXFP4 keys are scored from the
+ * FP4 codes directly (E2M1 x E2M1 products with their two scales: exact);
+ * bf16 keys against the exactly dequantised query.  Accumulation is
+ * float32. */
+csa2_status csa2_indexer_score_fp4q(int32_t keyfmt, const void *k_codes,
+                                    const void *k_scales, int64_t n_cap,
+                                    const int32_t *n_entries,
+                                    const int32_t *cand, int32_t n_cand,
+                                    const uint8_t *q_codes,
+                                    const uint8_t *q_scales, const float *w,
+                                    int32_t B, float *scores, void *stream);
+
 /* ------------------------------------------------------------------------
  * csa2_topk -- exact top-k per row ([V4] CSA step 2 top-k equation; [KVC]
  * 4.1 S_t = Top512).  Row b holds scores[b*ld + i], i < n_valid[b]
@@ -201,6 +219,17 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache *kv,
                                     float scale, const csa2_pool_opts *pool,
                                     uint16_t *out, int32_t *topk_out, void *ws,
                                     size_t ws_bytes, void *stream);
+
+/* csa2_sparse_attn_decode_fp4q -- csa2_sparse_attn_decode with the
+ * indexer query in MXFP4 planes (q_codes [B][32][64], q_scales [B][32][4],
+ * as in csa2_indexer_score_fp4q); every other argument, the workspace and
+ * the outputs as there. */
+csa2_status csa2_sparse_attn_decode_fp4q(
+    const csa2_cache *kv, const uint8_t *q_codes, const uint8_t *q_scales,
+    const float *w, const uint16_t *q, const uint8_t *swa,
+    const int32_t *n_swa, int32_t B, int32_t k, float scale,
+    const csa2_pool_opts *pool, uint16_t *out, int32_t *topk_out, void *ws,
+    size_t ws_bytes, void *stream);
 
 /* csa2_reuse_attn -- a Reuse-mode layer ([ARCH] 2.3.1; [KVC] 4.2 table):
  * no indexer; attention over the given top-k ids (entries < 0 skipped) of
