@@ -128,9 +128,14 @@ __device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
 }
 constexpr int kFmtFp4 = 4;          // E2M1 in the op's format fields
 
-// Tiles of loads kept in flight ahead of the matrix work.
-template <int KEYFMT> struct Depth { static constexpr int value = 2; };
-template <> struct Depth<1> { static constexpr int value = 1; };
+// Tiles of loads kept in flight ahead of the matrix work (the scaled-op
+// path does little per tile, so it keeps one more).
+template <int KEYFMT, bool SCALED> struct Depth {
+  static constexpr int value = SCALED ? 3 : 2;
+};
+template <bool SCALED> struct Depth<1, SCALED> {
+  static constexpr int value = 1;
+};
 
 // KEYS: write selection keys (see score_key) instead of float scores, and
 // each 32-row tile's largest key to tmax[B][ceil(n_rows/32)].
@@ -144,8 +149,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ q_in, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ w, float* __restrict__ scores,
     uint32_t* __restrict__ tmax) {
-  constexpr int D = Depth<KEYFMT>::value;
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
+  constexpr int D = Depth<KEYFMT, kScaledOp>::value;
   constexpr int T = kTilesPerWave;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
