@@ -208,6 +208,17 @@ def hier_pool(block_scores, n_entries, n_keep=2048, block=8):
     return out
 
 
+def block_max_scores(scores, n_entries, block=8):
+    """Block score of the hierarchical indexer as the pages define it,
+    [KVC] 4.3 equation and [ARCH] 2.3.2: s_b = max of the first Full
+    layer's fine scores I_j over the positions j < n_entries of block b.
+    Returns float64 [ceil(n_entries / block)]."""
+    nb = -(-n_entries // block)
+    pad = np.full(nb * block, -np.inf)
+    pad[:n_entries] = np.asarray(scores[:n_entries], dtype=np.float64)
+    return pad.reshape(nb, block).max(axis=1)
+
+
 # ---------------------------------------------------------- attention ----
 def mqa_decode(q_bits, keys, scale):
     """Shared-KV multi-query attention for one decode query, [V4] CSA step 3
@@ -270,3 +281,36 @@ def hier_layer(main_codes, main_scales, idx_codes, idx_scales, bkeys_bits,
     sel = topk(fine, k, ids=valid)
     kv = gather_keys(main_codes, main_scales, sel, swa_codes, n_swa)
     return sel, mqa_decode(q_bits, kv, scale), pool, fine
+
+
+def full_pool_layer(main_codes, main_scales, idx_codes, idx_scales,
+                    n_entries, q_idx_bits, w, q_bits, swa_codes, n_swa, k,
+                    scale, n_keep=2048, block=8):
+    """First Full layer of a hierarchical decoder group, [KVC] 4.3 and
+    [ARCH] 2.3.2 (Figure 5): the Full layer itself (its own top-k and
+    attention over every visible entry), plus the candidate pool of the
+    Reindex layers after it -- the n_keep blocks with the largest
+    block_max_scores, expanded to their positions < n_entries, ascending.
+    Returns (top-k ids, output, pool [n_keep * block], fine scores)."""
+    sel, out, sc = full_layer(main_codes, main_scales, idx_codes, idx_scales,
+                              n_entries, q_idx_bits, w, q_bits, swa_codes,
+                              n_swa, k, scale)
+    pool = hier_pool(block_max_scores(sc, n_entries, block), n_entries,
+                     n_keep, block)
+    return sel, out, pool, sc
+
+
+def reindex_layer(main_codes, main_scales, idx_codes, idx_scales, pool,
+                  q_idx_bits, w, q_bits, swa_codes, n_swa, k, scale):
+    """Reindex-mode layer, [KVC] 4.2 table and 4.3 equation: the layer's own
+    indexer query scores only the pool's positions (ids < 0 skipped) on the
+    shared indexer keys, its top-k among them, then attention over the
+    chosen main entries and the layer's own window.
+    Returns (top-k ids, output, pool scores)."""
+    pool = np.asarray(pool)
+    valid = pool[pool >= 0]
+    fine = indexer_scores(q_idx_bits, w, unpack_idx(idx_codes[valid],
+                                                    idx_scales[valid]))
+    sel = topk(fine, k, ids=valid)
+    kv = gather_keys(main_codes, main_scales, sel, swa_codes, n_swa)
+    return sel, mqa_decode(q_bits, kv, scale), fine

@@ -293,3 +293,65 @@ def test_attention_rows_with_far_apart_logits():
     ref = torch.nn.functional.scaled_dot_product_attention(
         qt, kt, kt, scale=SCALE)[0, :, 0, :].numpy()
     assert np.allclose(got, ref, rtol=1e-10, atol=1e-10)
+
+
+# ------------------------------------- hierarchical decoder group (pages) --
+def test_block_max_scores_bruteforce():
+    rng = np.random.default_rng(21)
+    sc = rng.standard_normal(101)
+    for n, block in ((101, 8), (96, 8), (7, 8), (50, 4), (33, 1)):
+        got = O.block_max_scores(sc, n, block)
+        nb = -(-n // block)
+        assert len(got) == nb
+        for bi in range(nb):
+            assert got[bi] == max(sc[j] for j in range(bi * block,
+                                                       min(n, bi * block + block)))
+
+
+def test_full_pool_bruteforce_with_ties():
+    c = _case(203, 22)
+    sel, out, pool, sc = O.full_pool_layer(
+        c["mc"], c["ms"], c["ic"], c["is_"], 203, c["qi"], c["w"], c["q"],
+        c["sw"], 128, 16, SCALE, n_keep=9, block=8)
+    # brute force: blocks by (-max, block id), first 9, expanded below n
+    bmax = [max(sc[j] for j in range(b * 8, min(203, b * 8 + 8)))
+            for b in range(26)]
+    order = sorted(range(26), key=lambda b: (-bmax[b], b))[:9]
+    want = sorted(j for b in order for j in range(b * 8, b * 8 + 8) if j < 203)
+    assert list(pool[:len(want)]) == want and np.all(pool[len(want):] == -1)
+    # planted tie: two blocks with the same maximum at the cut -> lower block
+    sc2 = np.zeros(40)
+    sc2[[3, 12, 20, 35]] = [5.0, 4.0, 4.0, 1.0]    # blocks 0, 1, 2, 4
+    p2 = O.hier_pool(O.block_max_scores(sc2, 40, 8), 40, 2, 8)
+    assert list(p2) == list(range(0, 16))
+
+
+def test_reindex_equals_full_when_pool_covers_all():
+    c = _case(150, 23)
+    sel_f, out_f, _ = O.full_layer(c["mc"], c["ms"], c["ic"], c["is_"], 150,
+                                   c["qi"], c["w"], c["q"], c["sw"], 128, 32,
+                                   SCALE)
+    pool = np.concatenate([np.arange(150), -np.ones(10, np.int64)])
+    sel_r, out_r, _ = O.reindex_layer(c["mc"], c["ms"], c["ic"], c["is_"],
+                                      pool, c["qi"], c["w"], c["q"], c["sw"],
+                                      128, 32, SCALE)
+    assert np.array_equal(sel_f, sel_r)
+    assert np.array_equal(out_f, out_r)
+
+
+def test_reindex_with_full_query_keeps_full_topk():
+    """Every block holding one of the Full layer's top-k has a block maximum
+    >= the k-th score and every other block's maximum is below it, so with
+    n_keep >= k the pool holds the whole top-k and a Reindex layer using
+    the Full layer's own query reproduces it (no ties at the boundary)."""
+    c = _case(3000, 24)
+    sel, out, pool, sc = O.full_pool_layer(
+        c["mc"], c["ms"], c["ic"], c["is_"], 3000, c["qi"], c["w"], c["q"],
+        c["sw"], 128, 64, SCALE, n_keep=64, block=8)
+    assert O.topk_gap(sc, 64) > 1e-9
+    assert set(sel.tolist()) <= set(pool.tolist())
+    sel_r, out_r, _ = O.reindex_layer(c["mc"], c["ms"], c["ic"], c["is_"],
+                                      pool, c["qi"], c["w"], c["q"], c["sw"],
+                                      128, 64, SCALE)
+    assert np.array_equal(sel, sel_r)
+    assert np.array_equal(out, out_r)
