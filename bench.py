@@ -198,6 +198,36 @@ def run_gpu(args, wl):
                                      ws=ws)
 
     steps = {"bf16": step_bf16, "mxfp4": step_mxfp4}
+    if not wl.pool:
+        # The pages' hierarchical decoder group on the same caches: the first
+        # Full layer also emitting the max-of-fine-scores pool (2,048 blocks
+        # of 8), and a Reindex layer scoring only that pool with its own
+        # indexer query.
+        from fp4_kv_cache_amd import inputs
+        group_pool = (2048, 8)
+        pool_ids = torch.empty((wl.B, group_pool[0] * group_pool[1]),
+                               dtype=torch.int32, device=dev)
+        ws_fp = csa2.workspace(csa2.load().csa2_workspace_size(
+            csa2.OP_FULL_POOL, wl.B, wl.n, k,
+            csa2.ctypes.byref(csa2.PoolOpts(*group_pool))), dev)
+        ws_ri = csa2.workspace(csa2.load().csa2_workspace_size(
+            csa2.OP_REINDEX, wl.B, pool_ids.shape[1], k, None), dev)
+        qi1, w1 = (torch.stack(t).contiguous() for t in zip(*[
+            inputs.index_query(wl, b, dev, layer=1) for b in range(wl.B)]))
+
+        def step_full_pool(i):
+            csa2.full_pool_decode(reps[i % R], st.q_idx, st.w, st.q[0],
+                                  st.swa[0], st.n_swa, k, st.scale,
+                                  pool=group_pool, out=out, topk_out=ids,
+                                  pool_out=pool_ids, ws=ws_fp)
+
+        def step_reindex(i):
+            csa2.reindex_decode(reps[i % R], pool_ids, qi1, w1, st.q[0],
+                                st.swa[0], st.n_swa, k, st.scale, out=out,
+                                topk_out=ids, ws=ws_ri)
+
+        steps["full_pool"] = step_full_pool
+        steps["reindex"] = step_reindex
     timing = {q: time_steps(fn, args, R, out, ids) for q, fn in steps.items()}
 
     # -- per-kernel durations with HIP events on the launch stream: the same
@@ -432,6 +462,16 @@ def main():
             "value": wl.B / alt["step_s"], "ms_per_step": alt["step_s"] * 1e3,
             "roofline": alt["roofline"]}},
     }
+    if "full_pool" in g["timing"]:
+        fp, ri = (g["timing"][x] for x in ("full_pool", "reindex"))
+        fp_s = fp[1] if fp[1] is not None else fp[0]
+        ri_s = ri[1] if ri[1] is not None else ri[0]
+        line["variants"]["decoder_group_pool"] = {
+            "pool": [2048, 8],
+            "full_pool_layer": {"value": wl.B / fp_s, "ms_per_step": fp_s * 1e3},
+            "reindex_layer": {"value": wl.B / ri_s, "ms_per_step": ri_s * 1e3,
+                              "scored_entries_per_seq": 2048 * 8},
+            "unit": "query-tokens/s"}
     if not args.no_cpu:
         cpu = run_cpu(wl, args.cpu_seconds)
         line["cpu_baseline"] = cpu

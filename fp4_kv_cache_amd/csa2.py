@@ -15,13 +15,13 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 FMT_MAIN, FMT_IDX, FMT_SWA = 0, 1, 2
 KEYS_MXFP4, KEYS_BF16 = 0, 1
-OP_TOPK, OP_DECODE, OP_REUSE = 0, 1, 2
+OP_TOPK, OP_DECODE, OP_REUSE, OP_FULL_POOL, OP_REINDEX = 0, 1, 2, 3, 4
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGNMENT",
           4: "WORKSPACE", 5: "HIP"}
 EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
            "csa2_indexer_score", "csa2_indexer_score_fp4q", "csa2_topk",
            "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_fp4q",
-           "csa2_reuse_attn", "csa2_workspace_size", "csa2_entry_bytes",
+           "csa2_full_pool_decode", "csa2_reindex_decode", "csa2_reuse_attn", "csa2_workspace_size", "csa2_entry_bytes",
            "csa2_kv_bytes_per_token", "csa2_last_error", "csa2_version"]
 
 
@@ -78,6 +78,13 @@ def load(path=None):
                                                P, P, P, P, P, I32, I32, F32,
                                                ctypes.POINTER(PoolOpts), P, P,
                                                P, SZ, P]),
+        "csa2_full_pool_decode": (I32, [ctypes.POINTER(CacheDesc), P, P, P,
+                                        P, P, I32, I32, F32,
+                                        ctypes.POINTER(PoolOpts), P, P, P, P,
+                                        SZ, P]),
+        "csa2_reindex_decode": (I32, [ctypes.POINTER(CacheDesc), P, I64, P,
+                                      P, P, P, P, I32, I32, F32, P, P, P, SZ,
+                                      P]),
         "csa2_reuse_attn": (I32, [P, P, I64, P, I32, P, P, P, I32, F32, P, P,
                                   SZ, P]),
         "csa2_workspace_size": (SZ, [I32, I32, I64, I32,
@@ -295,6 +302,52 @@ def sparse_attn_decode_fp4q(cache, q_codes, q_scales, w, q, swa, n_swa, k,
         _ptr(swa), _ptr(n_swa), B, k, float(scale),
         ctypes.byref(po) if po else None, _ptr(out), _ptr(topk_out), _ptr(ws),
         ws.numel(), _stream()))
+    return out, topk_out
+
+
+def full_pool_decode(cache, q_idx, w, q, swa, n_swa, k, scale,
+                     pool=(2048, 8), out=None, topk_out=None, pool_out=None,
+                     ws=None):
+    """First Full layer of a hierarchical decoder group: returns (out bf16
+    [B,64,512], topk [B,k], pool [B, n_blocks_keep*8])."""
+    B = q.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
+    if topk_out is None:
+        topk_out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if pool_out is None:
+        pool_out = torch.empty((B, pool[0] * pool[1]), dtype=torch.int32,
+                               device=dev)
+    po = PoolOpts(*pool)
+    if ws is None:
+        need = load().csa2_workspace_size(OP_FULL_POOL, B, cache.n_cap, k,
+                                          ctypes.byref(po))
+        ws = workspace(need, dev)
+    _check(load().csa2_full_pool_decode(
+        ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
+        _ptr(n_swa), B, k, float(scale), ctypes.byref(po), _ptr(out),
+        _ptr(topk_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream()))
+    return out, topk_out, pool_out
+
+
+def reindex_decode(cache, pool_ids, q_idx, w, q, swa, n_swa, k, scale,
+                   out=None, topk_out=None, ws=None):
+    """Reindex layer over a pool [B, n_pool]: returns (out, topk)."""
+    B, n_pool = pool_ids.shape
+    dev = q.device
+    _need(pool_ids, torch.int32, name="pool_ids")
+    if out is None:
+        out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
+    if topk_out is None:
+        topk_out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if ws is None:
+        need = load().csa2_workspace_size(OP_REINDEX, B, n_pool, k, None)
+        ws = workspace(need, dev)
+    _check(load().csa2_reindex_decode(
+        ctypes.byref(cache), _ptr(pool_ids), n_pool, _ptr(q_idx), _ptr(w),
+        _ptr(q), _ptr(swa), _ptr(n_swa), B, k, float(scale), _ptr(out),
+        _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
     return out, topk_out
 
 

@@ -101,6 +101,50 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
   return L;
 }
 
+// Workspace of csa2_full_pool_decode: keys, tile maxima, block maxima and
+// their 32-block maxima, attention partials.
+struct FullPoolLayout {
+  int64_t nb = 0;
+  size_t off_scores = 0, off_tmax = 0, off_bmax = 0, off_btmax = 0,
+         off_attn = 0, total = 0;
+};
+FullPoolLayout full_pool_layout(int B, int64_t n_cap, int k) {
+  FullPoolLayout L;
+  L.nb = (n_cap + 7) / 8;
+  size_t off = 0;
+  L.off_scores = off;
+  off += align256((size_t)B * round32(n_cap) * 4);
+  L.off_tmax = off;
+  off += align256((size_t)B * tiles_of(n_cap) * 4);
+  L.off_bmax = off;
+  off += align256((size_t)B * round32(L.nb) * 4);
+  L.off_btmax = off;
+  off += align256((size_t)B * tiles_of(L.nb) * 4);
+  L.off_attn = off;
+  off += align256(csa2::attn_workspace(B, k));
+  L.total = off;
+  return L;
+}
+
+// Workspace of csa2_reindex_decode: pool keys, their tile maxima, attention.
+struct ReindexLayout {
+  size_t off_scores = 0, off_tmax = 0, off_attn = 0, total = 0;
+};
+ReindexLayout reindex_layout(int B, int64_t n_pool, int k) {
+  ReindexLayout L;
+  size_t off = 0;
+  L.off_scores = off;
+  off += align256((size_t)B * round32(n_pool) * 4);
+  L.off_tmax = off;
+  off += align256((size_t)B * tiles_of(n_pool) * 4);
+  L.off_attn = off;
+  off += align256(csa2::attn_workspace(B, k));
+  L.total = off;
+  return L;
+}
+
+constexpr int64_t kMaxPool = int64_t(1) << 26;
+
 csa2_status check_pool(const csa2_pool_opts* pool) {
   if (!pool) return CSA2_OK;
   if (pool->n_blocks_keep < 1 || pool->block < 1 || pool->block > kMaxBlock)
@@ -184,6 +228,14 @@ size_t csa2_workspace_size(int32_t op, int32_t B, int64_t n_cap, int32_t k,
       return decode_layout(B, n_cap, k, pool).total;
     case CSA2_OP_REUSE:
       return csa2::attn_workspace(B, k);
+    case CSA2_OP_FULL_POOL:
+      if (!pool || pool->block != 8 || pool->n_blocks_keep < 1 ||
+          pool->n_blocks_keep > kMaxK)
+        return 0;
+      return full_pool_layout(B, n_cap, k).total;
+    case CSA2_OP_REINDEX:
+      if (n_cap < 1 || n_cap > kMaxPool) return 0;
+      return reindex_layout(B, n_cap, k).total;
     default:
       return 0;
   }
@@ -493,3 +545,113 @@ csa2_status csa2_sparse_attn_decode_fp4q(
 }
 
 }  // extern "C"
+
+csa2_status csa2_full_pool_decode(const csa2_cache* kv, const uint16_t* q_idx,
+                                  const float* w, const uint16_t* q,
+                                  const uint8_t* swa, const int32_t* n_swa,
+                                  int32_t B, int32_t k, float scale,
+                                  const csa2_pool_opts* pool, uint16_t* out,
+                                  int32_t* topk_out, int32_t* pool_out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (!kv) return fail(CSA2_ERR_INVALID_ARG, "null cache descriptor");
+  csa2_status st = check_attn_common(kv->main_codes, kv->main_scales,
+                                     kv->n_cap, q, swa, n_swa, B, k, scale, out);
+  if (st) return st;
+  if (!pool) return fail(CSA2_ERR_INVALID_ARG, "null pool options");
+  if (pool->block != 8 || pool->n_blocks_keep < 1 ||
+      pool->n_blocks_keep > kMaxK)
+    return fail(CSA2_ERR_UNSUPPORTED, "the pool needs block == 8 and "
+                "n_blocks_keep in 1..%d", kMaxK);
+  if (B == 0) return CSA2_OK;
+  if (kv->n_cap < 1) return fail(CSA2_ERR_INVALID_ARG, "n_cap must be >= 1");
+  if (!kv->idx_codes || !kv->idx_scales || !kv->n_entries || !topk_out ||
+      !pool_out)
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  st = check_query(csa2::IndexQuery{q_idx, nullptr, w});
+  if (st) return st;
+  if (!aligned(kv->idx_codes, 16) || !aligned(kv->idx_scales, 4) ||
+      !aligned(topk_out, 4) || !aligned(pool_out, 4))
+    return fail(CSA2_ERR_ALIGNMENT, "misaligned indexer argument");
+  const int64_t n_pool = (int64_t)pool->n_blocks_keep * 8;
+  if (overlap(pool_out, (size_t)B * n_pool * 4, topk_out, (size_t)B * k * 4))
+    return fail(CSA2_ERR_INVALID_ARG, "pool_out overlaps topk_out");
+  const FullPoolLayout L = full_pool_layout(B, kv->n_cap, k);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(CSA2_ERR_WORKSPACE, "full-pool decode needs %zu bytes of "
+                "256-byte aligned workspace (got %zu)", L.total, ws_bytes);
+  st = need_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* scores = reinterpret_cast<float*>(base + L.off_scores);
+  uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
+  uint32_t* bmax = reinterpret_cast<uint32_t*>(base + L.off_bmax);
+  uint32_t* btmax = reinterpret_cast<uint32_t*>(base + L.off_btmax);
+  hipError_t e = csa2::launch_indexer(
+      CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales, kv->n_cap,
+      kv->n_entries, nullptr, kv->n_cap, csa2::IndexQuery{q_idx, nullptr, w},
+      B, scores, s, tmax, bmax, btmax);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  // The layer's own top-k, and beside it (same launch) the pool: the
+  // n_blocks_keep blocks with the largest maximum, expanded to their
+  // positions below n_entries (blocks past the end hold key 0 and are never
+  // chosen).
+  const csa2::KeyRows own{scores, tmax, round32(kv->n_cap), kv->n_cap,
+                          kv->n_entries, k, 1, nullptr, topk_out};
+  const csa2::KeyRows blocks{bmax, btmax, round32(L.nb), L.nb, nullptr,
+                             pool->n_blocks_keep, 8, kv->n_entries, pool_out};
+  e = csa2::launch_row_select_pair(own, blocks, B, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k and pool launch");
+  e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
+                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return CSA2_OK;
+}
+
+csa2_status csa2_reindex_decode(const csa2_cache* kv, const int32_t* pool,
+                                int64_t n_pool, const uint16_t* q_idx,
+                                const float* w, const uint16_t* q,
+                                const uint8_t* swa, const int32_t* n_swa,
+                                int32_t B, int32_t k, float scale,
+                                uint16_t* out, int32_t* topk_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!kv) return fail(CSA2_ERR_INVALID_ARG, "null cache descriptor");
+  csa2_status st = check_attn_common(kv->main_codes, kv->main_scales,
+                                     kv->n_cap, q, swa, n_swa, B, k, scale, out);
+  if (st) return st;
+  if (n_pool < 1 || n_pool > kMaxPool)
+    return fail(CSA2_ERR_INVALID_ARG, "n_pool must be in 1..2^26");
+  if (B == 0) return CSA2_OK;
+  if (!kv->idx_codes || !kv->idx_scales || !kv->n_entries || !pool ||
+      !topk_out)
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  st = check_query(csa2::IndexQuery{q_idx, nullptr, w});
+  if (st) return st;
+  if (!aligned(kv->idx_codes, 16) || !aligned(kv->idx_scales, 4) ||
+      !aligned(pool, 4) || !aligned(topk_out, 4))
+    return fail(CSA2_ERR_ALIGNMENT, "misaligned indexer argument");
+  if (overlap(topk_out, (size_t)B * k * 4, pool, (size_t)B * n_pool * 4))
+    return fail(CSA2_ERR_INVALID_ARG, "topk_out overlaps pool");
+  const ReindexLayout L = reindex_layout(B, n_pool, k);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(CSA2_ERR_WORKSPACE, "reindex decode needs %zu bytes of "
+                "256-byte aligned workspace (got %zu)", L.total, ws_bytes);
+  st = need_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* scores = reinterpret_cast<float*>(base + L.off_scores);
+  uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
+  hipError_t e = csa2::launch_indexer(
+      CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales, kv->n_cap,
+      kv->n_entries, pool, n_pool, csa2::IndexQuery{q_idx, nullptr, w}, B,
+      scores, s, tmax);
+  if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
+  e = csa2::launch_row_select(scores, tmax, true, round32(n_pool), n_pool,
+                              nullptr, pool, B, k, 1, nullptr, topk_out, s);
+  if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
+  e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
+                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return CSA2_OK;
+}

@@ -138,7 +138,10 @@ template <bool SCALED> struct Depth<1, SCALED> {
 };
 
 // KEYS: write selection keys (see score_key) instead of float scores, and
-// each 32-row tile's largest key to tmax[B][ceil(n_rows/32)].
+// each 32-row tile's largest key to tmax[B][ceil(n_rows/32)]; with `bmax`
+// also each 8-row block's largest key to bmax[B][round32(nb)] (nb =
+// ceil(n_rows/8)) and each 256-row group's (a wavefront's rows) to
+// btmax[B][ceil(nb/32)].
 // QFP4: the query is MXFP4 planes (codes q[B][32][64], scales
 // q_scales[B][32][4]) instead of bf16 q[B][32][128].
 template <int KEYFMT, bool KEYS, bool QFP4>
@@ -148,7 +151,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const int32_t* __restrict__ cand, int64_t n_rows,
     const void* __restrict__ q_in, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ w, float* __restrict__ scores,
-    uint32_t* __restrict__ tmax) {
+    uint32_t* __restrict__ tmax, uint32_t* __restrict__ bmax,
+    uint32_t* __restrict__ btmax) {
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int D = Depth<KEYFMT, kScaledOp>::value;
   constexpr int T = kTilesPerWave;
@@ -284,6 +288,9 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     }
   }
   // Stores after the loop keep the loads' wait counts static.
+  static_assert(kTilesPerWave * 32 == 256, "a wavefront's rows are one "
+                "32-block group of the block maxima");
+  uint32_t wmax = 0u;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (t >= nt) break;
@@ -297,12 +304,31 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       const int64_t ld32 = (n_rows + 31) & ~(int64_t)31;
       if (half == 0 && i < n_rows)
         reinterpret_cast<uint32_t*>(scores)[(int64_t)b * ld32 + i] = key;
-      const uint32_t mx = wave_max_u32(key);
+      // The tile maximum by the DPP max network (as wave_max_u32); after
+      // its first three steps lane 8j+7 holds the largest key of entries
+      // 8j .. 8j+7: the block maximum of the hierarchical pool.
+      uint32_t m = dpp_max<0x111, 0xf>(key);
+      m = dpp_max<0x112, 0xf>(m);
+      m = dpp_max<0x114, 0xf>(m);
+      if (bmax != nullptr && half == 0 && (col & 7) == 7) {
+        const int64_t nbs = (n_rows + 7) >> 3;
+        const int64_t blk = i >> 3;
+        if (blk < nbs) bmax[(int64_t)b * ((nbs + 31) & ~(int64_t)31) + blk] = m;
+      }
+      m = dpp_max<0x118, 0xf>(m);
+      m = dpp_max<0x142, 0xa>(m);
+      m = dpp_max<0x143, 0xc>(m);
+      const uint32_t mx = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
       if (lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
+      wmax = max(wmax, mx);
     } else {
       if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
     }
+  }
+  if (KEYS && btmax != nullptr && lane == 0) {
+    const int64_t nbt = (((n_rows + 7) >> 3) + 31) >> 5;
+    btmax[(int64_t)b * nbt + (base >> 8)] = wmax;
   }
 }
 
@@ -313,22 +339,26 @@ template <int KEYFMT, bool KEYS, bool QFP4>
 void launch_one(dim3 grid, hipStream_t s, const void* k_codes,
                 const uint8_t* k_scales, int64_t n_cap,
                 const int32_t* n_entries, const int32_t* cand, int64_t n_rows,
-                const IndexQuery& iq, float* scores, uint32_t* tmax) {
+                const IndexQuery& iq, float* scores, uint32_t* tmax,
+                uint32_t* bmax, uint32_t* btmax) {
   hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256), 0,
                      s, k_codes, k_scales, n_cap, n_entries, cand, n_rows,
-                     iq.q, iq.q_scales, iq.w, scores, tmax);
+                     iq.q, iq.q_scales, iq.w, scores, tmax, bmax, btmax);
 }
 template <int KEYFMT, bool KEYS>
 void launch_q(dim3 grid, hipStream_t s, const void* k_codes,
               const uint8_t* k_scales, int64_t n_cap, const int32_t* n_entries,
               const int32_t* cand, int64_t n_rows, const IndexQuery& iq,
-              float* scores, uint32_t* tmax) {
+              float* scores, uint32_t* tmax, uint32_t* bmax,
+              uint32_t* btmax) {
   if (iq.q_scales)
     launch_one<KEYFMT, KEYS, true>(grid, s, k_codes, k_scales, n_cap,
-                                   n_entries, cand, n_rows, iq, scores, tmax);
+                                   n_entries, cand, n_rows, iq, scores, tmax,
+                                   bmax, btmax);
   else
     launch_one<KEYFMT, KEYS, false>(grid, s, k_codes, k_scales, n_cap,
-                                    n_entries, cand, n_rows, iq, scores, tmax);
+                                    n_entries, cand, n_rows, iq, scores, tmax,
+                                    bmax, btmax);
 }
 }  // namespace
 
@@ -336,22 +366,24 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,
                           const int32_t* n_entries, const int32_t* cand,
                           int64_t n_rows, const IndexQuery& iq, int B,
-                          float* scores, hipStream_t s, uint32_t* tmax) {
+                          float* scores, hipStream_t s, uint32_t* tmax,
+                          uint32_t* bmax, uint32_t* btmax) {
   if (n_rows == 0 || B == 0) return hipSuccess;
+  if (bmax && (!tmax || cand || !btmax)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((n_rows + kEntriesPerBlock - 1) / kEntriesPerBlock),
                   (unsigned)B);
   if (keyfmt == 0 && tmax)
     launch_q<0, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                      n_rows, iq, scores, tmax);
+                      n_rows, iq, scores, tmax, bmax, btmax);
   else if (keyfmt == 0)
     launch_q<0, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                       n_rows, iq, scores, tmax);
+                       n_rows, iq, scores, tmax, bmax, btmax);
   else if (tmax)
     launch_q<1, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                      n_rows, iq, scores, tmax);
+                      n_rows, iq, scores, tmax, bmax, btmax);
   else
     launch_q<1, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                       n_rows, iq, scores, tmax);
+                       n_rows, iq, scores, tmax, bmax, btmax);
   return hipGetLastError();
 }
 

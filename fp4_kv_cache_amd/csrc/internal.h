@@ -27,7 +27,9 @@ hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
 // scores[B][n_rows].  With `tmax` (the decode path) it writes selection keys
 // (score_key, as uint32) instead, rows padded to a multiple of 32 entries
 // (scores[B][round_up(n_rows, 32)]), and each 32-row tile's largest key into
-// tmax[B][ceil(n_rows/32)].
+// tmax[B][ceil(n_rows/32)].  With `bmax` (and `btmax`; all rows, no
+// candidates) also the 8-row block maxima bmax[B][round_up(nb, 32)], nb =
+// ceil(n_rows/8), and their 32-block maxima btmax[B][ceil(nb/32)].
 // The indexer query of every sequence: bf16 q[B][32][128] (q_scales null),
 // or MXFP4 planes q[B][32][64] codes + q_scales[B][32][4]; weights w[B][32].
 struct IndexQuery {
@@ -40,7 +42,8 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const int32_t* n_entries, const int32_t* cand,
                           int64_t n_rows, const IndexQuery& iq, int B,
                           float* scores, hipStream_t s,
-                          uint32_t* tmax = nullptr);
+                          uint32_t* tmax = nullptr, uint32_t* bmax = nullptr,
+                          uint32_t* btmax = nullptr);
 
 // topk.hip
 // Exact per-row top-k (see topk.hip) of float scores (keys == false) or of
@@ -52,6 +55,20 @@ hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
                              const int32_t* ids, int B, int k, int block,
                              const int32_t* limit, int32_t* out,
                              hipStream_t s);
+
+// Two key selections (no ids) over the same B rows in one launch, side by
+// side: rows of r0 on workgroups 0..B-1, rows of r1 on B..2B-1.
+struct KeyRows {
+  const void* keys;         // [B][ld] selection keys, ld a multiple of 32
+  const void* tmax;         // [B][ceil(n_cols/32)] or null
+  int64_t ld, n_cols;
+  const int32_t* n_valid;   // nullable
+  int k, block;
+  const int32_t* limit;     // nullable
+  int32_t* out;             // [B][k * block]
+};
+hipError_t launch_row_select_pair(const KeyRows& r0, const KeyRows& r1, int B,
+                                  hipStream_t s);
 // Standalone top-k over a score array (computes tile maxima in `ws`).
 size_t topk_workspace(int B, int64_t ld);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,

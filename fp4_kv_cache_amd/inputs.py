@@ -92,10 +92,12 @@ def _rows(wl, tensor, dim, b, lo, hi, device):
     return torch.cat(parts) if len(parts) > 1 else parts[0]
 
 
-def index_query(wl, b, device="cpu"):
-    """(q_idx bf16 [32, 128], w float32 [32]) of sequence b."""
-    q = _normal((H_IDX, D_IDX), seed(wl.cid, T_QIDX, b), device)
-    w = torch.rand((H_IDX,), generator=_gen(device, seed(wl.cid, T_W, b)),
+def index_query(wl, b, device="cpu", layer=0):
+    """(q_idx bf16 [32, 128], w float32 [32]) of sequence b in a layer (a
+    Reindex layer has its own indexer query)."""
+    q = _normal((H_IDX, D_IDX), seed(wl.cid, T_QIDX, b, layer=layer), device)
+    w = torch.rand((H_IDX,), generator=_gen(device, seed(wl.cid, T_W, b,
+                                                         layer=layer)),
                    device=device, dtype=torch.float32)
     return q.to(torch.bfloat16), w
 

@@ -85,7 +85,9 @@ enum {
 enum {
   CSA2_OP_TOPK = 0,
   CSA2_OP_DECODE = 1, /* csa2_sparse_attn_decode                          */
-  CSA2_OP_REUSE = 2   /* csa2_reuse_attn                                  */
+  CSA2_OP_REUSE = 2,  /* csa2_reuse_attn                                  */
+  CSA2_OP_FULL_POOL = 3, /* csa2_full_pool_decode (needs the pool options)  */
+  CSA2_OP_REINDEX = 4    /* csa2_reindex_decode (n_cap argument = n_pool)  */
 };
 
 /* The caches one Full layer owns (or a Reindex layer shares). */
@@ -230,6 +232,46 @@ csa2_status csa2_sparse_attn_decode_fp4q(
     const int32_t *n_swa, int32_t B, int32_t k, float scale,
     const csa2_pool_opts *pool, uint16_t *out, int32_t *topk_out, void *ws,
     size_t ws_bytes, void *stream);
+
+/* csa2_full_pool_decode -- the first Full layer of a hierarchical decoder
+ * group as the pages define it ([KVC] 4.3 equation; [ARCH] 2.3.2 and
+ * Figure 5): exactly csa2_sparse_attn_decode without a pool (scores over
+ * all n_entries[b] visible entries, its own top-k, attention), and besides
+ * it the candidate pool of the Reindex layers after it -- block j (positions
+ * 8j .. 8j+7) scores the largest of its fine scores, the n_blocks_keep
+ * best blocks (equal maxima: the lower block first) are taken and expanded
+ * to their positions below n_entries[b].
+ *   pool      n_blocks_keep in 1..2048, block == 8 (CSA2_ERR_UNSUPPORTED
+ *             otherwise); kv->block_keys is not used
+ *   pool_out  [B][n_blocks_keep * 8] positions, ascending, -1 padded
+ *   other arguments and outputs as in csa2_sparse_attn_decode.
+ *   ws / ws_bytes: csa2_workspace_size(CSA2_OP_FULL_POOL, B, n_cap, k,
+ *             pool) bytes, 256-byte aligned. */
+csa2_status csa2_full_pool_decode(const csa2_cache *kv, const uint16_t *q_idx,
+                                  const float *w, const uint16_t *q,
+                                  const uint8_t *swa, const int32_t *n_swa,
+                                  int32_t B, int32_t k, float scale,
+                                  const csa2_pool_opts *pool, uint16_t *out,
+                                  int32_t *topk_out, int32_t *pool_out,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* csa2_reindex_decode -- a Reindex-mode layer ([KVC] 4.2 table, 4.3
+ * equation; [ARCH] 2.3.1): the layer's own indexer query (q_idx, w) scores
+ * only the pool positions on the shared indexer keys, its top-k among them
+ * is taken (ids ascending, -1 padded), then attention over those main
+ * entries plus the layer's own window, as in csa2_sparse_attn_decode.
+ *   pool      [B][n_pool] positions (from csa2_full_pool_decode); entries
+ *             < 0 or >= n_entries[b] are skipped; valid entries ascending
+ *   n_pool    1..2^26
+ *   ws / ws_bytes: csa2_workspace_size(CSA2_OP_REINDEX, B, n_pool, k,
+ *             NULL) bytes, 256-byte aligned. */
+csa2_status csa2_reindex_decode(const csa2_cache *kv, const int32_t *pool,
+                                int64_t n_pool, const uint16_t *q_idx,
+                                const float *w, const uint16_t *q,
+                                const uint8_t *swa, const int32_t *n_swa,
+                                int32_t B, int32_t k, float scale,
+                                uint16_t *out, int32_t *topk_out, void *ws,
+                                size_t ws_bytes, void *stream);
 
 /* csa2_reuse_attn -- a Reuse-mode layer ([ARCH] 2.3.1; [KVC] 4.2 table):
  * no indexer; attention over the given top-k ids (entries < 0 skipped) of
