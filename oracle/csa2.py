@@ -233,6 +233,43 @@ def mqa_decode(q_bits, keys, scale):
     return p @ keys
 
 
+def mqa_decode_sink(q_bits, keys, scale, sink):
+    """mqa_decode with a per-head attention sink, [V4] "other details",
+    attention-sink equation: a learnable logit z'_h joins only the softmax
+    denominator, a_s = exp(l_s) / (sum_s' exp(l_s') + exp(z'_h)), so a head's
+    weights may sum to less than 1.  sink: [64] (logit units, like
+    q.k * scale).  float64 throughout."""
+    q = F.bf16_bits_to_f64(q_bits)
+    z = np.asarray(sink, dtype=np.float32).astype(np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros((q.shape[0], keys.shape[1]))
+    logits = (q @ keys.T) * float(scale)                     # [64, m]
+    ref = np.maximum(logits.max(axis=1), z)
+    p = np.exp(logits - ref[:, None])
+    den = p.sum(axis=1) + np.exp(z - ref)
+    return (p / den[:, None]) @ keys
+
+
+def rope_derotate(o, t, theta=10000.0, r=64):
+    """The output de-rotation of partial RoPE, [V4] "other details" (partial
+    RoPE paragraph and the R_{-t} o_t equation): RoPE applies to the last
+    r = 64 dims only, and the output is rotated once by position -t so the
+    absolute rotation R_s carried by each value becomes R_{s-t}.  Reading
+    (the page does not spell the rotation out): standard RoPE on the
+    interleaved pairs (d0 + 2i, d0 + 2i + 1), d0 = 512 - r, with frequency
+    theta ** (-2i / r); position p maps (x, y) to
+    (x cos p w - y sin p w, x sin p w + y cos p w).  o: [H, 512]."""
+    o = np.array(o, dtype=np.float64)
+    d0 = o.shape[1] - r
+    i = np.arange(r // 2)
+    ang = -float(t) * float(theta) ** (-2.0 * i / r)
+    c, s = np.cos(ang), np.sin(ang)
+    x, y = o[:, d0::2].copy(), o[:, d0 + 1::2].copy()
+    o[:, d0::2] = x * c - y * s
+    o[:, d0 + 1::2] = x * s + y * c
+    return o
+
+
 def gather_keys(main_codes, main_scales, idx, swa_codes, n_swa):
     """Keys of one query: the selected main entries (ids >= 0, in the given
     order) followed by the first n_swa sliding-window rows, concatenated
@@ -314,3 +351,14 @@ def reindex_layer(main_codes, main_scales, idx_codes, idx_scales, pool,
     sel = topk(fine, k, ids=valid)
     kv = gather_keys(main_codes, main_scales, sel, swa_codes, n_swa)
     return sel, mqa_decode(q_bits, kv, scale), fine
+
+
+def reuse_layer_ext(main_codes, main_scales, sel, q_bits, swa_codes, n_swa,
+                    scale, sink=None, pos=None, theta=10000.0):
+    """Reuse-mode attention with the [V4] epilogue details: the per-head
+    sink (mqa_decode_sink) and/or the partial-RoPE output de-rotation at the
+    query position `pos` (rope_derotate)."""
+    kv = gather_keys(main_codes, main_scales, sel, swa_codes, n_swa)
+    o = (mqa_decode(q_bits, kv, scale) if sink is None
+         else mqa_decode_sink(q_bits, kv, scale, sink))
+    return o if pos is None else rope_derotate(o, pos, theta)

@@ -355,3 +355,69 @@ def test_reindex_with_full_query_keeps_full_topk():
                                       128, 64, SCALE)
     assert np.array_equal(sel, sel_r)
     assert np.array_equal(out, out_r)
+
+
+# ------------------------------------------- attention epilogue details --
+def test_sink_limits_and_closed_form():
+    c = _case(40, 31)
+    keys = O.gather_keys(c["mc"], c["ms"], np.arange(40), c["sw"], 128)
+    plain = O.mqa_decode(c["q"], keys, SCALE)
+    # a sink at -inf changes nothing; a huge sink sends every weight to 0
+    assert np.allclose(O.mqa_decode_sink(c["q"], keys, SCALE,
+                                         np.full(64, -np.inf)), plain,
+                       rtol=1e-13, atol=1e-13)
+    assert np.abs(O.mqa_decode_sink(c["q"], keys, SCALE,
+                                    np.full(64, 800.0))).max() < 1e-300
+    # one key: a = e^l / (e^l + e^z), o = a k, for every head
+    k1 = keys[:1]
+    z = np.linspace(-3, 3, 64).astype(np.float32)
+    q = F.bf16_bits_to_f64(c["q"])
+    got = O.mqa_decode_sink(c["q"], k1, SCALE, z)
+    for h in range(64):
+        l = float(q[h] @ k1[0]) * SCALE
+        a = math.exp(l) / (math.exp(l) + math.exp(float(z[h])))
+        assert np.allclose(got[h], a * k1[0], rtol=1e-12, atol=1e-12)
+    # no keys: the output is zero
+    assert np.array_equal(O.mqa_decode_sink(c["q"], keys[:0], SCALE, z),
+                          np.zeros((64, 512)))
+
+
+def test_rope_derotate_hand_and_group_law():
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((3, 512))
+    assert np.array_equal(O.rope_derotate(o, 0), o)          # t = 0
+    got = O.rope_derotate(o, 5, theta=10000.0)
+    assert np.array_equal(got[:, :448], o[:, :448])           # first 448 dims
+    # pair 0 has frequency 1: rotation by -5 rad, by hand
+    c, s = math.cos(-5.0), math.sin(-5.0)
+    assert np.allclose(got[:, 448], o[:, 448] * c - o[:, 449] * s)
+    assert np.allclose(got[:, 449], o[:, 448] * s + o[:, 449] * c)
+    # pair i has frequency 10000^(-2i/64): pair 31 by hand
+    w = 10000.0 ** (-62.0 / 64)
+    c, s = math.cos(-5 * w), math.sin(-5 * w)
+    assert np.allclose(got[:, 510], o[:, 510] * c - o[:, 511] * s)
+    # pair norms are kept; R_{-t} R_{-u} = R_{-(t+u)} (with R_p = rotation by +p)
+    n0 = o[:, 448::2] ** 2 + o[:, 449::2] ** 2
+    n1 = got[:, 448::2] ** 2 + got[:, 449::2] ** 2
+    assert np.allclose(n0, n1)
+    assert np.allclose(O.rope_derotate(O.rope_derotate(o, 7), 11),
+                       O.rope_derotate(o, 18), rtol=1e-12, atol=1e-12)
+
+
+def test_derotated_output_is_relative():
+    """The page's identity: with values stored rotated to their own position
+    s (R_s e_s), R_{-t} o_t = sum_s a_s R_{s-t} e_s -- shifting every
+    position by the same amount leaves the de-rotated output unchanged."""
+    rng = np.random.default_rng(33)
+    e = rng.standard_normal((6, 512))
+    a = rng.dirichlet(np.ones(6))
+    pos = np.array([3, 10, 11, 40, 41, 90])
+
+    def rot(x, p):                      # R_p = de-rotation by -p
+        return O.rope_derotate(x, -p)
+    for shift in (0, 1000, 123457):
+        o = sum(a[i] * rot(e[i:i + 1], pos[i] + shift) for i in range(6))
+        d = O.rope_derotate(o, 95 + shift)
+        if shift == 0:
+            base = d
+        assert np.allclose(d, base, rtol=1e-9, atol=1e-9)
