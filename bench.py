@@ -197,7 +197,19 @@ def run_gpu(args, wl):
                                      pool=wl.pool, out=out, topk_out=ids,
                                      ws=ws)
 
-    steps = {"bf16": step_bf16, "mxfp4": step_mxfp4}
+    # The V4 attention details on the same step: per-head sink logits and
+    # the partial-RoPE output de-rotation at each sequence's position.
+    g_sink = torch.linspace(-2.0, 2.0, 64, device=dev)
+    g_pos = torch.full((wl.B,), wl.ctx - 1, dtype=torch.int32, device=dev)
+
+    def step_epilogue(i):
+        csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
+                                st.swa[0], st.n_swa, k, st.scale,
+                                pool=wl.pool, out=out, topk_out=ids, ws=ws,
+                                sink=g_sink, pos=g_pos)
+
+    steps = {"bf16": step_bf16, "mxfp4": step_mxfp4,
+             "sink_rope": step_epilogue}
     if not wl.pool:
         # The pages' hierarchical decoder group on the same caches: the first
         # Full layer also emitting the max-of-fine-scores pool (2,048 blocks
@@ -462,6 +474,12 @@ def main():
             "value": wl.B / alt["step_s"], "ms_per_step": alt["step_s"] * 1e3,
             "roofline": alt["roofline"]}},
     }
+    ep = g["timing"]["sink_rope"]
+    ep_s = ep[1] if ep[1] is not None else ep[0]
+    line["variants"]["attn_sink_rope"] = {
+        "value": wl.B / ep_s, "ms_per_step": ep_s * 1e3,
+        "what": "the headline step with per-head sink logits and the "
+                "partial-RoPE output de-rotation (csa2_sparse_attn_decode_ex)"}
     if "full_pool" in g["timing"]:
         fp, ri = (g["timing"][x] for x in ("full_pool", "reindex"))
         fp_s = fp[1] if fp[1] is not None else fp[0]

@@ -21,7 +21,8 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGNMENT",
 EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
            "csa2_indexer_score", "csa2_indexer_score_fp4q", "csa2_topk",
            "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_fp4q",
-           "csa2_full_pool_decode", "csa2_reindex_decode", "csa2_reuse_attn", "csa2_workspace_size", "csa2_entry_bytes",
+           "csa2_full_pool_decode", "csa2_reindex_decode", "csa2_reuse_attn",
+           "csa2_sparse_attn_decode_ex", "csa2_reuse_attn_ex", "csa2_workspace_size", "csa2_entry_bytes",
            "csa2_kv_bytes_per_token", "csa2_last_error", "csa2_version"]
 
 
@@ -43,6 +44,24 @@ class CacheDesc(ctypes.Structure):
 
 class PoolOpts(ctypes.Structure):
     _fields_ = [("n_blocks_keep", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+class AttnOpts(ctypes.Structure):
+    _fields_ = [("sink", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("rope_theta", ctypes.c_float)]
+
+
+def _attn_opts(sink, pos, rope_theta):
+    """csa2_attn_opts for the optional sink [64] float32 / positions [B]
+    int32, or None when neither is given."""
+    if sink is None and pos is None:
+        return None
+    if sink is not None:
+        _need(sink, torch.float32, (64,), "sink")
+    if pos is not None:
+        _need(pos, torch.int32, name="pos")
+    return AttnOpts(None if sink is None else sink.data_ptr(),
+                    None if pos is None else pos.data_ptr(), float(rope_theta))
 
 
 _lib = None
@@ -85,6 +104,13 @@ def load(path=None):
         "csa2_reindex_decode": (I32, [ctypes.POINTER(CacheDesc), P, I64, P,
                                       P, P, P, P, I32, I32, F32, P, P, P, SZ,
                                       P]),
+        "csa2_sparse_attn_decode_ex": (I32, [ctypes.POINTER(CacheDesc), P, P,
+                                             P, P, P, I32, I32, F32,
+                                             ctypes.POINTER(PoolOpts),
+                                             ctypes.POINTER(AttnOpts), P, P,
+                                             P, SZ, P]),
+        "csa2_reuse_attn_ex": (I32, [P, P, I64, P, I32, P, P, P, I32, F32,
+                                     ctypes.POINTER(AttnOpts), P, P, SZ, P]),
         "csa2_reuse_attn": (I32, [P, P, I64, P, I32, P, P, P, I32, F32, P, P,
                                   SZ, P]),
         "csa2_workspace_size": (SZ, [I32, I32, I64, I32,
@@ -257,7 +283,8 @@ def cache_desc(main_codes, main_scales, idx_codes, idx_scales, n_entries,
 
 
 def sparse_attn_decode(cache, q_idx, w, q, swa, n_swa, k, scale, pool=None,
-                       out=None, topk_out=None, ws=None):
+                       out=None, topk_out=None, ws=None, sink=None, pos=None,
+                       rope_theta=10000.0):
     """One Full-layer decode step.  `cache` is a CacheDesc (keep the
     tensors it points to alive).  Returns (out bf16 [B,64,512], topk
     [B,k])."""
@@ -272,10 +299,18 @@ def sparse_attn_decode(cache, q_idx, w, q, swa, n_swa, k, scale, pool=None,
         need = load().csa2_workspace_size(OP_DECODE, B, cache.n_cap, k,
                                           ctypes.byref(po) if po else None)
         ws = workspace(need, dev)
-    _check(load().csa2_sparse_attn_decode(
-        ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
-        _ptr(n_swa), B, k, float(scale), ctypes.byref(po) if po else None,
-        _ptr(out), _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
+    ao = _attn_opts(sink, pos, rope_theta)
+    if ao is None:
+        _check(load().csa2_sparse_attn_decode(
+            ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
+            _ptr(n_swa), B, k, float(scale), ctypes.byref(po) if po else None,
+            _ptr(out), _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
+    else:
+        _check(load().csa2_sparse_attn_decode_ex(
+            ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
+            _ptr(n_swa), B, k, float(scale), ctypes.byref(po) if po else None,
+            ctypes.byref(ao), _ptr(out), _ptr(topk_out), _ptr(ws), ws.numel(),
+            _stream()))
     return out, topk_out
 
 
@@ -352,15 +387,23 @@ def reindex_decode(cache, pool_ids, q_idx, w, q, swa, n_swa, k, scale,
 
 
 def reuse_attn(main_codes, main_scales, topk_ids, q, swa, n_swa, scale,
-               out=None, ws=None):
+               out=None, ws=None, sink=None, pos=None, rope_theta=10000.0):
     B, k = topk_ids.shape
     dev = q.device
     if out is None:
         out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
     if ws is None:
         ws = workspace(workspace_size(OP_REUSE, B, main_codes.shape[1], k), dev)
-    _check(load().csa2_reuse_attn(
-        _ptr(main_codes), _ptr(main_scales), main_codes.shape[1],
-        _ptr(topk_ids), k, _ptr(q), _ptr(swa), _ptr(n_swa), B, float(scale),
-        _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    ao = _attn_opts(sink, pos, rope_theta)
+    if ao is None:
+        _check(load().csa2_reuse_attn(
+            _ptr(main_codes), _ptr(main_scales), main_codes.shape[1],
+            _ptr(topk_ids), k, _ptr(q), _ptr(swa), _ptr(n_swa), B,
+            float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    else:
+        _check(load().csa2_reuse_attn_ex(
+            _ptr(main_codes), _ptr(main_scales), main_codes.shape[1],
+            _ptr(topk_ids), k, _ptr(q), _ptr(swa), _ptr(n_swa), B,
+            float(scale), ctypes.byref(ao), _ptr(out), _ptr(ws), ws.numel(),
+            _stream()))
     return out

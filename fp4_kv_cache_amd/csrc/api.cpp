@@ -1,6 +1,7 @@
 // libcsa2 C ABI: argument validation, workspace layout and the enqueue
 // order of each call.  Every check happens before the first launch; on
 // failure nothing is enqueued and a thread-local message is kept.
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -315,6 +316,26 @@ csa2_status csa2_build_block_keys(const uint8_t* idx_codes,
 }
 
 namespace {
+// The attention epilogue of csa2_attn_opts: pair frequencies in double,
+// rope_theta^(-2i/64).
+csa2_status make_epilogue(const csa2_attn_opts* o, csa2::AttnEpilogue& epi) {
+  epi = csa2::AttnEpilogue{};
+  if (!o) return CSA2_OK;
+  if (o->sink && !aligned(o->sink, 4))
+    return fail(CSA2_ERR_ALIGNMENT, "sink needs 4-byte alignment");
+  if (o->pos) {
+    if (!aligned(o->pos, 4))
+      return fail(CSA2_ERR_ALIGNMENT, "pos needs 4-byte alignment");
+    if (!(o->rope_theta > 0.0f) || !std::isfinite(o->rope_theta))
+      return fail(CSA2_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+    for (int i = 0; i < 32; ++i)
+      epi.rope_w[i] = std::pow((double)o->rope_theta, -2.0 * i / 64.0);
+  }
+  epi.sink = o->sink;
+  epi.pos = o->pos;
+  return CSA2_OK;
+}
+
 // Checks the indexer query (bf16, or MXFP4 planes when q_scales is set).
 csa2_status check_query(const csa2::IndexQuery& iq) {
   if (!iq.q || !iq.w) return fail(CSA2_ERR_INVALID_ARG, "null indexer query");
@@ -426,6 +447,21 @@ csa2_status csa2_reuse_attn(const uint8_t* main_codes,
                             const uint8_t* swa, const int32_t* n_swa,
                             int32_t B, float scale, uint16_t* out, void* ws,
                             size_t ws_bytes, void* stream) {
+  return csa2_reuse_attn_ex(main_codes, main_scales, n_cap, topk, k, q, swa,
+                            n_swa, B, scale, nullptr, out, ws, ws_bytes,
+                            stream);
+}
+
+csa2_status csa2_reuse_attn_ex(const uint8_t* main_codes,
+                               const uint8_t* main_scales, int64_t n_cap,
+                               const int32_t* topk, int32_t k,
+                               const uint16_t* q, const uint8_t* swa,
+                               const int32_t* n_swa, int32_t B, float scale,
+                               const csa2_attn_opts* opts, uint16_t* out,
+                               void* ws, size_t ws_bytes, void* stream) {
+  csa2::AttnEpilogue epi;
+  csa2_status est = make_epilogue(opts, epi);
+  if (est) return est;
   csa2_status st = check_attn_common(main_codes, main_scales, n_cap, q, swa,
                                      n_swa, B, k, scale, out);
   if (st) return st;
@@ -439,7 +475,7 @@ csa2_status csa2_reuse_attn(const uint8_t* main_codes,
   if (st) return st;
   hipError_t e = csa2::launch_attn(main_codes, main_scales, n_cap, topk, k, q,
                                    swa, n_swa, B, scale, out, ws,
-                                   static_cast<hipStream_t>(stream));
+                                   static_cast<hipStream_t>(stream), epi);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_reuse_attn launch");
 }
 
@@ -449,7 +485,11 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
                         const int32_t* n_swa, int32_t B, int32_t k,
                         float scale, const csa2_pool_opts* pool,
                         uint16_t* out, int32_t* topk_out, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        size_t ws_bytes, void* stream,
+                        const csa2_attn_opts* opts = nullptr) {
+  csa2::AttnEpilogue epi;
+  csa2_status est = make_epilogue(opts, epi);
+  if (est) return est;
   if (!kv) return fail(CSA2_ERR_INVALID_ARG, "null cache descriptor");
   csa2_status st = check_attn_common(kv->main_codes, kv->main_scales,
                                      kv->n_cap, q, swa, n_swa, B, k, scale, out);
@@ -514,7 +554,8 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
     if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
   }
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
-                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
+                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s,
+                        epi);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return CSA2_OK;
 }
@@ -654,4 +695,19 @@ csa2_status csa2_reindex_decode(const csa2_cache* kv, const int32_t* pool,
                         k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return CSA2_OK;
+}
+
+csa2_status csa2_sparse_attn_decode_ex(const csa2_cache* kv,
+                                       const uint16_t* q_idx, const float* w,
+                                       const uint16_t* q, const uint8_t* swa,
+                                       const int32_t* n_swa, int32_t B,
+                                       int32_t k, float scale,
+                                       const csa2_pool_opts* pool,
+                                       const csa2_attn_opts* opts,
+                                       uint16_t* out, int32_t* topk_out,
+                                       void* ws, size_t ws_bytes,
+                                       void* stream) {
+  return decode_impl(kv, csa2::IndexQuery{q_idx, nullptr, w}, q, swa, n_swa,
+                     B, k, scale, pool, out, topk_out, ws, ws_bytes, stream,
+                     opts);
 }

@@ -74,6 +74,30 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // Chunk index (16-byte units) of (dim d) inside a quarter of the V buffer.
 __device__ __forceinline__ int vs_phys(int d) { return d ^ ((d >> 3) & 7); }
 
+// Rotation of RoPE pair i at query position t by -t * w (w = the pair's
+// frequency, computed on the host in double): the angle is formed and
+// reduced modulo 2 pi in double (t * w reaches about 1e6 rad at a million
+// positions), then the cosine and sine of the remainder in float.
+__device__ __forceinline__ void rope_cs(int32_t t, double w, float& c,
+                                        float& s) {
+  constexpr double kTwoPiHi = 6.283185307179586;          // 2 pi, head
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;     // 2 pi, tail
+  const double ang = -(double)t * w;
+  const double kq = rint(ang * (1.0 / kTwoPiHi));
+  double r = fma(-kq, kTwoPiHi, ang);
+  r = fma(-kq, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
+}
+
+// (x, y) -> (x c - y s, x s + y c): the rotation of one pair.
+__device__ __forceinline__ void rotate_pair(float& x, float& y, float c,
+                                            float s) {
+  const float nx = x * c - y * s;
+  const float ny = x * s + y * c;
+  x = nx;
+  y = ny;
+}
+
 struct AttnArgs {
   const uint8_t* main_codes;
   const uint8_t* main_scales;
@@ -91,6 +115,7 @@ struct AttnArgs {
   int splits;
   int tiles_per_split;
   int n_tiles;
+  AttnEpilogue epi;        // sink and de-rotation (final output only)
 };
 
 // Raw gather registers for the 8 slots this lane dequantises in one tile.
@@ -433,7 +458,30 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   // Fold the running sums of the four lanes that share a head.
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const bool final_out = p.splits == 1;
+  // A sink logit joins the denominator of the final output (a split's
+  // partial keeps its own sum; the merge adds the sink once).  With no key
+  // at all (m_run = -inf) the output is zero either way.
+  float den = l_tot;
+  if (final_out && p.epi.sink != nullptr)
+    den += exp2f(p.epi.sink[head] * kLog2e - m_run);
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  if (final_out && p.epi.pos != nullptr) {
+    // De-rotate dims 448..511 (blocks 28..31): this lane holds dims
+    // 16*blk + 4*q4 + r, pairs (r = 0, 1) and (r = 2, 3).
+    const int32_t t = p.epi.pos[b];
+#pragma unroll
+    for (int blk = 28; blk < 32; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        float c, sn;
+        rope_cs(t, p.epi.rope_w[8 * (blk - 28) + 2 * q4 + r / 2], c, sn);
+        float x = acc[blk][r], y = acc[blk][r + 1];
+        rotate_pair(x, y, c, sn);
+        acc[blk][r] = x;
+        acc[blk][r + 1] = y;
+      }
+  }
 
   // The output (final bf16, or this split's fp16 partial normalised by its
   // own sum -- a convex combination of keys, so |value| <= 2688 fits fp16
@@ -442,7 +490,6 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   // and whole 1 KB head rows per instruction.
   constexpr int kRowH = 512 + 8;                 // staged row, +16 B pad
   uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + wave * 16 * kRowH;
-  const bool final_out = p.splits == 1;
 #pragma unroll
   for (int blk = 0; blk < 32; ++blk) {
     uint32_t lo, hi;
@@ -479,7 +526,7 @@ constexpr int kMaxSplits = 16;
 
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
-    int splits, int B, uint16_t* __restrict__ out) {
+    int splits, int B, uint16_t* __restrict__ out, AttnEpilogue epi) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= (int64_t)B * kHeads * 64) return;
   const int d8 = (int)(t & 63);
@@ -500,8 +547,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
     if (s < splits) M = fmaxf(M, ml[s].x);
+  // A sink logit (log2 units here) joins the denominator once; the
+  // reference point covers it too.
+  const float z = epi.sink != nullptr ? epi.sink[head] * kLog2e
+                                      : -__builtin_inff();
+  M = fmaxf(M, z);
   const float mref = M == -__builtin_inff() ? 0.0f : M;
-  float L = 0.0f;
+  float L = z == -__builtin_inff() ? 0.0f : exp2f(z - mref);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
@@ -518,6 +570,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  if (epi.pos != nullptr && d8 >= 56) {
+    // Dims 8*d8 .. 8*d8+7 are RoPE pairs 4*(d8-56) .. +3.
+    const int32_t t = epi.pos[b];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float c, sn;
+      rope_cs(t, epi.rope_w[4 * (d8 - 56) + j], c, sn);
+      rotate_pair(o[2 * j], o[2 * j + 1], c, sn);
+    }
+  }
   u32x4 w;
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = pack_bf16(o[2 * i] * inv, o[2 * i + 1] * inv);
@@ -553,7 +615,8 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        int64_t n_cap, const int32_t* topk, int k,
                        const uint16_t* q, const uint8_t* swa,
                        const int32_t* n_swa, int B, float scale,
-                       uint16_t* out, void* ws, hipStream_t s) {
+                       uint16_t* out, void* ws, hipStream_t s,
+                       const AttnEpilogue& epi) {
   if (B == 0) return hipSuccess;
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(attn_kernel),
@@ -572,6 +635,7 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   a.out = out;
   a.B = B;
   a.n_tiles = (k + kWindow + kTile - 1) / kTile;
+  a.epi = epi;
   a.splits = attn_splits(B, k);
   a.tiles_per_split = (a.n_tiles + a.splits - 1) / a.splits;
   if (a.splits > 1) {
@@ -588,7 +652,7 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   const int64_t threads = (int64_t)B * kHeads * 64;
   hipLaunchKernelGGL(attn_combine_kernel,
                      dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     a.part_o, a.part_ml, a.splits, B, out);
+                     a.part_o, a.part_ml, a.splits, B, out, epi);
   return hipGetLastError();
 }
 

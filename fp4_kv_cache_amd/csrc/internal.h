@@ -79,10 +79,19 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
 // attn.hip
 int attn_splits(int B, int k);
 size_t attn_workspace(int B, int k);
+// Optional output details of the attention: a per-head sink logit in the
+// softmax denominator, and the partial-RoPE de-rotation of the last 64
+// output dims by the query position (pair i turns by -pos * rope_w[i]).
+struct AttnEpilogue {
+  const float* sink = nullptr;     // [64] logits, or null
+  const int32_t* pos = nullptr;    // [B] query positions, or null
+  double rope_w[32] = {};          // frequencies of the 32 pairs
+};
 hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        int64_t n_cap, const int32_t* topk, int k,
                        const uint16_t* q, const uint8_t* swa,
                        const int32_t* n_swa, int B, float scale,
-                       uint16_t* out, void* ws, hipStream_t s);
+                       uint16_t* out, void* ws, hipStream_t s,
+                       const AttnEpilogue& epi = AttnEpilogue{});
 
 }  // namespace csa2

@@ -284,6 +284,45 @@ csa2_status csa2_reuse_attn(const uint8_t *main_codes,
                             int32_t B, float scale, uint16_t *out, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* csa2_attn_opts -- the attention details of [V4] "other details" (NULL
+ * pointers leave either out):
+ *   sink        [64] float32 per-head sink logits z'_h (attention-sink
+ *               equation): exp(z'_h) joins only the softmax denominator, in
+ *               the units of the scaled logits scale * q.k
+ *   pos         [B] int32 query positions t (device): the last 64 output
+ *               dims are de-rotated by -t (partial-RoPE paragraph, the
+ *               R_{-t} o_t equation).  Reading: interleaved pairs
+ *               (448 + 2i, 449 + 2i), frequency rope_theta^(-2i/64),
+ *               position p turning (x, y) into (x cos - y sin, x sin + y cos)
+ *               of the angle p * frequency
+ *   rope_theta  > 0 (10000 in the usual RoPE), used with pos. */
+typedef struct {
+  const float *sink;
+  const int32_t *pos;
+  float rope_theta;
+} csa2_attn_opts;
+
+/* csa2_sparse_attn_decode_ex / csa2_reuse_attn_ex -- csa2_sparse_attn_decode
+ * and csa2_reuse_attn with the csa2_attn_opts details applied to the
+ * output (opts NULL: identical to the plain calls). */
+csa2_status csa2_sparse_attn_decode_ex(const csa2_cache *kv,
+                                       const uint16_t *q_idx, const float *w,
+                                       const uint16_t *q, const uint8_t *swa,
+                                       const int32_t *n_swa, int32_t B,
+                                       int32_t k, float scale,
+                                       const csa2_pool_opts *pool,
+                                       const csa2_attn_opts *opts,
+                                       uint16_t *out, int32_t *topk_out,
+                                       void *ws, size_t ws_bytes,
+                                       void *stream);
+csa2_status csa2_reuse_attn_ex(const uint8_t *main_codes,
+                               const uint8_t *main_scales, int64_t n_cap,
+                               const int32_t *topk, int32_t k,
+                               const uint16_t *q, const uint8_t *swa,
+                               const int32_t *n_swa, int32_t B, float scale,
+                               const csa2_attn_opts *opts, uint16_t *out,
+                               void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * Helpers. */
 
