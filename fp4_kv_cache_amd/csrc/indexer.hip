@@ -143,8 +143,9 @@ template <bool SCALED> struct Depth<1, SCALED> {
 // ceil(n_rows/8)) and each 256-row group's (a wavefront's rows) to
 // btmax[B][ceil(nb/32)].
 // QFP4: the query is MXFP4 planes (codes q[B][32][64], scales
-// q_scales[B][32][4]) instead of bf16 q[B][32][128].
-template <int KEYFMT, bool KEYS, bool QFP4>
+// q_scales[B][32][4]) instead of bf16 q[B][32][128].  BLK (with KEYS):
+// the block maxima are written too.
+template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       uint32_t m = dpp_max<0x111, 0xf>(key);
       m = dpp_max<0x112, 0xf>(m);
       m = dpp_max<0x114, 0xf>(m);
-      if (bmax != nullptr && half == 0 && (col & 7) == 7) {
+      if (BLK && half == 0 && (col & 7) == 7) {
         const int64_t nbs = (n_rows + 7) >> 3;
         const int64_t blk = i >> 3;
         if (blk < nbs) bmax[(int64_t)b * ((nbs + 31) & ~(int64_t)31) + blk] = m;
@@ -321,12 +322,12 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       const uint32_t mx = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
       if (lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
-      wmax = max(wmax, mx);
+      if constexpr (BLK) wmax = max(wmax, mx);
     } else {
       if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
     }
   }
-  if (KEYS && btmax != nullptr && lane == 0) {
+  if (BLK && lane == 0) {
     const int64_t nbt = (((n_rows + 7) >> 3) + 31) >> 5;
     btmax[(int64_t)b * nbt + (base >> 8)] = wmax;
   }
@@ -341,9 +342,16 @@ void launch_one(dim3 grid, hipStream_t s, const void* k_codes,
                 const int32_t* n_entries, const int32_t* cand, int64_t n_rows,
                 const IndexQuery& iq, float* scores, uint32_t* tmax,
                 uint32_t* bmax, uint32_t* btmax) {
-  hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256), 0,
-                     s, k_codes, k_scales, n_cap, n_entries, cand, n_rows,
-                     iq.q, iq.q_scales, iq.w, scores, tmax, bmax, btmax);
+  if (KEYS && KEYFMT == 0 && !QFP4 && bmax)
+    hipLaunchKernelGGL((indexer_kernel<0, true, false, true>), grid,
+                       dim3(256), 0, s, k_codes, k_scales, n_cap, n_entries,
+                       cand, n_rows, iq.q, iq.q_scales, iq.w, scores, tmax,
+                       bmax, btmax);
+  else
+    hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256),
+                       0, s, k_codes, k_scales, n_cap, n_entries, cand,
+                       n_rows, iq.q, iq.q_scales, iq.w, scores, tmax, bmax,
+                       btmax);
 }
 template <int KEYFMT, bool KEYS>
 void launch_q(dim3 grid, hipStream_t s, const void* k_codes,
@@ -369,7 +377,9 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           float* scores, hipStream_t s, uint32_t* tmax,
                           uint32_t* bmax, uint32_t* btmax) {
   if (n_rows == 0 || B == 0) return hipSuccess;
-  if (bmax && (!tmax || cand || !btmax)) return hipErrorInvalidValue;
+  // Block maxima: MXFP4 keys, bf16 query, all rows.
+  if (bmax && (!tmax || cand || !btmax || keyfmt != 0 || iq.q_scales))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)((n_rows + kEntriesPerBlock - 1) / kEntriesPerBlock),
                   (unsigned)B);
   if (keyfmt == 0 && tmax)

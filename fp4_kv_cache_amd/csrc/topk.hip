@@ -421,16 +421,11 @@ __device__ __forceinline__ int gather_dispatch(
                                                            len, src);
 }
 
-// Workgroups 0 .. B0-1 take the rows of a0, the rest those of a1 (two
-// independent selections in one launch, run side by side).
+// One row b of a selection (the workgroup's whole work).
 template <bool HAS_IDS, bool KEYS>
-__global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a0,
-                                                         RowArgs a1, int B0) {
+__device__ __forceinline__ void row_select_row(const RowArgs& a, int b) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
-  const bool second = (int)blockIdx.x >= B0;
-  const RowArgs& a = second ? a1 : a0;
-  const int b = second ? (int)blockIdx.x - B0 : (int)blockIdx.x;
   const int tid = threadIdx.x;
   for (int i = tid; i < kNT / 64 * kNB; i += kNT) (&sm.sel.hist[0][0])[i] = 0;
   int64_t len = a.n_cols;
@@ -474,6 +469,20 @@ __global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a0,
     a.out[ob + p] = -1;
 }
 
+template <bool HAS_IDS, bool KEYS>
+__global__ __launch_bounds__(kNT) void row_select_kernel(RowArgs a) {
+  row_select_row<HAS_IDS, KEYS>(a, blockIdx.x);
+}
+
+// Two independent key selections in one launch, side by side: workgroups
+// 0 .. B0-1 take the rows of a0, the rest those of a1.
+__global__ __launch_bounds__(kNT) void row_select_pair_kernel(RowArgs a0,
+                                                              RowArgs a1,
+                                                              int B0) {
+  if ((int)blockIdx.x < B0) row_select_row<false, true>(a0, blockIdx.x);
+  else row_select_row<false, true>(a1, (int)blockIdx.x - B0);
+}
+
 // Tile maxima of a plain score array (entries with a negative id count as
 // -inf).  One thread per tile.
 __global__ void tilemax_kernel(const float* __restrict__ scores, int64_t ld,
@@ -501,16 +510,14 @@ size_t topk_workspace(int B, int64_t ld) {
 }
 
 template <bool HAS_IDS, bool KEYS>
-hipError_t launch_rows(const RowArgs& a0, int B0, const RowArgs& a1, int B1,
-                       hipStream_t s) {
+hipError_t launch_rows(const RowArgs& a, int B, hipStream_t s) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = ensure_lds_limit(
       reinterpret_cast<const void*>(row_select_kernel<HAS_IDS, KEYS>),
       (int)sizeof(RowSmem), lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((row_select_kernel<HAS_IDS, KEYS>),
-                     dim3((unsigned)(B0 + B1)), dim3(kNT), sizeof(RowSmem), s,
-                     a0, a1, B0);
+  hipLaunchKernelGGL((row_select_kernel<HAS_IDS, KEYS>), dim3((unsigned)B),
+                     dim3(kNT), sizeof(RowSmem), s, a);
   return hipGetLastError();
 }
 
@@ -540,10 +547,10 @@ hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
   if (n_cols > ld || (keys && !ids && (ld & 31))) return hipErrorInvalidValue;
   const RowArgs a = row_args(scores, tmax, ld, n_cols, n_valid, ids, k, block,
                              limit, out);
-  if (ids) return keys ? launch_rows<true, true>(a, B, a, 0, s)
-                       : launch_rows<true, false>(a, B, a, 0, s);
-  return keys ? launch_rows<false, true>(a, B, a, 0, s)
-              : launch_rows<false, false>(a, B, a, 0, s);
+  if (ids) return keys ? launch_rows<true, true>(a, B, s)
+                       : launch_rows<true, false>(a, B, s);
+  return keys ? launch_rows<false, true>(a, B, s)
+              : launch_rows<false, false>(a, B, s);
 }
 
 hipError_t launch_row_select_pair(const KeyRows& r0, const KeyRows& r1, int B,
@@ -555,7 +562,14 @@ hipError_t launch_row_select_pair(const KeyRows& r0, const KeyRows& r1, int B,
                               nullptr, r0.k, r0.block, r0.limit, r0.out);
   const RowArgs a1 = row_args(r1.keys, r1.tmax, r1.ld, r1.n_cols, r1.n_valid,
                               nullptr, r1.k, r1.block, r1.limit, r1.out);
-  return launch_rows<false, true>(a0, B, a1, B, s);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(
+      reinterpret_cast<const void*>(row_select_pair_kernel),
+      (int)sizeof(RowSmem), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_select_pair_kernel, dim3((unsigned)(2 * B)),
+                     dim3(kNT), sizeof(RowSmem), s, a0, a1, B);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
