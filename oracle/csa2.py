@@ -362,3 +362,28 @@ def reuse_layer_ext(main_codes, main_scales, sel, q_bits, swa_codes, n_swa,
     o = (mqa_decode(q_bits, kv, scale) if sink is None
          else mqa_decode_sink(q_bits, kv, scale, sink))
     return o if pos is None else rope_derotate(o, pos, theta)
+
+
+# ------------------------------------------------ write path (compressor) --
+def softmax_pool(c, z):
+    """Sequence compression of one block, [KVC] 4.1: the new entry is the
+    per-channel softmax(Z)-weighted sum of the block's m token rows,
+    C_bar = sum_i softmax_i(Z_i) (.) C_i.  c, z: float64 [m, 512]."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max(axis=0, keepdims=True))
+    return (e * np.asarray(c, dtype=np.float64)).sum(axis=0) / e.sum(axis=0)
+
+
+def compress_block(h_bits, w_kv_bits, w_z_bits, w_ik_bits):
+    """The CSA2 write path for one block of m tokens, [KVC] 4.1 (main-KV,
+    sequence-compression and indexer-K equations; [ARCH] 2.3): C = H W^KV
+    and Z = H W^Z for the block's hidden states, C_bar = softmax_pool(C, Z)
+    (non-overlapping blocks), and K^I = C_bar W^IK.  bf16 bits: h [m, d];
+    w_kv, w_z [512, d] and w_ik [128, 512] (output x input).
+    Returns (C [m, 512], C_bar [512], K^I [128]), float64."""
+    h = F.bf16_bits_to_f64(h_bits)
+    c = h @ F.bf16_bits_to_f64(w_kv_bits).T
+    z = h @ F.bf16_bits_to_f64(w_z_bits).T
+    cbar = softmax_pool(c, z)
+    ki = cbar @ F.bf16_bits_to_f64(w_ik_bits).T
+    return c, cbar, ki

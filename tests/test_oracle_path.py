@@ -421,3 +421,44 @@ def test_derotated_output_is_relative():
         if shift == 0:
             base = d
         assert np.allclose(d, base, rtol=1e-9, atol=1e-9)
+
+
+# -------------------------------------------------------- compressor ----
+def test_softmax_pool_bruteforce_and_limits():
+    rng = np.random.default_rng(51)
+    c = rng.standard_normal((3, 512))
+    z = rng.standard_normal((3, 512)) * 3
+    got = O.softmax_pool(c, z)
+    for ch in range(0, 512, 37):
+        ws = [math.exp(z[i, ch]) for i in range(3)]
+        want = sum(ws[i] * c[i, ch] for i in range(3)) / sum(ws)
+        assert got[ch] == pytest.approx(want, rel=1e-12, abs=1e-12)
+    assert np.array_equal(O.softmax_pool(c[:1], z[:1]), c[0])       # m = 1
+    assert np.allclose(O.softmax_pool(c, np.zeros_like(z)), c.mean(axis=0))
+    zz = np.zeros_like(z)
+    zz[2] = 1000.0                                                  # dominant
+    assert np.allclose(O.softmax_pool(c, zz), c[2])
+
+
+def test_compress_block_bruteforce():
+    rng = np.random.default_rng(52)
+    d, m = 16, 2
+    hb = _bf16(rng.standard_normal((m, d)))
+    wkv = _bf16(rng.standard_normal((512, d)) / 4)
+    wz = _bf16(rng.standard_normal((512, d)) / 4)
+    wik = _bf16(rng.standard_normal((128, 512)) / 16)
+    c, cbar, ki = O.compress_block(hb, wkv, wz, wik)
+    h, Wkv, Wz, Wik = (F.bf16_bits_to_f64(x) for x in (hb, wkv, wz, wik))
+    for i in range(m):
+        for o in (0, 7, 300, 511):
+            assert c[i, o] == pytest.approx(
+                math.fsum(h[i, j] * Wkv[o, j] for j in range(d)), rel=1e-13)
+    zc = [[math.fsum(h[i, j] * Wz[o, j] for j in range(d)) for o in range(512)]
+          for i in range(m)]
+    for o in (3, 256):
+        ws = [math.exp(zc[i][o]) for i in range(m)]
+        want = sum(ws[i] * c[i, o] for i in range(m)) / sum(ws)
+        assert cbar[o] == pytest.approx(want, rel=1e-12)
+    for o in (0, 127):
+        assert ki[o] == pytest.approx(
+            math.fsum(cbar[j] * Wik[o, j] for j in range(512)), rel=1e-12)
