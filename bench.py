@@ -240,6 +240,28 @@ def run_gpu(args, wl):
 
         steps["full_pool"] = step_full_pool
         steps["reindex"] = step_reindex
+    # The write path at decode: one new entry per sequence from the m newest
+    # tokens' hidden states (d = 7168, the pages' model width), appended to
+    # caches of its own (the timed steps' caches stay as they are).
+    from fp4_kv_cache_amd import inputs as inp
+    cm, cd = wl.m, 7168
+    c_h = inp.hidden_states(900, wl.B, cm, cd, dev)
+    c_w = inp.compressor_weights(900, cd, dev)
+    c_rows = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
+    c_slot = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
+    c_bufs = [torch.zeros(sh, dtype=torch.uint8, device=dev)
+              for sh in ((wl.B, 1, 256), (wl.B, 1, 32), (wl.B, 1, 64),
+                         (wl.B, 1, 4), (wl.B, 128, 512))]
+    c_ws = csa2.workspace(csa2.load().csa2_workspace_size(
+        csa2.OP_COMPRESS, wl.B, cm, cd, None), dev)
+
+    def step_compress(i):
+        csa2.compress_append(c_h, *c_w, c_rows, *c_bufs[:4], swa=c_bufs[4],
+                             swa_slot=c_slot, ws=c_ws)
+
+    steps["compress"] = step_compress
+    compress_bytes = (2 * 512 * cd * 2 + 128 * 512 * 2 + wl.B * cm * cd * 2
+                      + wl.B * (288 + 68 + cm * 512))
     timing = {q: time_steps(fn, args, R, out, ids) for q, fn in steps.items()}
 
     # -- per-kernel durations with HIP events on the launch stream: the same
@@ -300,7 +322,7 @@ def run_gpu(args, wl):
     t_tk = timed(k_topk, M)
     t_at = timed(k_attn, M)
     return dict(timing=timing, t_idx=t_idx, t_topk=t_tk, t_attn=t_at,
-                replicas=R, st=st)
+                replicas=R, st=st, compress=(cm, cd, compress_bytes))
 
 
 COPY_ELEMS = 64 << 20          # float32 elements of the calibration copy
@@ -480,6 +502,15 @@ def main():
         "value": wl.B / ep_s, "ms_per_step": ep_s * 1e3,
         "what": "the headline step with per-head sink logits and the "
                 "partial-RoPE output de-rotation (csa2_sparse_attn_decode_ex)"}
+    cp = g["timing"]["compress"]
+    cp_s = cp[1] if cp[1] is not None else cp[0]
+    cm, cd, cbytes = g["compress"]
+    line["variants"]["compress_append"] = {
+        "value": wl.B / cp_s, "ms_per_step": cp_s * 1e3, "m": cm, "d": cd,
+        "algorithmic_bytes": cbytes,
+        "achieved_GBs": cbytes / cp_s / 1e9,
+        "what": "csa2_compress_append: one new entry per sequence (C, Z "
+                "projections, softmax pooling, K^I, FP4/MXFP4/E4M3 append)"}
     if "full_pool" in g["timing"]:
         fp, ri = (g["timing"][x] for x in ("full_pool", "reindex"))
         fp_s = fp[1] if fp[1] is not None else fp[0]

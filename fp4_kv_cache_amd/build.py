@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "libcsa2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "pack.hip", "indexer.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.cpp", "pack.hip", "indexer.hip", "topk.hip", "attn.hip",
+           "compress.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -15,14 +15,16 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 FMT_MAIN, FMT_IDX, FMT_SWA = 0, 1, 2
 KEYS_MXFP4, KEYS_BF16 = 0, 1
-OP_TOPK, OP_DECODE, OP_REUSE, OP_FULL_POOL, OP_REINDEX = 0, 1, 2, 3, 4
+OP_TOPK, OP_DECODE, OP_REUSE, OP_FULL_POOL, OP_REINDEX, OP_COMPRESS = (
+    0, 1, 2, 3, 4, 5)
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGNMENT",
           4: "WORKSPACE", 5: "HIP"}
 EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
            "csa2_indexer_score", "csa2_indexer_score_fp4q", "csa2_topk",
            "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_fp4q",
            "csa2_full_pool_decode", "csa2_reindex_decode", "csa2_reuse_attn",
-           "csa2_sparse_attn_decode_ex", "csa2_reuse_attn_ex", "csa2_workspace_size", "csa2_entry_bytes",
+           "csa2_sparse_attn_decode_ex", "csa2_reuse_attn_ex",
+           "csa2_compress_append", "csa2_workspace_size", "csa2_entry_bytes",
            "csa2_kv_bytes_per_token", "csa2_last_error", "csa2_version"]
 
 
@@ -111,6 +113,8 @@ def load(path=None):
                                              P, SZ, P]),
         "csa2_reuse_attn_ex": (I32, [P, P, I64, P, I32, P, P, P, I32, F32,
                                      ctypes.POINTER(AttnOpts), P, P, SZ, P]),
+        "csa2_compress_append": (I32, [P, I32, I32, I32, P, P, P, P, P, P, P,
+                                       P, I64, P, P, P, P, P, P, SZ, P]),
         "csa2_reuse_attn": (I32, [P, P, I64, P, I32, P, P, P, I32, F32, P, P,
                                   SZ, P]),
         "csa2_workspace_size": (SZ, [I32, I32, I64, I32,
@@ -407,3 +411,35 @@ def reuse_attn(main_codes, main_scales, topk_ids, q, swa, n_swa, scale,
             float(scale), ctypes.byref(ao), _ptr(out), _ptr(ws), ws.numel(),
             _stream()))
     return out
+
+
+def compress_append(h, w_kv, w_z, w_ik, rows, main_codes, main_scales,
+                    idx_codes, idx_scales, swa=None, swa_slot=None,
+                    debug=False, ws=None):
+    """The decode-time write path: h [B, m, d] bf16 -> one new entry per
+    sequence at rows [B] (int32) of the caches ([B, n_cap, ...]); the m
+    rows C_i go to window slots (swa_slot + i) mod 128 when swa is given.
+    With debug=True returns (C_bar [B,512], K^I [B,128], C [B,m,512])
+    float32."""
+    B, m, d = h.shape
+    _need(h, torch.bfloat16, name="h")
+    for t, shp, nm in ((w_kv, (512, d), "w_kv"), (w_z, (512, d), "w_z"),
+                       (w_ik, (128, 512), "w_ik")):
+        _need(t, torch.bfloat16, shp, nm)
+    _need(rows, torch.int32, (B,), "rows")
+    dev = h.device
+    outs = (None, None, None)
+    if debug:
+        outs = (torch.empty((B, 512), dtype=torch.float32, device=dev),
+                torch.empty((B, 128), dtype=torch.float32, device=dev),
+                torch.empty((B, m, 512), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = workspace(load().csa2_workspace_size(OP_COMPRESS, B, m, d, None),
+                       dev)
+    _check(load().csa2_compress_append(
+        _ptr(h), B, m, d, _ptr(w_kv), _ptr(w_z), _ptr(w_ik), _ptr(rows),
+        _ptr(main_codes), _ptr(main_scales), _ptr(idx_codes),
+        _ptr(idx_scales), main_codes.shape[1], _ptr(swa), _ptr(swa_slot),
+        _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(ws), ws.numel(),
+        _stream()))
+    return outs if debug else None

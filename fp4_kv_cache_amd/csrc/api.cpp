@@ -218,6 +218,11 @@ double csa2_kv_bytes_per_token(const int32_t* m, int32_t n) {
 
 size_t csa2_workspace_size(int32_t op, int32_t B, int64_t n_cap, int32_t k,
                            const csa2_pool_opts* pool) {
+  if (op == CSA2_OP_COMPRESS) {     // n_cap = m, k = d
+    if (B < 0 || n_cap < 1 || n_cap > 16 || k < 16 || k > 16384 || k % 16)
+      return 0;
+    return csa2::compress_workspace(B, (int)n_cap, k);
+  }
   if (B < 0 || n_cap < 0 || n_cap > kMaxCap || k < 1 || k > kMaxK) return 0;
   switch (op) {
     case CSA2_OP_TOPK:
@@ -237,6 +242,8 @@ size_t csa2_workspace_size(int32_t op, int32_t B, int64_t n_cap, int32_t k,
     case CSA2_OP_REINDEX:
       if (n_cap < 1 || n_cap > kMaxPool) return 0;
       return reindex_layout(B, n_cap, k).total;
+    case CSA2_OP_COMPRESS:
+      return 0;     // handled above
     default:
       return 0;
   }
@@ -710,4 +717,43 @@ csa2_status csa2_sparse_attn_decode_ex(const csa2_cache* kv,
   return decode_impl(kv, csa2::IndexQuery{q_idx, nullptr, w}, q, swa, n_swa,
                      B, k, scale, pool, out, topk_out, ws, ws_bytes, stream,
                      opts);
+}
+
+csa2_status csa2_compress_append(const uint16_t* h, int32_t B, int32_t m,
+                                 int32_t d, const uint16_t* w_kv,
+                                 const uint16_t* w_z, const uint16_t* w_ik,
+                                 const int32_t* rows, uint8_t* main_codes,
+                                 uint8_t* main_scales, uint8_t* idx_codes,
+                                 uint8_t* idx_scales, int64_t n_cap,
+                                 uint8_t* swa, const int32_t* swa_slot,
+                                 float* cbar_out, float* ki_out, float* c_out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || n_cap < 1 || n_cap > kMaxCap)
+    return fail(CSA2_ERR_INVALID_ARG, "bad B or n_cap");
+  if (m < 1 || m > 16 || d < 16 || d > 16384 || d % 16)
+    return fail(CSA2_ERR_UNSUPPORTED, "m must be in 1..16 and d a multiple "
+                "of 16 in 16..16384");
+  if (B == 0) return CSA2_OK;
+  if (!h || !w_kv || !w_z || !w_ik || !rows || !main_codes || !main_scales ||
+      !idx_codes || !idx_scales)
+    return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
+  if ((swa == nullptr) != (swa_slot == nullptr))
+    return fail(CSA2_ERR_INVALID_ARG, "swa and swa_slot go together");
+  if (!aligned(h, 16) || !aligned(w_kv, 16) || !aligned(w_z, 16) ||
+      !aligned(w_ik, 16) || !aligned(rows, 4) || !aligned(main_codes, 16) ||
+      !aligned(idx_codes, 16) || (swa_slot && !aligned(swa_slot, 4)) ||
+      (cbar_out && !aligned(cbar_out, 4)) || (ki_out && !aligned(ki_out, 4)) ||
+      (c_out && !aligned(c_out, 4)))
+    return fail(CSA2_ERR_ALIGNMENT, "misaligned argument");
+  const size_t need = csa2::compress_workspace(B, m, d);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(CSA2_ERR_WORKSPACE, "compress needs %zu bytes of 256-byte "
+                "aligned workspace (got %zu)", need, ws_bytes);
+  csa2_status st = need_device();
+  if (st) return st;
+  hipError_t e = csa2::launch_compress(
+      h, B, m, d, w_kv, w_z, w_ik, rows, n_cap, main_codes, main_scales,
+      idx_codes, idx_scales, swa, swa_slot, cbar_out, ki_out, c_out, ws,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_compress_append launch");
 }

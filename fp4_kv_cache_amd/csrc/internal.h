@@ -94,4 +94,23 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        uint16_t* out, void* ws, hipStream_t s,
                        const AttnEpilogue& epi = AttnEpilogue{});
 
+// compress.hip
+// Workspace bytes of launch_compress (slice partials of the projections).
+size_t compress_workspace(int B, int m, int d);
+// The decode-time write path for B sequences: hidden rows h[B][m][d] (bf16)
+// -> C, Z (W^KV, W^Z: [512][d] bf16), C_bar (softmax pooling over the m
+// tokens), K^I = C_bar W^IK ([128][512] bf16), packed into row rows[b] of
+// each sequence's caches (skipped when outside [0, n_cap)), and the m rows
+// C_i into window slots (swa_slot[b] + i) mod 128 when swa is set.
+// cbar_out [B][512], ki_out [B][128], c_out [B][m][512] are optional.
+hipError_t launch_compress(const uint16_t* h, int B, int m, int d,
+                           const uint16_t* w_kv, const uint16_t* w_z,
+                           const uint16_t* w_ik, const int32_t* rows,
+                           int64_t n_cap, uint8_t* main_codes,
+                           uint8_t* main_scales, uint8_t* idx_codes,
+                           uint8_t* idx_scales, uint8_t* swa,
+                           const int32_t* swa_slot, float* cbar_out,
+                           float* ki_out, float* c_out, void* ws,
+                           hipStream_t s);
+
 }  // namespace csa2

@@ -56,6 +56,7 @@ WORKLOADS = {
 }
 
 T_MAIN, T_IDX, T_QIDX, T_W, T_Q, T_SWA, T_PLANT = 1, 2, 3, 4, 5, 6, 7
+T_HID, T_WKV, T_WZ, T_WIK = 8, 9, 10, 11
 
 
 def seed(cid, tensor, seq, chunk=0, layer=0):
@@ -135,3 +136,19 @@ def window_latents(wl, b, layer=0, device="cpu"):
     """float32 [128, 512] window rows of sequence b in a layer."""
     return _normal((N_WIN, D_MAIN), seed(wl.cid, T_SWA, b, layer=layer),
                    device)
+
+
+def hidden_states(cid, B, m, d, device="cpu"):
+    """bf16 [B, m, d] hidden states (N(0,1)) of the m newest tokens."""
+    return _normal((B, m, d), seed(cid, T_HID, 0), device).to(torch.bfloat16)
+
+
+def compressor_weights(cid, d, device="cpu"):
+    """Synthetic write-path weights, bf16, [out][in]: W^KV and W^Z [512, d]
+    and W^IK [128, 512], N(0, 1/in) so that the projections of N(0,1)
+    inputs have unit variance."""
+    wkv = _normal((512, d), seed(cid, T_WKV, 0), device) / d ** 0.5
+    wz = _normal((512, d), seed(cid, T_WZ, 0), device) / d ** 0.5
+    wik = _normal((128, 512), seed(cid, T_WIK, 0), device) / 512 ** 0.5
+    return (wkv.to(torch.bfloat16), wz.to(torch.bfloat16),
+            wik.to(torch.bfloat16))

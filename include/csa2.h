@@ -87,7 +87,8 @@ enum {
   CSA2_OP_DECODE = 1, /* csa2_sparse_attn_decode                          */
   CSA2_OP_REUSE = 2,  /* csa2_reuse_attn                                  */
   CSA2_OP_FULL_POOL = 3, /* csa2_full_pool_decode (needs the pool options)  */
-  CSA2_OP_REINDEX = 4    /* csa2_reindex_decode (n_cap argument = n_pool)  */
+  CSA2_OP_REINDEX = 4,   /* csa2_reindex_decode (n_cap argument = n_pool)  */
+  CSA2_OP_COMPRESS = 5   /* csa2_compress_append (n_cap = m, k = d)        */
 };
 
 /* The caches one Full layer owns (or a Reindex layer shares). */
@@ -322,6 +323,41 @@ csa2_status csa2_reuse_attn_ex(const uint8_t *main_codes,
                                const int32_t *n_swa, int32_t B, float scale,
                                const csa2_attn_opts *opts, uint16_t *out,
                                void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_compress_append -- the CSA2 write path at decode time ([KVC] 4.1
+ * main-KV, sequence-compression and indexer-K equations; [ARCH] 2.3):
+ * for each sequence the hidden states of the m newest tokens give
+ * C = H W^KV and Z = H W^Z (512 wide); the new main entry is their
+ * per-channel softmax(Z)-weighted sum over the m tokens, C_bar (blocks
+ * without overlap), and its indexer key K^I = C_bar W^IK (128 wide).  C_bar
+ * is packed (CSA2_FMT_MAIN rules, bit-exact with csa2_pack_kv of the same
+ * float32 values) into row rows[b] of the main planes and K^I (CSA2_FMT_IDX)
+ * into the same row of the indexer planes; rows outside [0, n_cap) are not
+ * written.  With swa non-NULL each token's C_i is also written, E4M3, to
+ * window slot (swa_slot[b] + i) mod 128.
+ *   h           [B][m][d] bf16 (16-byte aligned); d a multiple of 16,
+ *               16..16384; m 1..16
+ *   w_kv, w_z   [512][d] bf16 (output x input, 16-byte aligned)
+ *   w_ik        [128][512] bf16 (16-byte aligned)
+ *   rows        [B] int32 (device): the cache row of each new entry
+ *   main_codes/main_scales/idx_codes/idx_scales: the caches [B][n_cap][...]
+ *   swa, swa_slot  [B][128][512] window rows and [B] int32 slots, or both
+ *               NULL
+ *   cbar_out [B][512], ki_out [B][128], c_out [B][m][512]: optional float32
+ *               copies of C_bar, K^I and C (NULL to skip)
+ *   ws / ws_bytes: csa2_workspace_size(CSA2_OP_COMPRESS, B, m, d, NULL)
+ *               bytes, 256-byte aligned.
+ * Products are exact (bf16); sums are float32 in a fixed order. */
+csa2_status csa2_compress_append(const uint16_t *h, int32_t B, int32_t m,
+                                 int32_t d, const uint16_t *w_kv,
+                                 const uint16_t *w_z, const uint16_t *w_ik,
+                                 const int32_t *rows, uint8_t *main_codes,
+                                 uint8_t *main_scales, uint8_t *idx_codes,
+                                 uint8_t *idx_scales, int64_t n_cap,
+                                 uint8_t *swa, const int32_t *swa_slot,
+                                 float *cbar_out, float *ki_out, float *c_out,
+                                 void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Helpers. */
