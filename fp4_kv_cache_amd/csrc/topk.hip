@@ -12,7 +12,7 @@
 // score is known (the indexer writes it; tilemax_kernel computes it for a
 // plain score array).  Let M be the k-th largest tile maximum: k different
 // tiles each hold an element >= M, so the k-th largest score is >= M, and
-// every top-k element lies in a tile whose maximum is >= M.  One 512-thread
+// every top-k element lies in a tile whose maximum is >= M.  One 1024-thread
 // workgroup per row therefore (1) finds M by selecting the top-k tile
 // maxima, (2) lists, in order, every tile whose maximum is >= M (about k
 // tiles), and (3) selects the top-k among those tiles' scores only.  Rows
@@ -28,11 +28,16 @@
 namespace csa2 {
 namespace {
 
-constexpr int kNT = 512;                    // threads per row
-constexpr int kPer = 32;                    // keys per thread
+// A row's selection is a chain of dependent steps (loads, histograms,
+// scans), so a workgroup of 16 wavefronts with 16 keys per thread
+// finishes it sooner than fewer threads holding more keys each (measured:
+// 11.9 us at 1024 threads, 13.1 at 512, 17.7 at 256 for 32 rows of 32,768
+// scores).
+constexpr int kNT = 1024;                   // threads per row
+constexpr int kPer = 16;                    // keys per thread
 constexpr int kCap = kNT * kPer;            // 16384 keys per pass
 constexpr int kNB = 256;                    // bins per selection pass
-constexpr int kTileList = 4096;             // candidate tiles held in LDS
+constexpr int kTileList = 4000;             // candidate tiles held in LDS
 // Winners (k <= 2048) are staged in the histograms between selections.
 static_assert(kNT / 64 * kNB >= 2048, "staging room for 2048 winners");
 
@@ -415,10 +420,9 @@ __device__ __forceinline__ int gather_dispatch(
     return gather_candidates<2, HAS_IDS, KEYS>(sm, n_list, M, len, src);
   if (n_list <= kNT / 64 * 8 * 4)
     return gather_candidates<4, HAS_IDS, KEYS>(sm, n_list, M, len, src);
-  if (HAS_IDS || n_list <= kNT / 64 * 8 * 8)
-    return gather_candidates<8, HAS_IDS, KEYS>(sm, n_list, M, len, src);
-  return gather_candidates<HAS_IDS ? 8 : 16, HAS_IDS, KEYS>(sm, n_list, M,
-                                                           len, src);
+  // Longer lists take more rounds of 8 steps (16 steps per round would
+  // need more registers than 16 wavefronts per workgroup allow).
+  return gather_candidates<8, HAS_IDS, KEYS>(sm, n_list, M, len, src);
 }
 
 // One row b of a selection (the workgroup's whole work).
