@@ -110,6 +110,22 @@ def test_topk_all_equal_and_short_rows():
     assert np.all(out[1, 100:] == -1)
 
 
+@pytest.mark.parametrize("k", [512, 2048])
+def test_topk_pruning_overflows(k):
+    """Rows whose tile maxima all tie: every tile is listed, so a row of
+    200,000 scores overflows the tile list (6,250 tiles) and one of 100,000
+    the candidate store (3,125 tiles, 100,000 candidates); both fall back to
+    the streaming select, and the tie rule picks the lowest ids."""
+    ld = 200_000
+    sc = np.full((3, ld), 1.5, np.float32)
+    sc[2, 50_000:] = 2.0                    # the winners sit after the ties
+    nv = torch.tensor([ld, 100_000, ld], dtype=torch.int32, device=DEV)
+    out = csa2.topk(torch.from_numpy(sc).to(DEV), k, n_valid=nv).cpu().numpy()
+    assert out[0].tolist() == list(range(k))
+    assert out[1].tolist() == list(range(k))
+    assert out[2].tolist() == list(range(50_000, 50_000 + k))
+
+
 def test_topk_ids_and_block_expansion():
     rng = np.random.default_rng(9)
     B, ld, kb, blk = 2, 20000, 300, 8
