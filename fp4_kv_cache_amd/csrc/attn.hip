@@ -418,9 +418,9 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   uint32_t kinds[2] = {0u, 0u};
   const int32_t id01 = load_ids(p, b, ta, tb, wave, lane);
   int32_t idn = load_ids(p, b, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
-  // Loads are issued in the order they are consumed (wait counts retire in
-  // order): ids, rows of the first tile, the query, rows of the second.
-  load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
+  // The query does not depend on the ids, so its loads go out before the
+  // wait for them: the two latencies overlap (issue stops at that wait).
+  // The rows of the first and second tiles follow.
   // Q^T operand: head `head`, dims 32s + 8*q4 .. +7, converted to fp16.
   bf16x8_t qraw[16];
   {
@@ -429,6 +429,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) qraw[s] = qr[4 * s];
   }
+  load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
   load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
   f16x8_t qb[16];
 #pragma unroll
