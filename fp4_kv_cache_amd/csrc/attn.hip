@@ -490,19 +490,21 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   // tile's barrier) so that every store writes 16 contiguous bytes per lane
   // and whole 1 KB head rows per instruction.
   constexpr int kRowH = 512 + 8;                 // staged row, +16 B pad
+  // (The uniform choice of format is made once, outside the unrolled
+  // loops, so each is straight-line code.)
   uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + wave * 16 * kRowH;
+  uint2* srow = reinterpret_cast<uint2*>(stg + col * kRowH + 4 * q4);
+  if (final_out) {
 #pragma unroll
-  for (int blk = 0; blk < 32; ++blk) {
-    uint32_t lo, hi;
-    if (final_out) {
-      lo = pack_bf16(acc[blk][0] * inv, acc[blk][1] * inv);
-      hi = pack_bf16(acc[blk][2] * inv, acc[blk][3] * inv);
-    } else {
-      lo = f16x2_bits(f16x2_t{(_Float16)(acc[blk][0] * inv), (_Float16)(acc[blk][1] * inv)});
-      hi = f16x2_bits(f16x2_t{(_Float16)(acc[blk][2] * inv), (_Float16)(acc[blk][3] * inv)});
-    }
-    *reinterpret_cast<uint2*>(stg + col * kRowH + 16 * blk + 4 * q4) =
-        make_uint2(lo, hi);
+    for (int blk = 0; blk < 32; ++blk)
+      srow[4 * blk] = make_uint2(pack_bf16(acc[blk][0] * inv, acc[blk][1] * inv),
+                                 pack_bf16(acc[blk][2] * inv, acc[blk][3] * inv));
+  } else {
+#pragma unroll
+    for (int blk = 0; blk < 32; ++blk)
+      srow[4 * blk] = make_uint2(
+          f16x2_bits(f16x2_t{(_Float16)(acc[blk][0] * inv), (_Float16)(acc[blk][1] * inv)}),
+          f16x2_bits(f16x2_t{(_Float16)(acc[blk][2] * inv), (_Float16)(acc[blk][3] * inv)}));
   }
   __syncthreads();
   const int64_t row0 = final_out
