@@ -194,27 +194,45 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
                                               int quarter, int g,
                                               _Float16* buf, int32_t* valid) {
   uint32_t kd[8][4];
+  // The slot kinds are the same in every lane.  A wavefront whose 8 slots
+  // are all chosen entries or all window rows (every tile but the one
+  // holding slot k, when the ids are valid and the window is full) takes
+  // one straight-line path; others decide per slot.
+  auto main_slot = [&](int e) {
+    // (s, s) in fp16 from the E4M3 scale byte duplicated into two lanes.
+    const uint32_t sb = (raw.c[e] >> (8 * ((g >> 1) & 3))) & 0xFFu;
+    const f16x2_t ss = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+        sb * 0x101u, 1.0f, false);
+    const uint32_t cw = raw.a[e];
+    kd[e][0] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ss);
+    kd[e][1] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ss);
+    kd[e][2] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * ss);
+    kd[e][3] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss);
+  };
+  auto window_slot = [&](int e) {
+    kd[e][0] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.a[e], 1.0f, false));
+    kd[e][1] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.a[e], 1.0f, true));
+    kd[e][2] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.c[e], 1.0f, false));
+    kd[e][3] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.c[e], 1.0f, true));
+  };
+  if (kinds == 0x5555u) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t kind = (kinds >> (2 * e)) & 3u;
-    if (kind == 1) {
-      // (s, s) in fp16 from the E4M3 scale byte duplicated into two lanes.
-      const uint32_t sb = (raw.c[e] >> (8 * ((g >> 1) & 3))) & 0xFFu;
-      const f16x2_t ss = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-          sb * 0x101u, 1.0f, false);
-      const uint32_t cw = raw.a[e];
-      kd[e][0] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ss);
-      kd[e][1] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ss);
-      kd[e][2] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * ss);
-      kd[e][3] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss);
-    } else if (kind == 2) {
-      kd[e][0] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.a[e], 1.0f, false));
-      kd[e][1] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.a[e], 1.0f, true));
-      kd[e][2] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.c[e], 1.0f, false));
-      kd[e][3] = f16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw.c[e], 1.0f, true));
-    } else {
+    for (int e = 0; e < 8; ++e) main_slot(e);
+  } else if (kinds == 0xAAAAu) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kd[e][i] = 0;
+    for (int e = 0; e < 8; ++e) window_slot(e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t kind = (kinds >> (2 * e)) & 3u;
+      if (kind == 1) {
+        main_slot(e);
+      } else if (kind == 2) {
+        window_slot(e);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kd[e][i] = 0;
+      }
     }
   }
   // Key-major rows: slot j, dims 8g .. 8g+7.
