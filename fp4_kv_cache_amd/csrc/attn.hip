@@ -434,11 +434,21 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   const int tb = t0 + 1 < t1 ? t0 + 1 : ta;
   Raw raw[2];
   uint32_t kinds[2] = {0u, 0u};
+  // The accumulators are zeroed before any load is issued: zeroing them
+  // after the loads would have to wait for every load still in flight
+  // (their registers may be reused), stalling on the second tile's rows.
+  TileState st;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -__builtin_inff();
+  st.l_run = 0.0f;
   const int32_t id01 = load_ids(p, b, ta, tb, wave, lane);
   int32_t idn = load_ids(p, b, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
   // The query does not depend on the ids, so its loads go out before the
   // wait for them: the two latencies overlap (issue stops at that wait).
-  // The rows of the first and second tiles follow.
+  // The rows of the first tile follow; those of the second (needed only at
+  // the end of the first tile) are issued once the first is in LDS, so the
+  // registers they land in are not wanted by the accumulators meanwhile.
   // Q^T operand: head `head`, dims 32s + 8*q4 .. +7, converted to fp16.
   bf16x8_t qraw[16];
   {
@@ -448,19 +458,20 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
     for (int s = 0; s < 16; ++s) qraw[s] = qr[4 * s];
   }
   load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
-  load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
   f16x8_t qb[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s)
 #pragma unroll
     for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)(float)qraw[s][j];
-  TileState st;
+  // Keep the conversion here, where it runs while the first tile's rows
+  // are in flight (left to itself the compiler moves it to the first
+  // product, where nothing overlaps it).  The empty statement only marks
+  // each converted operand as used at this point.
 #pragma unroll
-  for (int i = 0; i < 32; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m_run = -__builtin_inff();
-  st.l_run = 0.0f;
+  for (int s = 0; s < 16; ++s) asm volatile("" : : "v"(qb[s]));
 
   if (t0 < t1) dequant_store(raw[0], kinds[0], wave, lane, bufs, valid_base);
+  load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
   __syncthreads();
 
   for (int t = t0; t < t1; t += 2) {
