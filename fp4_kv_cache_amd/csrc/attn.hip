@@ -380,17 +380,24 @@ __device__ __forceinline__ void tile_step(
   // O^T += V^T P^T.
   {
     constexpr int kAhead = 4;
+    // vs_phys(16 blk + col) = 16 blk + (col ^ x) with x = (2 blk + col/8) & 7,
+    // which repeats every 4 blocks: four per-lane bases plus a constant
+    // 256-byte step per block (an immediate offset of the read).
     const _Float16* v0 = vs + q4 * (512 * 8);
+    const _Float16* vb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      vb[j] = v0 + (col ^ ((2 * j + (col >> 3)) & 7)) * 8;
     f16x8_t va[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i)
-      va[i] = *reinterpret_cast<const f16x8_t*>(v0 + vs_phys(16 * i + col) * 8);
+      va[i] = *reinterpret_cast<const f16x8_t*>(vb[i & 3] + 128 * i);
 #pragma unroll
     for (int blk = 0; blk < 32; ++blk) {
       const f16x8_t c = va[blk % kAhead];
       if (blk + kAhead < 32)
         va[blk % kAhead] = *reinterpret_cast<const f16x8_t*>(
-            v0 + vs_phys(16 * (blk + kAhead) + col) * 8);
+            vb[(blk + kAhead) & 3] + 128 * (blk + kAhead));
       st.acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c, pb, st.acc[blk], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
