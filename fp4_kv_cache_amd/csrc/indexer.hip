@@ -230,13 +230,18 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) qa[s] = qrow[s];
   }
-  // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
-  float wr[16];
+  // Weights of the 16 output rows a lane holds, head 8a + 4*half + r, for
+  // both lane halves: wavefront-uniform, so they stay in scalar registers
+  // (16 vector registers fewer keeps the kernel at 4 wavefronts per SIMD,
+  // which lets a 32-sequence scan start every wavefront at once).
+  float wlo[16], whi[16];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      wr[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 * half + r];
+    for (int r = 0; r < 4; ++r) {
+      wlo[4 * a + r] = w[b * kIdxHeads + 8 * a + r];
+      whi[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 + r];
+    }
 
   RawKey<KEYFMT> buf[D + 1];
 #pragma unroll
@@ -272,14 +277,25 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       }
       // ReLU as an integer max on the float bits (negatives and -0 go to
       // +0; the dots are finite), weights, and the head sum in two chains.
-      float p0 = 0.0f, p1 = 0.0f;
+      // Both halves' weighted sums are formed (a scalar weight per fused
+      // multiply-add) and each lane keeps its own half's.
+      float p0 = 0.0f, p1 = 0.0f, h0 = 0.0f, h1 = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
-        p0 += wr[j] * __int_as_float(max(__float_as_int(acc[j]), 0));
-        p1 += wr[j + 1] * __int_as_float(max(__float_as_int(acc[j + 1]), 0));
+        const float r0 = __int_as_float(max(__float_as_int(acc[j]), 0));
+        const float r1 = __int_as_float(max(__float_as_int(acc[j + 1]), 0));
+        p0 += wlo[j] * r0;
+        p1 += wlo[j + 1] * r1;
+        h0 += whi[j] * r0;
+        h1 += whi[j + 1] * r1;
       }
-      // Fold the lane halves (dims 0-63 and 64-127 of the same entry):
-      // the swap gives every lane both halves, added in the same order.
+      if (half) {
+        p0 = h0;
+        p1 = h1;
+      }
+      // Fold the lane halves (the two halves hold different heads of the
+      // same entry): the swap gives every lane both halves' partial head
+      // sums, added in the same order.
       const auto hv = __builtin_amdgcn_permlane32_swap(
           __float_as_uint(p0 + p1), __float_as_uint(p0 + p1), false, false);
       const float sum = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
