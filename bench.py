@@ -124,7 +124,10 @@ def time_steps(step, args, R, out, ids):
     """Eager and HIP-graph time per step of `step(i)` (i picks the cache
     replica).  The graph holds one step per replica (R steps) and is
     replayed until at least K steps have run; a replay must reproduce the
-    eager result bit for bit."""
+    eager result bit for bit.  After the timed region, further replays are
+    timed one by one with events for the spread (p10 / p50 / p90 of the time
+    per step within a replay)."""
+    import numpy as np
     import torch
     for i in range(args.warmup):
         step(i)
@@ -135,7 +138,7 @@ def time_steps(step, args, R, out, ids):
     torch.cuda.synchronize()
     eager_s = (time.perf_counter() - t0) / args.steps
     if args.no_graph:
-        return eager_s, None, args.steps
+        return eager_s, None, args.steps, None
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -157,6 +160,17 @@ def time_steps(step, args, R, out, ids):
         g.replay()
     torch.cuda.synchronize()
     graph_s = (time.perf_counter() - t0) / steps_run
+    per_step = []
+    for _ in range(max(10, min(reps_needed, 50))):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        per_step.append(e0.elapsed_time(e1) * 1e3 / R)
+    spread = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
+    spread.update(replays=len(per_step), steps_per_replay=R)
     step(R - 1)
     torch.cuda.synchronize()
     e_out, e_ids = out.clone(), ids.clone()
@@ -165,7 +179,7 @@ def time_steps(step, args, R, out, ids):
     assert torch.equal(out.view(torch.int16), e_out.view(torch.int16))
     assert torch.equal(ids, e_ids)
     del g
-    return eager_s, graph_s, steps_run
+    return eager_s, graph_s, steps_run, spread
 
 
 def run_gpu(args, wl):
@@ -333,7 +347,8 @@ def run_pmc_pass(args, wl):
     the bf16 query, then M with the MXFP4 query (the roofline kernels, same
     arguments as the timed ones), then 4 copies
     y = x * 1 over COPY_ELEMS float32 (a kernel whose HBM bytes are known:
-    4 * COPY_ELEMS read and written)."""
+    4 * COPY_ELEMS read and written), then M eager decode steps with the
+    bf16 query (the counters of the attention, select and merge kernels)."""
     import torch
     from fp4_kv_cache_amd import csa2, workload
 
@@ -359,7 +374,19 @@ def run_pmc_pass(args, wl):
     for _ in range(4):
         torch.mul(x, 1.0, out=y)
     torch.cuda.synchronize()
+    del x, y
+    if not wl.pool:
+        out = torch.empty((wl.B, 64, 512), dtype=torch.bfloat16, device=dev)
+        ids = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
+        ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, wl.B, wl.n,
+                                                wl.k, None), dev)
+        for i in range(M):
+            csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
+                                    st.swa[0], st.n_swa, wl.k, st.scale,
+                                    out=out, topk_out=ids, ws=ws)
+        torch.cuda.synchronize()
     print(json.dumps({"pmc_pass": True, "indexer_launches": M,
+                      "decode_steps": 0 if wl.pool else M,
                       "indexer_algorithmic_bytes": {
                           q: indexer_bytes(wl, q) for q in ("bf16", "mxfp4")},
                       "copy_bytes_each_way": 4 * COPY_ELEMS}))
@@ -440,7 +467,7 @@ def main():
                  else "indexer_kernel<0, *, Q> (MXFP4 scan)")
 
     def summary(query):
-        eager_s, graph_s, steps_run = g["timing"][query]
+        eager_s, graph_s, steps_run, spread = g["timing"][query]
         step_s = graph_s if graph_s is not None else eager_s
         idx_alg = indexer_bytes(wl, query)
         achieved = idx_alg / g["t_idx"][query] / 1e9
@@ -448,7 +475,7 @@ def main():
         qf = "true" if query == "mxfp4" else "false"
         return dict(
             step_s=step_s, eager_s=eager_s, graph_s=graph_s,
-            steps_run=steps_run, per_call=per_call,
+            steps_run=steps_run, per_call=per_call, spread=spread,
             roofline={"bound": "hbm", "achieved": achieved,
                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": achieved / HBM_PEAK_GBS,
@@ -492,6 +519,7 @@ def main():
                        "topk": g["t_topk"] * 1e6,
                        "attention": g["t_attn"] * 1e6},
         "eager_ms_per_step": head["eager_s"] * 1e3,
+        "graph_step_us_spread": head["spread"],
         "variants": {f"indexer_query_{other}": {
             "value": wl.B / alt["step_s"], "ms_per_step": alt["step_s"] * 1e3,
             "roofline": alt["roofline"]}},

@@ -19,7 +19,8 @@
 // exactly to fp16 and written to LDS twice: key-major for S^T = K Q^T and,
 // through a register transpose, slot-grouped for O^T = V^T P^T, so both
 // products run on v_mfma_f32_16x16x32_f16 with all operands read as 16-byte
-// LDS vectors (XOR-swizzled, bank-conflict free).
+// LDS vectors, bank-conflict free (key-major rows padded by 32 bytes, the
+// slot-grouped layout XOR-swizzled).
 //
 // Why fp16: an E2M1 value times an E4M3 scale has at most 6 significant
 // bits and lies in [2^-10, 2688], so it is exact in fp16, and the scale
@@ -45,7 +46,11 @@ namespace csa2 {
 namespace {
 
 constexpr int kTile = 32;                   // key slots per tile
-constexpr int kKtStride = 520;              // fp16 per Kt row (+16 B pad)
+// fp16 per Kt row: 1024 bytes + 32 bytes of padding.  With a 16-byte pad
+// the logit operand reads (lane (c, q4) at row c, chunk q4 + 4s) take two
+// LDS cycles per 16 lanes on gfx950 (measured: 1.66x the time of
+// contiguous reads); with 32 bytes they take one.
+constexpr int kKtStride = 528;
 constexpr int kKtElems = kTile * kKtStride;
 constexpr int kVsElems = 4 * 512 * 8;
 constexpr int kBufElems = kKtElems + kVsElems;
