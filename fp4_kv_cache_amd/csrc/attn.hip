@@ -563,34 +563,34 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   }
 }
 
-// Merge of split partials: one thread per (sequence, head, 8 dims).
-// o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - M).  Every load is
-// issued before any is used (at most kMaxSplits partials).
+// Merge of split partials: one wavefront per (sequence, head), lane d8
+// merging dims 8*d8 .. 8*d8+7.  o = sum_s w_s o_s / sum_s w_s with
+// w_s = l_s 2^(m_s - M).  The split count S is a template parameter, so the
+// loads are straight-line code, all issued before any is used; the splits'
+// maxima and sums are wavefront-uniform and come through scalar loads.
 constexpr int kMaxSplits = 16;
 
+template <int S>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
-    int splits, int B, uint16_t* __restrict__ out, AttnEpilogue epi) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)B * kHeads * 64) return;
-  const int d8 = (int)(t & 63);
-  const int64_t bh = t >> 6;
+    int B, uint16_t* __restrict__ out, AttnEpilogue epi) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t bh = (int64_t)blockIdx.x * 4 + wave;
+  if (bh >= (int64_t)B * kHeads) return;       // wavefront-uniform
+  const int d8 = threadIdx.x & 63;
   const int head = (int)(bh % kHeads);
   const int64_t b = bh / kHeads;
-  float2 ml[kMaxSplits];
-  u32x4 v[kMaxSplits];
+  float2 ml[S];
+  u32x4 v[S];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < splits) {
-      const int64_t ps = (b * splits + s) * kHeads + head;
-      ml[s] = *reinterpret_cast<const float2*>(part_ml + ps * 2);
-      v[s] = *reinterpret_cast<const u32x4*>(part_o + ps * 512 + 8 * d8);
-    }
+  for (int s = 0; s < S; ++s) {
+    const int64_t ps = (b * S + s) * kHeads + head;
+    ml[s] = *reinterpret_cast<const float2*>(part_ml + ps * 2);
+    v[s] = *reinterpret_cast<const u32x4*>(part_o + ps * 512 + 8 * d8);
   }
   float M = -__builtin_inff();
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
-    if (s < splits) M = fmaxf(M, ml[s].x);
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s].x);
   // A sink logit (log2 units here) joins the denominator once; the
   // reference point covers it too.
   const float z = epi.sink != nullptr ? epi.sink[head] * kLog2e
@@ -600,17 +600,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   float L = z == -__builtin_inff() ? 0.0f : exp2f(z - mref);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < splits) {
-      const float wgt = ml[s].x == -__builtin_inff()
-                            ? 0.0f : ml[s].y * exp2f(ml[s].x - mref);
-      L += wgt;
+  for (int s = 0; s < S; ++s) {
+    const float wgt = ml[s].x == -__builtin_inff()
+                          ? 0.0f : ml[s].y * exp2f(ml[s].x - mref);
+    L += wgt;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f16x2_t h = bits_f16x2(v[s][i]);
-        o[2 * i] += wgt * (float)h[0];
-        o[2 * i + 1] += wgt * (float)h[1];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t h = bits_f16x2(v[s][i]);
+      o[2 * i] += wgt * (float)h[0];
+      o[2 * i + 1] += wgt * (float)h[1];
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -628,6 +626,23 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = pack_bf16(o[2 * i] * inv, o[2 * i + 1] * inv);
   *reinterpret_cast<u32x4*>(out + bh * 512 + 8 * d8) = w;
+}
+
+template <int S>
+hipError_t launch_combine(const uint16_t* part_o, const float* part_ml,
+                          int splits, int B, uint16_t* out,
+                          const AttnEpilogue& epi, hipStream_t s) {
+  if constexpr (S <= kMaxSplits) {
+    if (splits != S)
+      return launch_combine<S + 1>(part_o, part_ml, splits, B, out, epi, s);
+    const int64_t waves = (int64_t)B * kHeads;
+    hipLaunchKernelGGL(attn_combine_kernel<S>,
+                       dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
+                       part_o, part_ml, B, out, epi);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;              // more splits than planned
+  }
 }
 
 }  // namespace
@@ -693,11 +708,7 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(256), kSmemBytes, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const int64_t threads = (int64_t)B * kHeads * 64;
-  hipLaunchKernelGGL(attn_combine_kernel,
-                     dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     a.part_o, a.part_ml, a.splits, B, out, epi);
-  return hipGetLastError();
+  return launch_combine<2>(a.part_o, a.part_ml, a.splits, B, out, epi, s);
 }
 
 }  // namespace csa2
