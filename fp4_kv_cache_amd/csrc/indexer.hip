@@ -145,7 +145,7 @@ template <bool SCALED> struct Depth<1, SCALED> {
 // QFP4: the query is MXFP4 planes (codes q[B][32][64], scales
 // q_scales[B][32][4]) instead of bf16 q[B][32][128].  BLK (with KEYS):
 // the block maxima are written too.
-template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false>
+template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false, bool CAND = false>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
@@ -174,15 +174,14 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int nt = (int)((n_rows - base + 31) >> 5) < T
                      ? (int)((n_rows - base + 31) >> 5) : T;
 
-  // Row (within the sequence) of every tile position this lane will read
-  // (candidate ids first, all in one round), with validity; invalid rows
-  // are clamped to row 0.
-  uint32_t row[T];
+  // Row (within the sequence) of every tile position this lane will read,
+  // with validity; invalid rows are clamped to row 0.  Candidate ids are
+  // loaded first, all in one round (one wait, not one per tile); without
+  // them the row of tile t is base + 32t + col, formed where it is used
+  // (8 registers fewer).
+  uint32_t crow_v[CAND ? T : 1];
   uint32_t vmask = 0;
-  int64_t ent[T];
-  if (cand) {
-    // Every id load is issued before any is used (one wait, not one per
-    // tile).
+  if constexpr (CAND) {
     int32_t cv[T];
     const int32_t* crow = cand + (int64_t)b * n_rows;
 #pragma unroll
@@ -191,19 +190,25 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       cv[t] = crow[i < n_rows ? i : n_rows - 1];
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) ent[t] = cv[t];
-  } else {
-#pragma unroll
-    for (int t = 0; t < T; ++t) ent[t] = base + 32 * t + col;
+    for (int t = 0; t < T; ++t) {
+      const int64_t i = base + 32 * t + col;
+      const int64_t e = cv[t];
+      const bool v = (i < n_rows) & (e >= 0) & (e < n);
+      vmask |= (v ? 1u : 0u) << t;
+      crow_v[t] = v ? (uint32_t)e : 0u;
+    }
   }
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int64_t i = base + 32 * t + col;
-    const int64_t e = ent[t];
-    const bool v = (i < n_rows) & (e >= 0) & (e < n);
-    vmask |= (v ? 1u : 0u) << t;
-    row[t] = v ? (uint32_t)e : 0u;
-  }
+  // Plain rows: valid below lim = min(n_rows, n); base < 2^24.
+  const uint32_t lim = (uint32_t)(n_rows < n ? n_rows : n);
+  const uint32_t r0 = (uint32_t)base + (uint32_t)col;
+  auto row_of = [&](int t) -> uint32_t {
+    if constexpr (CAND) return crow_v[t];
+    else return r0 + 32u * t < lim ? r0 + 32u * t : 0u;
+  };
+  auto valid = [&](int t) -> bool {
+    if constexpr (CAND) return (vmask >> t) & 1u;
+    else return r0 + 32u * t < lim;
+  };
 
   // A operand: head `col`, dims 64*half + 8*s .. +7 for step s (bf16), or
   // the head's MXFP4 codes for dims 64*half .. +63 and its two scale bytes
@@ -230,35 +235,30 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) qa[s] = qrow[s];
   }
-  // Weights of the 16 output rows a lane holds, head 8a + 4*half + r, for
-  // both lane halves: wavefront-uniform, so they stay in scalar registers
-  // (16 vector registers fewer keeps the kernel at 4 wavefronts per SIMD,
-  // which lets a 32-sequence scan start every wavefront at once).
-  float wlo[16], whi[16];
+  // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
+  float wr[16];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      wlo[4 * a + r] = w[b * kIdxHeads + 8 * a + r];
-      whi[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 + r];
-    }
+    for (int r = 0; r < 4; ++r)
+      wr[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 * half + r];
 
   RawKey<KEYFMT> buf[D + 1];
 #pragma unroll
   for (int t = 0; t < D; ++t)
-    load_key<KEYFMT, kScaledOp>(buf[t], seq_codes, seq_scales, row[t], half);
+    load_key<KEYFMT, kScaledOp>(buf[t], seq_codes, seq_scales, row_of(t), half);
   float total[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (t + D < T)
       load_key<KEYFMT, kScaledOp>(buf[(t + D) % (D + 1)], seq_codes,
-                                  seq_scales, row[t + D], half);
+                                  seq_scales, row_of(t + D), half);
     // MXFP4 keys: no branch around the tile -- a conditional block would
     // let the compiler sink this tile's loads into it (and serialise them);
     // tiles past the end compute on clamped rows and are masked out.  The
     // bf16 block keys (one tile of loads ahead) keep the per-tile test,
     // which schedules better there.
-    if (KEYFMT == 0 || (t < nt && base + 32 * t < (cand ? n_rows : n))) {
+    if (KEYFMT == 0 || (t < nt && base + 32 * t < (CAND ? n_rows : n))) {
       const RawKey<KEYFMT>& cur = buf[t % (D + 1)];
       f32x16 acc = {};
       if constexpr (kScaledOp) {
@@ -277,21 +277,11 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       }
       // ReLU as an integer max on the float bits (negatives and -0 go to
       // +0; the dots are finite), weights, and the head sum in two chains.
-      // Both halves' weighted sums are formed (a scalar weight per fused
-      // multiply-add) and each lane keeps its own half's.
-      float p0 = 0.0f, p1 = 0.0f, h0 = 0.0f, h1 = 0.0f;
+      float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
-        const float r0 = __int_as_float(max(__float_as_int(acc[j]), 0));
-        const float r1 = __int_as_float(max(__float_as_int(acc[j + 1]), 0));
-        p0 += wlo[j] * r0;
-        p1 += wlo[j + 1] * r1;
-        h0 += whi[j] * r0;
-        h1 += whi[j + 1] * r1;
-      }
-      if (half) {
-        p0 = h0;
-        p1 = h1;
+        p0 += wr[j] * __int_as_float(max(__float_as_int(acc[j]), 0));
+        p1 += wr[j + 1] * __int_as_float(max(__float_as_int(acc[j + 1]), 0));
       }
       // Fold the lane halves (the two halves hold different heads of the
       // same entry): the swap gives every lane both halves' partial head
@@ -299,7 +289,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       const auto hv = __builtin_amdgcn_permlane32_swap(
           __float_as_uint(p0 + p1), __float_as_uint(p0 + p1), false, false);
       const float sum = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
-      total[t] = (vmask & (1u << t)) ? sum : -__builtin_inff();
+      total[t] = valid(t) ? sum : -__builtin_inff();
     } else {
       total[t] = -__builtin_inff();
     }
@@ -363,6 +353,11 @@ void launch_one(dim3 grid, hipStream_t s, const void* k_codes,
                        dim3(256), 0, s, k_codes, k_scales, n_cap, n_entries,
                        cand, n_rows, iq.q, iq.q_scales, iq.w, scores, tmax,
                        bmax, btmax);
+  else if (cand)
+    hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4, false, true>),
+                       grid, dim3(256), 0, s, k_codes, k_scales, n_cap,
+                       n_entries, cand, n_rows, iq.q, iq.q_scales, iq.w,
+                       scores, tmax, bmax, btmax);
   else
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256),
                        0, s, k_codes, k_scales, n_cap, n_entries, cand,
