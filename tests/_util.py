@@ -46,3 +46,25 @@ def topk_set_ok(gpu_ids, ref_scores, k, ids=None):
     if np.any(sg < kth * (1 - GAP_TOL)):
         return False, "contains a clear loser"
     return True, f"near-tie (gap {gap:.3g})"
+
+
+def planned_splits(B, k):
+    """Workgroups per sequence the attention plans for B sequences and k
+    chosen entries (k + 128 slots in 32-slot tiles): about one per compute
+    unit, at least 3 tiles each with 16 or more sequences, at most 16, and
+    the same number of tiles in every split."""
+    n_tiles = (k + 128 + 31) // 32
+    s = (256 + B - 1) // B
+    max_s = (n_tiles + 2) // 3 if B >= 16 else n_tiles
+    s = max(1, min(s, max_s, 16))
+    tps = -(-n_tiles // s)
+    return -(-n_tiles // tps)
+
+
+def split_parts_bytes(B, S):
+    """Workspace of S split partials: fp16 outputs [B][S][64][512] and
+    float32 (max, sum) [B][S][64][2], each 256-byte aligned; none for S = 1."""
+    if S <= 1:
+        return 0
+    a = lambda x: (x + 255) & ~255
+    return a(B * S * 64 * 512 * 2) + a(B * S * 64 * 2 * 4)
