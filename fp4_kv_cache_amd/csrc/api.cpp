@@ -61,7 +61,7 @@ struct DecodeLayout {
   bool pool;
   int64_t nb = 0, n_cand = 0;
   int kb = 0;
-  size_t off_scores = 0, off_tmax = 0, off_nblk = 0, off_bscores = 0,
+  size_t off_scores = 0, off_tmax = 0, off_bscores = 0,
          off_pool = 0, off_pscores = 0, off_attn = 0, total = 0;
 };
 
@@ -85,8 +85,6 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     L.kb = (int)std::min<int64_t>(pool->n_blocks_keep, L.nb);
     if (L.kb < 1) L.kb = 1;
     L.n_cand = (int64_t)L.kb * pool->block;
-    L.off_nblk = off;
-    off += align256((size_t)B * 4);
     L.off_bscores = off;
     off += align256((size_t)B * round32(L.nb) * 4);
     L.off_pool = off;
@@ -538,18 +536,18 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
                                 nullptr, topk_out, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
   } else {
-    int32_t* nblk = reinterpret_cast<int32_t*>(base + L.off_nblk);
     float* bscores = reinterpret_cast<float*>(base + L.off_bscores);
     int32_t* pool_ids = reinterpret_cast<int32_t*>(base + L.off_pool);
     float* pscores = reinterpret_cast<float*>(base + L.off_pscores);
-    e = csa2::launch_nblocks(kv->n_entries, B, pool->block, nblk, s);
-    if (e != hipSuccess) return hip_fail(e, "block count launch");
+    // Blocks of `block` entries: sequence b has ceil(n_entries[b] / block)
+    // of them, which the scan and the select work out themselves.
     e = csa2::launch_indexer(CSA2_KEYS_BF16, kv->block_keys, nullptr, L.nb,
-                             nblk, nullptr, L.nb, iq, B, bscores, s, tmax);
+                             kv->n_entries, nullptr, L.nb, iq, B, bscores, s,
+                             tmax, nullptr, nullptr, pool->block);
     if (e != hipSuccess) return hip_fail(e, "block indexer launch");
-    e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb, nblk,
-                                nullptr, B, L.kb, pool->block, kv->n_entries,
-                                pool_ids, s);
+    e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb,
+                                kv->n_entries, nullptr, B, L.kb, pool->block,
+                                kv->n_entries, pool_ids, s, pool->block);
     if (e != hipSuccess) return hip_fail(e, "block top-k launch");
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, pool_ids, L.n_cand,

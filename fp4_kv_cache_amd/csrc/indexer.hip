@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ q_in, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ w, float* __restrict__ scores,
     uint32_t* __restrict__ tmax, uint32_t* __restrict__ bmax,
-    uint32_t* __restrict__ btmax) {
+    uint32_t* __restrict__ btmax, int n_div) {
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int D = Depth<KEYFMT, kScaledOp>::value;
   constexpr int T = kTilesPerWave;
@@ -165,8 +165,11 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int64_t base =
       ((int64_t)blockIdx.x * kWaves + wave) * (kTilesPerWave * 32);
   if (base >= n_rows) return;                  // wave-uniform; no barriers
-  int64_t n = n_entries[b];
-  n = n < 0 ? 0 : (n > n_cap ? n_cap : n);     // never past the cache
+  // Valid rows: ceil(n_entries[b] / n_div) (n_div > 1: rows are blocks of
+  // n_div entries), never past the cache.
+  const int32_t ne = n_entries[b];
+  int64_t n = ne <= 0 ? 0 : ((int64_t)ne + n_div - 1) / n_div;
+  n = n > n_cap ? n_cap : n;
   const void* seq_codes = static_cast<const uint8_t*>(k_codes) +
                           (int64_t)b * n_cap * (KEYFMT == 0 ? 64 : 256);
   const uint8_t* seq_scales =
@@ -347,37 +350,37 @@ void launch_one(dim3 grid, hipStream_t s, const void* k_codes,
                 const uint8_t* k_scales, int64_t n_cap,
                 const int32_t* n_entries, const int32_t* cand, int64_t n_rows,
                 const IndexQuery& iq, float* scores, uint32_t* tmax,
-                uint32_t* bmax, uint32_t* btmax) {
+                uint32_t* bmax, uint32_t* btmax, int n_div) {
   if (KEYS && KEYFMT == 0 && !QFP4 && bmax)
     hipLaunchKernelGGL((indexer_kernel<0, true, false, true>), grid,
                        dim3(256), 0, s, k_codes, k_scales, n_cap, n_entries,
                        cand, n_rows, iq.q, iq.q_scales, iq.w, scores, tmax,
-                       bmax, btmax);
+                       bmax, btmax, n_div);
   else if (cand)
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4, false, true>),
                        grid, dim3(256), 0, s, k_codes, k_scales, n_cap,
                        n_entries, cand, n_rows, iq.q, iq.q_scales, iq.w,
-                       scores, tmax, bmax, btmax);
+                       scores, tmax, bmax, btmax, n_div);
   else
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256),
                        0, s, k_codes, k_scales, n_cap, n_entries, cand,
                        n_rows, iq.q, iq.q_scales, iq.w, scores, tmax, bmax,
-                       btmax);
+                       btmax, n_div);
 }
 template <int KEYFMT, bool KEYS>
 void launch_q(dim3 grid, hipStream_t s, const void* k_codes,
               const uint8_t* k_scales, int64_t n_cap, const int32_t* n_entries,
               const int32_t* cand, int64_t n_rows, const IndexQuery& iq,
               float* scores, uint32_t* tmax, uint32_t* bmax,
-              uint32_t* btmax) {
+              uint32_t* btmax, int n_div) {
   if (iq.q_scales)
     launch_one<KEYFMT, KEYS, true>(grid, s, k_codes, k_scales, n_cap,
                                    n_entries, cand, n_rows, iq, scores, tmax,
-                                   bmax, btmax);
+                                   bmax, btmax, n_div);
   else
     launch_one<KEYFMT, KEYS, false>(grid, s, k_codes, k_scales, n_cap,
                                     n_entries, cand, n_rows, iq, scores, tmax,
-                                    bmax, btmax);
+                                    bmax, btmax, n_div);
 }
 }  // namespace
 
@@ -386,8 +389,9 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const int32_t* n_entries, const int32_t* cand,
                           int64_t n_rows, const IndexQuery& iq, int B,
                           float* scores, hipStream_t s, uint32_t* tmax,
-                          uint32_t* bmax, uint32_t* btmax) {
+                          uint32_t* bmax, uint32_t* btmax, int n_div) {
   if (n_rows == 0 || B == 0) return hipSuccess;
+  if (n_div < 1) return hipErrorInvalidValue;
   // Block maxima: MXFP4 keys, bf16 query, all rows.
   if (bmax && (!tmax || cand || !btmax || keyfmt != 0 || iq.q_scales))
     return hipErrorInvalidValue;
@@ -395,16 +399,16 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                   (unsigned)B);
   if (keyfmt == 0 && tmax)
     launch_q<0, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                      n_rows, iq, scores, tmax, bmax, btmax);
+                      n_rows, iq, scores, tmax, bmax, btmax, n_div);
   else if (keyfmt == 0)
     launch_q<0, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                       n_rows, iq, scores, tmax, bmax, btmax);
+                       n_rows, iq, scores, tmax, bmax, btmax, n_div);
   else if (tmax)
     launch_q<1, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                      n_rows, iq, scores, tmax, bmax, btmax);
+                      n_rows, iq, scores, tmax, bmax, btmax, n_div);
   else
     launch_q<1, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
-                       n_rows, iq, scores, tmax, bmax, btmax);
+                       n_rows, iq, scores, tmax, bmax, btmax, n_div);
   return hipGetLastError();
 }
 

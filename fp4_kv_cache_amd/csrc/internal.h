@@ -19,15 +19,14 @@ hipError_t launch_unpack(int fmt, const uint8_t* codes, const uint8_t* scales,
 hipError_t launch_block_keys(const uint8_t* codes, const uint8_t* scales,
                              int64_t n_cap, const int32_t* n_entries, int B,
                              int block, uint16_t* keys, hipStream_t s);
-hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
-                          int32_t* nblk, hipStream_t s);
 
 // indexer.hip
 // Scores rows (all n_rows, or the n_rows candidate ids `cand`) into float
 // scores[B][n_rows].  With `tmax` (the decode path) it writes selection keys
 // (score_key, as uint32) instead, rows padded to a multiple of 32 entries
 // (scores[B][round_up(n_rows, 32)]), and each 32-row tile's largest key into
-// tmax[B][ceil(n_rows/32)].  With `bmax` (and `btmax`; all rows, no
+// tmax[B][ceil(n_rows/32)].  A row is valid below ceil(n_entries[b] / n_div)
+// (n_div > 1: rows are blocks of n_div entries).  With `bmax` (and `btmax`; all rows, no
 // candidates) also the 8-row block maxima bmax[B][round_up(nb, 32)], nb =
 // ceil(n_rows/8), and their 32-block maxima btmax[B][ceil(nb/32)].
 // The indexer query of every sequence: bf16 q[B][32][128] (q_scales null),
@@ -43,18 +42,20 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           int64_t n_rows, const IndexQuery& iq, int B,
                           float* scores, hipStream_t s,
                           uint32_t* tmax = nullptr, uint32_t* bmax = nullptr,
-                          uint32_t* btmax = nullptr);
+                          uint32_t* btmax = nullptr, int n_div = 1);
 
 // topk.hip
 // Exact per-row top-k (see topk.hip) of float scores (keys == false) or of
 // selection keys (keys == true); rows of n_cols entries at stride ld (keys:
 // ld a multiple of 32), ids (nullable) at stride n_cols; `tmax` (tile maxima
 // [B][ceil(n_cols/32)] in the same form, nullable) enables tile pruning.
+// A row's length is min(n_cols, ceil(n_valid[b] / valid_div)) when n_valid
+// is given.
 hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
                              int64_t ld, int64_t n_cols, const int32_t* n_valid,
                              const int32_t* ids, int B, int k, int block,
                              const int32_t* limit, int32_t* out,
-                             hipStream_t s);
+                             hipStream_t s, int valid_div = 1);
 
 // Two key selections (no ids) over the same B rows in one launch, side by
 // side: rows of r0 on workgroups 0..B-1, rows of r1 on B..2B-1.

@@ -121,15 +121,6 @@ __global__ void block_keys_kernel(const uint8_t* __restrict__ codes,
   keys[t] = out;
 }
 
-// Visible blocks per sequence: ceil(n_entries / block).
-__global__ void nblocks_kernel(const int32_t* __restrict__ n_entries, int B,
-                               int block, int32_t* __restrict__ nblk) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  const int32_t n = n_entries[b] > 0 ? n_entries[b] : 0;
-  nblk[b] = (n + block - 1) / block;
-}
-
 inline unsigned grid_for(int64_t n, int threads) {
   return (unsigned)((n + threads - 1) / threads);
 }
@@ -179,14 +170,6 @@ hipError_t launch_block_keys(const uint8_t* codes, const uint8_t* scales,
   hipLaunchKernelGGL(block_keys_kernel, dim3(grid_for(total, 256)), dim3(256),
                      0, s, codes, scales, n_cap, n_entries, nb, block, keys,
                      total);
-  return hipGetLastError();
-}
-
-hipError_t launch_nblocks(const int32_t* n_entries, int B, int block,
-                          int32_t* nblk, hipStream_t s) {
-  if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(nblocks_kernel, dim3((unsigned)((B + 255) / 256)),
-                     dim3(256), 0, s, n_entries, B, block, nblk);
   return hipGetLastError();
 }
 

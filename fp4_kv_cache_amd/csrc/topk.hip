@@ -206,6 +206,7 @@ struct RowArgs {
   int64_t ld;               // keys without ids: a multiple of 32
   int64_t n_cols;           // row length (<= ld); ids row stride
   const int32_t* n_valid;   // nullable
+  int valid_div;            // row length ceil(n_valid[b] / valid_div)
   const int32_t* ids;       // nullable
   int k;
   int block;
@@ -434,8 +435,9 @@ __device__ __forceinline__ void row_select_row(const RowArgs& a, int b) {
   for (int i = tid; i < kNT / 64 * kNB; i += kNT) (&sm.sel.hist[0][0])[i] = 0;
   int64_t len = a.n_cols;
   if (a.n_valid) {
-    const int64_t nv = a.n_valid[b];
-    len = nv < len ? (nv > 0 ? nv : 0) : len;
+    const int32_t v = a.n_valid[b];
+    const int64_t nv = v <= 0 ? 0 : ((int64_t)v + a.valid_div - 1) / a.valid_div;
+    len = nv < len ? nv : len;
   }
   const ScoreSrc<HAS_IDS, KEYS> from_scores{
       static_cast<const uint32_t*>(a.scores) + (int64_t)b * a.ld,
@@ -534,6 +536,7 @@ RowArgs row_args(const void* scores, const void* tmax, int64_t ld,
   a.ld = ld;
   a.n_cols = n_cols;
   a.n_valid = n_valid;
+  a.valid_div = 1;
   a.ids = ids;
   a.k = k;
   a.block = block;
@@ -546,11 +549,13 @@ hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
                              int64_t ld, int64_t n_cols,
                              const int32_t* n_valid, const int32_t* ids, int B,
                              int k, int block, const int32_t* limit,
-                             int32_t* out, hipStream_t s) {
+                             int32_t* out, hipStream_t s, int valid_div) {
   if (B == 0) return hipSuccess;
-  if (n_cols > ld || (keys && !ids && (ld & 31))) return hipErrorInvalidValue;
-  const RowArgs a = row_args(scores, tmax, ld, n_cols, n_valid, ids, k, block,
-                             limit, out);
+  if (n_cols > ld || (keys && !ids && (ld & 31)) || valid_div < 1)
+    return hipErrorInvalidValue;
+  RowArgs a = row_args(scores, tmax, ld, n_cols, n_valid, ids, k, block,
+                       limit, out);
+  a.valid_div = valid_div;
   if (ids) return keys ? launch_rows<true, true>(a, B, s)
                        : launch_rows<true, false>(a, B, s);
   return keys ? launch_rows<false, true>(a, B, s)
