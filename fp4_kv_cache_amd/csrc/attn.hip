@@ -11,10 +11,12 @@
 // (the cache is dequantised before attention; FP4 is storage only);
 // "DeepSeek-V4.1-Flash, 2. Architecture" section 2.4.4.
 //
-// gfx950 mapping.  A workgroup of 4 wavefronts owns one sequence and a
+// gfx950 mapping.  A workgroup of 8 wavefronts owns one sequence and a
 // contiguous range of key slots (slots 0..k-1 are the chosen main entries,
-// k..k+127 the window rows); wavefront w owns heads 16w..16w+15 with its
-// queries resident in VGPRs.  Key tiles of 32 slots are gathered straight
+// k..k+127 the window rows).  Wavefronts 0..3 do the products (wavefront w:
+// heads 16w..16w+15, queries and accumulators resident in registers);
+// wavefronts 4..7 gather and dequantise the next tile meanwhile, one of each
+// kind per SIMD, meeting at one barrier per tile.  Key tiles of 32 slots are gathered straight
 // from HBM (one 256-byte code row per wavefront instruction), dequantised
 // exactly to fp16 and written to LDS twice: key-major for S^T = K Q^T and,
 // through a register transpose, slot-grouped for O^T = V^T P^T, so both
@@ -289,26 +291,34 @@ struct TileState {
   float l_run;             // running sum of this lane's weights
 };
 
-// One key tile of the split.  P = parity of the tile within the split: LDS
-// buffer P holds its dequantised keys, raw[P] is free again (its rows went
-// to LDS at the end of the previous step) and receives the rows of tile
-// t+2, and raw[P^1] (rows of t+1) is dequantised into buffer P^1 once the
-// products have read buffer P.
+// Producer side of one key tile (wavefronts 4..7, `quarter` = wavefront - 4).
+// P = parity of the tile within the split: raw[P] is free again (its rows
+// went to LDS in the previous step) and receives the rows of tile t+2, with
+// the ids of t+3 issued first (wait counts retire in order, so reading them
+// next step does not wait for these rows); then raw[P^1] (rows of t+1) is
+// dequantised into LDS buffer P^1 while the math wavefronts read buffer P.
 template <int P>
-__device__ __forceinline__ void tile_step(
-    const AttnArgs& p, const Bases& bs, int b, int t, int t1, int wave,
-    int lane, int nswa, int col, int q4, _Float16* bufs, int32_t* valid_base,
-    const f16x8_t (&qb)[16], Raw (&raw)[2], uint32_t (&kinds)[2],
-    int32_t& idn, TileState& st) {
-  // The ids of t+3 are issued before the rows of t+2: wait counts retire in
-  // order, so reading them next step does not wait for these rows.
+__device__ __forceinline__ void tile_produce(
+    const AttnArgs& p, const Bases& bs, int b, int t, int t1, int quarter,
+    int lane, int nswa, _Float16* bufs, int32_t* valid_base, Raw (&raw)[2],
+    uint32_t (&kinds)[2], int32_t& idn) {
   const int tl = t1 - 1;
   const int t3 = t + 3 < t1 ? t + 3 : tl;
-  const int32_t id3 = load_ids(p, b, t3, t3, wave, lane);
-  load_rows(p, bs, t + 2 < t1 ? t + 2 : tl, wave, lane, nswa, idn, 0, raw[P],
-            kinds[P]);
+  const int32_t id3 = load_ids(p, b, t3, t3, quarter, lane);
+  load_rows(p, bs, t + 2 < t1 ? t + 2 : tl, quarter, lane, nswa, idn, 0,
+            raw[P], kinds[P]);
   idn = id3;
+  if (t + 1 < t1)
+    dequant_store(raw[P ^ 1], kinds[P ^ 1], quarter, lane,
+                  bufs + (P ^ 1) * kBufElems, valid_base + (P ^ 1) * kTile);
+}
 
+// Math side of one key tile (wavefronts 0..3): logits, online softmax and
+// the value products over LDS buffer P.
+template <int P>
+__device__ __forceinline__ void tile_math(
+    const AttnArgs& p, int col, int q4, const _Float16* bufs,
+    const int32_t* valid_base, const f16x8_t (&qb)[16], TileState& st) {
   const _Float16* kt = bufs + P * kBufElems;
   const _Float16* vs = kt + kKtElems;
   const int32_t* valid = valid_base + P * kTile;
@@ -320,7 +330,7 @@ __device__ __forceinline__ void tile_step(
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   {
     f32x4 s0b = {0.f, 0.f, 0.f, 0.f}, s1b = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kAhead = 3;
+    constexpr int kAhead = 2;
     const _Float16* k0 = kt + col * kKtStride + 8 * q4;
     const _Float16* k1 = k0 + 16 * kKtStride;
     f16x8_t a0[kAhead], a1[kAhead];
@@ -408,13 +418,9 @@ __device__ __forceinline__ void tile_step(
     }
   }
 
-  if (t + 1 < t1)
-    dequant_store(raw[P ^ 1], kinds[P ^ 1], wave, lane,
-                  bufs + (P ^ 1) * kBufElems, valid_base + (P ^ 1) * kTile);
-  __syncthreads();
 }
 
-__global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
+__global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   _Float16* bufs = reinterpret_cast<_Float16*>(smem_raw);
   int32_t* valid_base = reinterpret_cast<int32_t*>(smem_raw + 2 * kBufElems * 2);
@@ -422,7 +428,14 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   int b, split;
   if (!map_workgroup(blockIdx.x, p.B, p.splits, b, split)) return;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Wavefronts 0..3 are the math side (wavefront w: heads 16w..16w+15, its
+  // queries and accumulators in registers); 4..7 the producers (gather and
+  // dequantisation, producer q handling slot quarter q of every tile).  Each
+  // SIMD holds one of each, so the matrix work of one tile overlaps the
+  // gather and dequantisation of the next.
+  const bool is_math = wv < 4;
+  const int wave = wv & 3;
   const int col = lane & 15;          // head within the wave / row in A
   const int q4 = lane >> 4;           // k-slot group
   const int head = 16 * wave + col;
@@ -433,11 +446,11 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   int t1 = t0 + p.tiles_per_split;
   if (t1 > p.n_tiles) t1 = p.n_tiles;
 
-  // Gather pipeline: while tile t runs on the matrix cores, the rows of
-  // tiles t+1 and t+2 are in flight (a two-slot register ring, slot =
-  // parity of the tile within the split) and the ids of tile t+3 behind
-  // them.  Tile indices past the split are clamped to its last tile, so every
-  // load is unconditional and valid.
+  // Gather pipeline (producers): while tile t runs on the matrix cores, the
+  // rows of tiles t+1 and t+2 are in flight (a two-slot register ring, slot
+  // = parity of the tile within the split) and the ids of tile t+3 behind
+  // them.  Tile indices past the split are clamped to its last tile, so
+  // every load is unconditional and valid.
   const Bases bs{p.main_codes + (int64_t)b * p.n_cap * 256,
                  p.main_scales + (int64_t)b * p.n_cap * 32,
                  p.swa + (int64_t)b * kWindow * 512};
@@ -446,117 +459,128 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs p) {
   const int tb = t0 + 1 < t1 ? t0 + 1 : ta;
   Raw raw[2];
   uint32_t kinds[2] = {0u, 0u};
-  // The accumulators are zeroed before any load is issued: zeroing them
-  // after the loads would have to wait for every load still in flight
-  // (their registers may be reused), stalling on the second tile's rows.
+  int32_t idn = 0;
   TileState st;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m_run = -__builtin_inff();
-  st.l_run = 0.0f;
-  const int32_t id01 = load_ids(p, b, ta, tb, wave, lane);
-  int32_t idn = load_ids(p, b, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
-  // The query does not depend on the ids, so its loads go out before the
-  // wait for them: the two latencies overlap (issue stops at that wait).
-  // The rows of the first tile follow; those of the second (needed only at
-  // the end of the first tile) are issued once the first is in LDS, so the
-  // registers they land in are not wanted by the accumulators meanwhile.
-  // Q^T operand: head `head`, dims 32s + 8*q4 .. +7, converted to fp16.
-  bf16x8_t qraw[16];
-  {
+  f16x8_t qb[16];
+  if (is_math) {
+    // Q^T operand: head `head`, dims 32s + 8*q4 .. +7, converted to fp16;
+    // the accumulators are zeroed after the conversion (the raw query is
+    // dead by then).
+    bf16x8_t qraw[16];
     const bf16x8_t* qr = reinterpret_cast<const bf16x8_t*>(
         p.q + ((int64_t)b * kHeads + head) * 512 + 8 * q4);
 #pragma unroll
     for (int s = 0; s < 16; ++s) qraw[s] = qr[4 * s];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)(float)qraw[s][j];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) asm volatile("" : : "v"(qb[s]));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -__builtin_inff();
+    st.l_run = 0.0f;
+  } else {
+    // The rows of the first two tiles go out together (a producer holds no
+    // accumulators, so nothing else wants their registers); the first is
+    // dequantised into buffer 0.
+    const int32_t id01 = load_ids(p, b, ta, tb, wave, lane);
+    idn = load_ids(p, b, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
+    load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
+    load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
+    if (t0 < t1) dequant_store(raw[0], kinds[0], wave, lane, bufs, valid_base);
   }
-  load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
-  f16x8_t qb[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)(float)qraw[s][j];
-  // Keep the conversion here, where it runs while the first tile's rows
-  // are in flight (left to itself the compiler moves it to the first
-  // product, where nothing overlaps it).  The empty statement only marks
-  // each converted operand as used at this point.
-#pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" : : "v"(qb[s]));
-
-  if (t0 < t1) dequant_store(raw[0], kinds[0], wave, lane, bufs, valid_base);
-  load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
   __syncthreads();
 
-  for (int t = t0; t < t1; t += 2) {
-    tile_step<0>(p, bs, b, t, t1, wave, lane, nswa, col, q4, bufs, valid_base,
-                 qb, raw, kinds, idn, st);
-    if (t + 1 < t1)
-      tile_step<1>(p, bs, b, t + 1, t1, wave, lane, nswa, col, q4, bufs,
-                   valid_base, qb, raw, kinds, idn, st);
-  }
-  f32x4 (&acc)[32] = st.acc;
-  const float m_run = st.m_run;
-  const float l_run = st.l_run;
-
-  // Fold the running sums of the four lanes that share a head.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const bool final_out = p.splits == 1;
-  // A sink logit joins the denominator of the final output (a split's
-  // partial keeps its own sum; the merge adds the sink once).  With no key
-  // at all (m_run = -inf) the output is zero either way.
-  float den = l_tot;
-  if (final_out && p.epi.sink != nullptr)
-    den += exp2f(p.epi.sink[head] * kLog2e - m_run);
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  if (final_out && p.epi.pos != nullptr) {
-    // De-rotate dims 448..511 (blocks 28..31): this lane holds dims
-    // 16*blk + 4*q4 + r, pairs (r = 0, 1) and (r = 2, 3).
-    const int32_t t = p.epi.pos[b];
-#pragma unroll
-    for (int blk = 28; blk < 32; ++blk)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        float c, sn;
-        rope_cs(t, p.epi.rope_w[8 * (blk - 28) + 2 * q4 + r / 2], c, sn);
-        float x = acc[blk][r], y = acc[blk][r + 1];
-        rotate_pair(x, y, c, sn);
-        acc[blk][r] = x;
-        acc[blk][r + 1] = y;
+  // Each side runs its own loop (the producers' in-flight rows are not
+  // live in the math loop); both pass the same barriers, one per tile.
+  if (is_math) {
+    for (int t = t0; t < t1; t += 2) {
+      tile_math<0>(p, col, q4, bufs, valid_base, qb, st);
+      __syncthreads();
+      if (t + 1 < t1) {
+        tile_math<1>(p, col, q4, bufs, valid_base, qb, st);
+        __syncthreads();
       }
+    }
+  } else {
+    for (int t = t0; t < t1; t += 2) {
+      tile_produce<0>(p, bs, b, t, t1, wave, lane, nswa, bufs, valid_base,
+                      raw, kinds, idn);
+      __syncthreads();
+      if (t + 1 < t1) {
+        tile_produce<1>(p, bs, b, t + 1, t1, wave, lane, nswa, bufs,
+                        valid_base, raw, kinds, idn);
+        __syncthreads();
+      }
+    }
   }
-
+  const bool final_out = p.splits == 1;
   // The output (final bf16, or this split's fp16 partial normalised by its
   // own sum -- a convex combination of keys, so |value| <= 2688 fits fp16
   // with 11 significant bits) is staged through LDS (free after the last
   // tile's barrier) so that every store writes 16 contiguous bytes per lane
   // and whole 1 KB head rows per instruction.
   constexpr int kRowH = 512 + 8;                 // staged row, +16 B pad
-  // (The uniform choice of format is made once, outside the unrolled
-  // loops, so each is straight-line code.)
-  uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + wave * 16 * kRowH;
-  uint2* srow = reinterpret_cast<uint2*>(stg + col * kRowH + 4 * q4);
-  if (final_out) {
+  uint16_t* stg_all = reinterpret_cast<uint16_t*>(smem_raw);
+  float m_run = 0.0f, l_tot = 0.0f;
+  if (is_math) {
+    f32x4 (&acc)[32] = st.acc;
+    m_run = st.m_run;
+    // Fold the running sums of the four lanes that share a head.
+    l_tot = st.l_run + __shfl_xor(st.l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    // A sink logit joins the denominator of the final output (a split's
+    // partial keeps its own sum; the merge adds the sink once).  With no key
+    // at all (m_run = -inf) the output is zero either way.
+    float den = l_tot;
+    if (final_out && p.epi.sink != nullptr)
+      den += exp2f(p.epi.sink[head] * kLog2e - m_run);
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    if (final_out && p.epi.pos != nullptr) {
+      // De-rotate dims 448..511 (blocks 28..31): this lane holds dims
+      // 16*blk + 4*q4 + r, pairs (r = 0, 1) and (r = 2, 3).
+      const int32_t t = p.epi.pos[b];
 #pragma unroll
-    for (int blk = 0; blk < 32; ++blk)
-      srow[4 * blk] = make_uint2(pack_bf16(acc[blk][0] * inv, acc[blk][1] * inv),
-                                 pack_bf16(acc[blk][2] * inv, acc[blk][3] * inv));
-  } else {
+      for (int blk = 28; blk < 32; ++blk)
 #pragma unroll
-    for (int blk = 0; blk < 32; ++blk)
-      srow[4 * blk] = make_uint2(
-          f16x2_bits(f16x2_t{(_Float16)(acc[blk][0] * inv), (_Float16)(acc[blk][1] * inv)}),
-          f16x2_bits(f16x2_t{(_Float16)(acc[blk][2] * inv), (_Float16)(acc[blk][3] * inv)}));
+        for (int r = 0; r < 4; r += 2) {
+          float c, sn;
+          rope_cs(t, p.epi.rope_w[8 * (blk - 28) + 2 * q4 + r / 2], c, sn);
+          float x = acc[blk][r], y = acc[blk][r + 1];
+          rotate_pair(x, y, c, sn);
+          acc[blk][r] = x;
+          acc[blk][r + 1] = y;
+        }
+    }
+    // Head row h of the workgroup is staged at row h (the uniform choice of
+    // format is made once, outside the unrolled loops, so each is
+    // straight-line code).
+    uint2* srow = reinterpret_cast<uint2*>(stg_all + head * kRowH + 4 * q4);
+    if (final_out) {
+#pragma unroll
+      for (int blk = 0; blk < 32; ++blk)
+        srow[4 * blk] = make_uint2(pack_bf16(acc[blk][0] * inv, acc[blk][1] * inv),
+                                   pack_bf16(acc[blk][2] * inv, acc[blk][3] * inv));
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 32; ++blk)
+        srow[4 * blk] = make_uint2(
+            f16x2_bits(f16x2_t{(_Float16)(acc[blk][0] * inv), (_Float16)(acc[blk][1] * inv)}),
+            f16x2_bits(f16x2_t{(_Float16)(acc[blk][2] * inv), (_Float16)(acc[blk][3] * inv)}));
+    }
   }
   __syncthreads();
-  const int64_t row0 = final_out
-      ? ((int64_t)b * kHeads + 16 * wave)
-      : (((int64_t)b * p.splits + split) * kHeads + 16 * wave);
+  // All eight wavefronts store: wavefront w writes head rows 8w .. 8w+7.
+  const int64_t row0 = final_out ? (int64_t)b * kHeads
+                                 : ((int64_t)b * p.splits + split) * kHeads;
   uint16_t* dst = (final_out ? p.out : p.part_o) + row0 * 512 + 8 * lane;
 #pragma unroll
-  for (int h = 0; h < 16; ++h)
+  for (int h = 8 * wv; h < 8 * wv + 8; ++h)
     *reinterpret_cast<u32x4*>(dst + h * 512) =
-        *reinterpret_cast<const u32x4*>(stg + h * kRowH + 8 * lane);
-  if (!final_out && q4 == 0) {
+        *reinterpret_cast<const u32x4*>(stg_all + h * kRowH + 8 * lane);
+  if (is_math && !final_out && q4 == 0) {
     const int64_t ps = ((int64_t)b * p.splits + split) * kHeads + head;
     p.part_ml[ps * 2 + 0] = m_run;
     p.part_ml[ps * 2 + 1] = l_tot;
@@ -705,7 +729,7 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   }
   const int groups = (B + 7) / 8;
   const unsigned grid = (unsigned)(8 * groups * a.splits);
-  hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(256), kSmemBytes, s, a);
+  hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(512), kSmemBytes, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   return launch_combine<2>(a.part_o, a.part_ml, a.splits, B, out, epi, s);
