@@ -165,10 +165,15 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int64_t base =
       ((int64_t)blockIdx.x * kWaves + wave) * (kTilesPerWave * 32);
   if (base >= n_rows) return;                  // wave-uniform; no barriers
-  // Valid rows: ceil(n_entries[b] / n_div) (n_div > 1: rows are blocks of
-  // n_div entries), never past the cache.
+  // Valid rows: n_entries[b], or for bf16 block keys ceil(n_entries[b] /
+  // n_div) (rows are blocks of n_div entries; 32-bit unsigned, exact for
+  // these ranges), never past the cache.  The MXFP4 scan carries no
+  // division: it would sit before every wavefront's first load.
   const int32_t ne = n_entries[b];
-  int64_t n = ne <= 0 ? 0 : ((int64_t)ne + n_div - 1) / n_div;
+  int64_t n = ne <= 0 ? 0 : (int64_t)ne;
+  if constexpr (KEYFMT == 1)
+    if (ne > 0 && n_div > 1)
+      n = (int64_t)(((uint32_t)ne + (uint32_t)n_div - 1u) / (uint32_t)n_div);
   n = n > n_cap ? n_cap : n;
   const void* seq_codes = static_cast<const uint8_t*>(k_codes) +
                           (int64_t)b * n_cap * (KEYFMT == 0 ? 64 : 256);
@@ -391,7 +396,7 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           float* scores, hipStream_t s, uint32_t* tmax,
                           uint32_t* bmax, uint32_t* btmax, int n_div) {
   if (n_rows == 0 || B == 0) return hipSuccess;
-  if (n_div < 1) return hipErrorInvalidValue;
+  if (n_div < 1 || (n_div > 1 && keyfmt != 1)) return hipErrorInvalidValue;
   // Block maxima: MXFP4 keys, bf16 query, all rows.
   if (bmax && (!tmax || cand || !btmax || keyfmt != 0 || iq.q_scales))
     return hipErrorInvalidValue;

@@ -25,8 +25,9 @@ hipError_t launch_block_keys(const uint8_t* codes, const uint8_t* scales,
 // scores[B][n_rows].  With `tmax` (the decode path) it writes selection keys
 // (score_key, as uint32) instead, rows padded to a multiple of 32 entries
 // (scores[B][round_up(n_rows, 32)]), and each 32-row tile's largest key into
-// tmax[B][ceil(n_rows/32)].  A row is valid below ceil(n_entries[b] / n_div)
-// (n_div > 1: rows are blocks of n_div entries).  With `bmax` (and `btmax`; all rows, no
+// tmax[B][ceil(n_rows/32)].  A row is valid below n_entries[b], or for bf16
+// block keys below ceil(n_entries[b] / n_div) (rows are blocks of n_div
+// entries; n_div > 1 only with those keys).  With `bmax` (and `btmax`; all rows, no
 // candidates) also the 8-row block maxima bmax[B][round_up(nb, 32)], nb =
 // ceil(n_rows/8), and their 32-block maxima btmax[B][ceil(nb/32)].
 // The indexer query of every sequence: bf16 q[B][32][128] (q_scales null),
