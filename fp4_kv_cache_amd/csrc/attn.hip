@@ -16,13 +16,13 @@
 // k..k+127 the window rows).  Wavefronts 0..3 do the products (wavefront w:
 // heads 16w..16w+15, queries and accumulators resident in registers);
 // wavefronts 4..7 gather and dequantise the next tile meanwhile, one of each
-// kind per SIMD, meeting at one barrier per tile.  Key tiles of 32 slots are gathered straight
-// from HBM (one 256-byte code row per wavefront instruction), dequantised
-// exactly to fp16 and written to LDS twice: key-major for S^T = K Q^T and,
-// through a register transpose, slot-grouped for O^T = V^T P^T, so both
-// products run on v_mfma_f32_16x16x32_f16 with all operands read as 16-byte
-// LDS vectors, bank-conflict free (key-major rows padded by 32 bytes, the
-// slot-grouped layout XOR-swizzled).
+// kind per SIMD, meeting at one barrier per tile.  Key tiles of 32 slots
+// are gathered straight from HBM (one 256-byte code row per wavefront
+// instruction), dequantised exactly to fp16 and written to LDS once,
+// key-major (rows padded by 32 bytes).  Both products run on
+// v_mfma_f32_16x16x32_f16: S^T = K Q^T reads 16-byte key rows, and
+// O^T = V^T P^T reads the same tile through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16), so the keys need no second, slot-grouped copy.
 //
 // Why fp16: an E2M1 value times an E4M3 scale has at most 6 significant
 // bits and lies in [2^-10, 2688], so it is exact in fp16, and the scale
@@ -54,8 +54,7 @@ constexpr int kTile = 32;                   // key slots per tile
 // contiguous reads); with 32 bytes they take one.
 constexpr int kKtStride = 528;
 constexpr int kKtElems = kTile * kKtStride;
-constexpr int kVsElems = 4 * 512 * 8;
-constexpr int kBufElems = kKtElems + kVsElems;
+constexpr int kBufElems = kKtElems;         // one key-major tile per buffer
 constexpr int kSmemBytes = 2 * kBufElems * 2 + 2 * kTile * 4;
 // The epilogue stages 4 waves x 16 heads x (512 + 8) halfs in the same LDS.
 static_assert(4 * 16 * (512 + 8) * 2 <= kSmemBytes, "output staging fits");
@@ -65,6 +64,7 @@ constexpr float kRescaleSlack = 8.0f;       // log2 units
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t f16x2_bits(f16x2_t v) {
   return __builtin_bit_cast(uint32_t, v);
@@ -78,8 +78,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return bf2_bits(v);
 }
 
-// Chunk index (16-byte units) of (dim d) inside a quarter of the V buffer.
-__device__ __forceinline__ int vs_phys(int d) { return d ^ ((d >> 3) & 7); }
 
 // Rotation of RoPE pair i at query position t by -t * w (w = the pair's
 // frequency, computed on the host in double): the angle is formed and
@@ -250,21 +248,6 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
     u32x4 v = {kd[e][0], kd[e][1], kd[e][2], kd[e][3]};
     *reinterpret_cast<u32x4*>(kt + j * kKtStride + 8 * g) = v;
   }
-  // Slot-grouped columns: for dim d, the 8 slots of this quarter.
-  _Float16* vs = buf + kKtElems + quarter * (512 * 8);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 lo, hi;
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const uint32_t x0 = kd[2 * e2][i], x1 = kd[2 * e2 + 1][i];
-      lo[e2] = (x0 & 0xFFFFu) | (x1 << 16);
-      hi[e2] = (x0 >> 16) | (x1 & 0xFFFF0000u);
-    }
-    const int d0 = 8 * g + 2 * i;
-    *reinterpret_cast<u32x4*>(vs + vs_phys(d0) * 8) = lo;
-    *reinterpret_cast<u32x4*>(vs + vs_phys(d0 + 1) * 8) = hi;
-  }
   if (g == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -320,7 +303,6 @@ __device__ __forceinline__ void tile_math(
     const AttnArgs& p, int col, int q4, const _Float16* bufs,
     const int32_t* valid_base, const f16x8_t (&qb)[16], TileState& st) {
   const _Float16* kt = bufs + P * kBufElems;
-  const _Float16* vs = kt + kKtElems;
   const int32_t* valid = valid_base + P * kTile;
 
   // S^T = K Q^T for the 32 slots of this tile, as four independent
@@ -392,27 +374,36 @@ __device__ __forceinline__ void tile_math(
 #pragma unroll
   for (int r = 0; r < 8; ++r) st.l_run += (float)pb[r];
 
-  // O^T += V^T P^T.
+  // O^T += V^T P^T, V^T read from the key-major tile by transposing LDS
+  // reads (ds_read_b64_tr_b16): within a 16-lane group, lane i receives
+  // element i mod 4 of the 8-byte chunks addressed by lanes 4j + i/4
+  // (j = 0..3).  The product's k index for lane group q4 runs over slots
+  // 4*q4 .. 4*q4+3 and then 16+4*q4 .. 16+4*q4+3 (the logits' output
+  // order, which is how the probabilities arrive), so lane m of group q4
+  // addresses row 4*q4 + m/4 (then 16 rows further) at dims
+  // 16*blk + 4*(m mod 4): lane i = col receives dim 16*blk + col of those
+  // eight slots.  Two bases per lane, a 32-byte immediate step per block.
   {
     constexpr int kAhead = 4;
-    // vs_phys(16 blk + col) = 16 blk + (col ^ x) with x = (2 blk + col/8) & 7,
-    // which repeats every 4 blocks: four per-lane bases plus a constant
-    // 256-byte step per block (an immediate offset of the read).
-    const _Float16* v0 = vs + q4 * (512 * 8);
-    const _Float16* vb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      vb[j] = v0 + (col ^ ((2 * j + (col >> 3)) & 7)) * 8;
+    const _Float16* ta0 =
+        kt + (4 * q4 + (col >> 2)) * kKtStride + 4 * (col & 3);
+    const _Float16* ta1 = ta0 + 16 * kKtStride;
+    auto v_operand = [&](int blk) -> f16x8_t {
+      typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(ta0 + 16 * blk));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(ta1 + 16 * blk));
+      return __builtin_bit_cast(
+          f16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     f16x8_t va[kAhead];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i)
-      va[i] = *reinterpret_cast<const f16x8_t*>(vb[i & 3] + 128 * i);
+    for (int i = 0; i < kAhead; ++i) va[i] = v_operand(i);
 #pragma unroll
     for (int blk = 0; blk < 32; ++blk) {
       const f16x8_t c = va[blk % kAhead];
-      if (blk + kAhead < 32)
-        va[blk % kAhead] = *reinterpret_cast<const f16x8_t*>(
-            vb[(blk + kAhead) & 3] + 128 * (blk + kAhead));
+      if (blk + kAhead < 32) va[blk % kAhead] = v_operand(blk + kAhead);
       st.acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c, pb, st.acc[blk], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
