@@ -664,8 +664,8 @@ hipError_t launch_combine(const uint16_t* part_o, const float* part_ml,
 
 int attn_splits(int B, int k) {
   const int n_tiles = (k + kWindow + kTile - 1) / kTile;
-  // About one workgroup per compute unit (256 CUs, one workgroup each:
-  // the double-buffered tiles take 129 KB of LDS); with many sequences at
+  // About one workgroup per compute unit (256 CUs, one workgroup each: its
+  // 8 wavefronts take all 512 registers per SIMD lane); with many sequences at
   // least 3 tiles each, to bound the partials' traffic.
   int s = (256 + B - 1) / (B > 0 ? B : 1);
   const int max_s = B >= 16 ? (n_tiles + 2) / 3 : n_tiles;
