@@ -176,20 +176,42 @@ __device__ __forceinline__ void load_rows(const AttnArgs& p, const Bases& bs,
   const uint32_t srow = ok_swa ? (uint32_t)rr : 0u;
   const uint32_t offa = main_l ? row * 256u : srow * 512u;
   const uint32_t offc = main_l ? row * 32u : srow * 512u + 4u;
-  const uint32_t kind = ok_main ? 1u : (ok_swa ? 2u : 0u);
   const uint32_t g4 = 4u * (uint32_t)g, g8 = 8u * (uint32_t)g;
   const uint32_t gs = (uint32_t)((g >> 1) & ~3);
-  kinds = 0;
+  // Slot kinds from two ballots (bit e: slot e, held by lane off+e), each
+  // bit spread to the low bit of a 2-bit field: 1 = chosen entry, 2 =
+  // window row (exclusive), 0 = empty.
+  auto spread = [](uint32_t x) {
+    x = (x | (x << 4)) & 0x0F0Fu;
+    x = (x | (x << 2)) & 0x3333u;
+    return (x | (x << 1)) & 0x5555u;
+  };
+  const uint32_t mm =
+      (uint32_t)(__builtin_amdgcn_ballot_w64(ok_main) >> off) & 0xFFu;
+  const uint32_t ms =
+      (uint32_t)(__builtin_amdgcn_ballot_w64(ok_swa) >> off) & 0xFFu;
+  kinds = spread(mm) | (spread(ms) << 1);
+  if (tile * kTile + 16 + 4 * quarter + 3 < p.k) {
+    // All 8 slots of this wavefront are chosen entries (every tile before
+    // the one holding slot k): no per-slot choice of plane or offset.
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bool is_main = tile * kTile + slot_of(quarter, e) < p.k;
-    const uint32_t oa = __builtin_amdgcn_readlane(offa, off + e);
-    const uint32_t oc = __builtin_amdgcn_readlane(offc, off + e);
-    kinds |= (uint32_t)__builtin_amdgcn_readlane(kind, off + e) << (2 * e);
-    const uint8_t* ba = is_main ? bs.codes : bs.swa;
-    const uint8_t* bc = is_main ? bs.scales : bs.swa;
-    raw.a[e] = *reinterpret_cast<const uint32_t*>(ba + (oa + (is_main ? g4 : g8)));
-    raw.c[e] = *reinterpret_cast<const uint32_t*>(bc + (oc + (is_main ? gs : g8)));
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t oa = __builtin_amdgcn_readlane(offa, off + e);
+      const uint32_t oc = __builtin_amdgcn_readlane(offc, off + e);
+      raw.a[e] = *reinterpret_cast<const uint32_t*>(bs.codes + (oa + g4));
+      raw.c[e] = *reinterpret_cast<const uint32_t*>(bs.scales + (oc + gs));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool is_main = tile * kTile + slot_of(quarter, e) < p.k;
+      const uint32_t oa = __builtin_amdgcn_readlane(offa, off + e);
+      const uint32_t oc = __builtin_amdgcn_readlane(offc, off + e);
+      const uint8_t* ba = is_main ? bs.codes : bs.swa;
+      const uint8_t* bc = is_main ? bs.scales : bs.swa;
+      raw.a[e] = *reinterpret_cast<const uint32_t*>(ba + (oa + (is_main ? g4 : g8)));
+      raw.c[e] = *reinterpret_cast<const uint32_t*>(bc + (oc + (is_main ? gs : g8)));
+    }
   }
 }
 
