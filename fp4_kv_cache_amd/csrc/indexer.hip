@@ -47,7 +47,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTilesPerWave = 8;    // 32-entry tiles per wavefront
-constexpr int kEntriesPerBlock = kWaves * kTilesPerWave * 32;
 
 // Raw key data one lane holds for one 32-entry tile.
 template <int KEYFMT> struct RawKey;
@@ -145,7 +144,8 @@ template <bool SCALED> struct Depth<1, SCALED> {
 // QFP4: the query is MXFP4 planes (codes q[B][32][64], scales
 // q_scales[B][32][4]) instead of bf16 q[B][32][128].  BLK (with KEYS):
 // the block maxima are written too.
-template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false, bool CAND = false>
+template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false, bool CAND = false,
+          int TPW = kTilesPerWave>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
@@ -156,14 +156,14 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     uint32_t* __restrict__ btmax, int n_div) {
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int D = Depth<KEYFMT, kScaledOp>::value;
-  constexpr int T = kTilesPerWave;
+  constexpr int T = TPW;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int half = lane >> 5;
   const int64_t base =
-      ((int64_t)blockIdx.x * kWaves + wave) * (kTilesPerWave * 32);
+      ((int64_t)blockIdx.x * kWaves + wave) * (T * 32);
   if (base >= n_rows) return;                  // wave-uniform; no barriers
   // Valid rows: n_entries[b], or for bf16 block keys ceil(n_entries[b] /
   // n_div) (rows are blocks of n_div entries; 32-bit unsigned, exact for
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     }
   }
   // Stores after the loop keep the loads' wait counts static.
-  static_assert(kTilesPerWave * 32 == 256, "a wavefront's rows are one "
+  static_assert(!BLK || T * 32 == 256, "a wavefront's rows are one "
                 "32-block group of the block maxima");
   uint32_t wmax = 0u;
 #pragma unroll
@@ -350,13 +350,31 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 }  // namespace
 
 namespace {
+// A plain MXFP4-key scan with the bf16 query takes 16 tiles per wavefront
+// once 8 would need three or more generations of wavefronts (4 per SIMD on
+// 256 CUs): each wavefront loads the 8 KB query, and there the dispatcher's
+// balancing no longer needs the shorter wavefronts (64 x 131,072 entries:
+// 112.9 against 121.1 us).  The MXFP4 query (2 KB) gains nothing from it.
+constexpr int64_t kLongScanWaves = 3 * 4096;
+
 template <int KEYFMT, bool KEYS, bool QFP4>
-void launch_one(dim3 grid, hipStream_t s, const void* k_codes,
+void launch_one(int B, hipStream_t s, const void* k_codes,
                 const uint8_t* k_scales, int64_t n_cap,
                 const int32_t* n_entries, const int32_t* cand, int64_t n_rows,
                 const IndexQuery& iq, float* scores, uint32_t* tmax,
                 uint32_t* bmax, uint32_t* btmax, int n_div) {
-  if (KEYS && KEYFMT == 0 && !QFP4 && bmax)
+  const auto grid_for = [&](int tpw) {
+    const int64_t epb = (int64_t)kWaves * tpw * 32;
+    return dim3((unsigned)((n_rows + epb - 1) / epb), (unsigned)B);
+  };
+  const dim3 grid = grid_for(kTilesPerWave);
+  const int64_t waves = (int64_t)grid.x * grid.y * kWaves;
+  if (KEYFMT == 0 && !QFP4 && !bmax && !cand && waves >= kLongScanWaves)
+    hipLaunchKernelGGL((indexer_kernel<0, KEYS, false, false, false, 16>),
+                       grid_for(16), dim3(256), 0, s, k_codes, k_scales,
+                       n_cap, n_entries, cand, n_rows, iq.q, iq.q_scales,
+                       iq.w, scores, tmax, bmax, btmax, n_div);
+  else if (KEYS && KEYFMT == 0 && !QFP4 && bmax)
     hipLaunchKernelGGL((indexer_kernel<0, true, false, true>), grid,
                        dim3(256), 0, s, k_codes, k_scales, n_cap, n_entries,
                        cand, n_rows, iq.q, iq.q_scales, iq.w, scores, tmax,
@@ -373,17 +391,17 @@ void launch_one(dim3 grid, hipStream_t s, const void* k_codes,
                        btmax, n_div);
 }
 template <int KEYFMT, bool KEYS>
-void launch_q(dim3 grid, hipStream_t s, const void* k_codes,
+void launch_q(int B, hipStream_t s, const void* k_codes,
               const uint8_t* k_scales, int64_t n_cap, const int32_t* n_entries,
               const int32_t* cand, int64_t n_rows, const IndexQuery& iq,
               float* scores, uint32_t* tmax, uint32_t* bmax,
               uint32_t* btmax, int n_div) {
   if (iq.q_scales)
-    launch_one<KEYFMT, KEYS, true>(grid, s, k_codes, k_scales, n_cap,
+    launch_one<KEYFMT, KEYS, true>(B, s, k_codes, k_scales, n_cap,
                                    n_entries, cand, n_rows, iq, scores, tmax,
                                    bmax, btmax, n_div);
   else
-    launch_one<KEYFMT, KEYS, false>(grid, s, k_codes, k_scales, n_cap,
+    launch_one<KEYFMT, KEYS, false>(B, s, k_codes, k_scales, n_cap,
                                     n_entries, cand, n_rows, iq, scores, tmax,
                                     bmax, btmax, n_div);
 }
@@ -400,19 +418,17 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
   // Block maxima: MXFP4 keys, bf16 query, all rows.
   if (bmax && (!tmax || cand || !btmax || keyfmt != 0 || iq.q_scales))
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((n_rows + kEntriesPerBlock - 1) / kEntriesPerBlock),
-                  (unsigned)B);
   if (keyfmt == 0 && tmax)
-    launch_q<0, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+    launch_q<0, true>(B, s, k_codes, k_scales, n_cap, n_entries, cand,
                       n_rows, iq, scores, tmax, bmax, btmax, n_div);
   else if (keyfmt == 0)
-    launch_q<0, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+    launch_q<0, false>(B, s, k_codes, k_scales, n_cap, n_entries, cand,
                        n_rows, iq, scores, tmax, bmax, btmax, n_div);
   else if (tmax)
-    launch_q<1, true>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+    launch_q<1, true>(B, s, k_codes, k_scales, n_cap, n_entries, cand,
                       n_rows, iq, scores, tmax, bmax, btmax, n_div);
   else
-    launch_q<1, false>(grid, s, k_codes, k_scales, n_cap, n_entries, cand,
+    launch_q<1, false>(B, s, k_codes, k_scales, n_cap, n_entries, cand,
                        n_rows, iq, scores, tmax, bmax, btmax, n_div);
   return hipGetLastError();
 }
