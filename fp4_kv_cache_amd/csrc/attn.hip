@@ -507,7 +507,11 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
   __syncthreads();
 
   // Each side runs its own loop (the producers' in-flight rows are not
-  // live in the math loop); both pass the same barriers, one per tile.
+  // live in the math loop); both pass the same number of barriers, one per
+  // tile.  The role is uniform within a wavefront (wv comes from
+  // readfirstlane), and the hardware barrier (s_barrier) releases once every
+  // wavefront of the workgroup has arrived at a barrier, whichever barrier
+  // instruction each executes, so the two loops stay in step.
   if (is_math) {
     for (int t = t0; t < t1; t += 2) {
       tile_math<0>(p, col, q4, bufs, valid_base, qb, st);
