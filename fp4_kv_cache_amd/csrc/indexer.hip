@@ -351,11 +351,12 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 
 namespace {
 // A plain MXFP4-key scan with the bf16 query takes 16 tiles per wavefront
-// once 8 would need three or more generations of wavefronts (4 per SIMD on
+// once 8 would need two or more generations of wavefronts (4 per SIMD on
 // 256 CUs): each wavefront loads the 8 KB query, and there the dispatcher's
 // balancing no longer needs the shorter wavefronts (64 x 131,072 entries:
-// 112.9 against 121.1 us).  The MXFP4 query (2 KB) gains nothing from it.
-constexpr int64_t kLongScanWaves = 3 * 4096;
+// 112.9 against 121.1 us; 4 x 524,288: 30.7 against 32.0 us).  A single
+// generation (32 x 32,768) keeps 8; the MXFP4 query (2 KB) gains nothing.
+constexpr int64_t kLongScanWaves = 2 * 4096;
 
 template <int KEYFMT, bool KEYS, bool QFP4>
 void launch_one(int B, hipStream_t s, const void* k_codes,
