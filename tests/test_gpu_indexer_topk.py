@@ -155,3 +155,33 @@ def test_topk_ids_and_block_expansion():
         ok = ids[b] >= 0
         ref = O.topk(sc2[b][ok].astype(np.float64), 512, ids=ids[b][ok])
         assert np.array_equal(out2[b], ref)
+
+
+def test_indexer_scores_long_scan_sampled():
+    """A scan long enough for the 16-tile wavefronts (8 rows of 262,181
+    entries: 8,224 wavefronts of 8 tiles, two generations), ragged row
+    counts, checked against the oracle on sampled positions (every tile
+    position of a wavefront, the row ends) and -inf past each count."""
+    B, n_cap = 8, 262144 + 37
+    gen = torch.Generator(device=DEV).manual_seed(4242)
+    x = torch.randn((B * n_cap, 128), generator=gen, device=DEV)
+    c, s = csa2.pack_kv(csa2.FMT_IDX, x)
+    del x
+    c, s = c.view(B, n_cap, 64), s.view(B, n_cap, 4)
+    qi, w = _query(B, 7)
+    n_entries = [n_cap, n_cap - 1000, 123457, 1, 0, 262144, 200000, 77]
+    ne = torch.tensor(n_entries, dtype=torch.int32, device=DEV)
+    sc = csa2.indexer_score(csa2.KEYS_MXFP4, c, s, ne, qi, w).cpu().numpy()
+    cc, ss = c.cpu().numpy(), s.cpu().numpy()
+    rng = np.random.default_rng(11)
+    for b in range(B):
+        n = n_entries[b]
+        if n:
+            rows = np.unique(np.concatenate([
+                rng.integers(0, n, 1500),
+                np.arange(0, min(n, 512 * 3)),          # whole wavefronts
+                np.arange(max(0, n - 300), n)]))        # the row's end
+            ref = _ref_scores(cc, ss, qi, w, b, rows)
+            np.testing.assert_allclose(sc[b, rows], ref, rtol=SCORE_RTOL,
+                                       atol=1e-4)
+        assert np.all(np.isneginf(sc[b, n:])), b
