@@ -454,8 +454,9 @@ def run_cpu(wl, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus "
-              f"{args.gpus}); sharding is described, not run", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (got --gpus "
+              f"{args.gpus}); the decode is not sharded across GPUs",
+              file=sys.stderr)
         sys.exit(2)
     from fp4_kv_cache_amd.inputs import WORKLOADS
     wl = WORKLOADS[args.workload]
