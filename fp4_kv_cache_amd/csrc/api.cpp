@@ -168,7 +168,7 @@ csa2_status check_attn_common(const uint8_t* main_codes,
   if (n_cap > kMaxAttnCap)
     return fail(CSA2_ERR_UNSUPPORTED,
                 "attention needs n_cap <= 2^24 (got %lld)", (long long)n_cap);
-  if (!(scale == scale) || scale == 0.0f)
+  if (!std::isfinite(scale) || scale == 0.0f)
     return fail(CSA2_ERR_INVALID_ARG, "scale must be a finite nonzero float");
   if (B == 0) return CSA2_OK;
   if (!main_codes || !main_scales || !q || !swa || !n_swa || !out)

@@ -489,19 +489,28 @@ __global__ __launch_bounds__(kNT) void row_select_pair_kernel(RowArgs a0,
   else row_select_row<false, true>(a1, (int)blockIdx.x - B0);
 }
 
-// Tile maxima of a plain score array (entries with a negative id count as
-// -inf).  One thread per tile.
+// Tile maxima of a plain score array.  Entries at or past the row's length
+// (n_valid[b] when given) and entries with a negative id count as -inf, so a
+// tile maximum is always the maximum of scores the selection may choose: a
+// stale value past the length must not lift a tile above the pruning bound.
+// One thread per tile.
 __global__ void tilemax_kernel(const float* __restrict__ scores, int64_t ld,
-                               const int32_t* __restrict__ ids, int B,
+                               const int32_t* __restrict__ ids,
+                               const int32_t* __restrict__ n_valid, int B,
                                float* __restrict__ tmax) {
   const int64_t nt = (ld + 31) >> 5;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= nt * B) return;
   const int64_t b = t / nt, tt = t % nt;
+  int64_t len = ld;
+  if (n_valid) {
+    const int32_t v = n_valid[b];
+    len = v <= 0 ? 0 : ((int64_t)v < ld ? (int64_t)v : ld);
+  }
   float mx = -__builtin_inff();
   for (int j = 0; j < 32; ++j) {
     const int64_t i = tt * 32 + j;
-    if (i >= ld) break;
+    if (i >= len) break;
     const float v = scores[b * ld + i];
     if ((!ids || ids[b * ld + i] >= 0) && v > mx) mx = v;
   }
@@ -591,7 +600,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
     tmax = static_cast<float*>(ws);
     const int64_t n = (int64_t)B * ((ld + 31) >> 5);
     hipLaunchKernelGGL(tilemax_kernel, dim3((unsigned)((n + 255) / 256)),
-                       dim3(256), 0, s, scores, ld, ids, B, tmax);
+                       dim3(256), 0, s, scores, ld, ids, n_valid, B, tmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

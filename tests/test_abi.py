@@ -96,6 +96,10 @@ def test_attention_errors(L):
     assert f(*mis) == ALIGN
     zero_scale = list(args); zero_scale[9] = ctypes.c_float(0.0)
     assert f(*zero_scale) == INVALID
+    for bad in (float("inf"), float("-inf"), float("nan")):
+        inf_scale = list(args); inf_scale[9] = ctypes.c_float(bad)
+        assert f(*inf_scale) == INVALID
+        assert "finite" in _err()
     alias = list(args); alias[10] = A       # out == main_codes
     assert f(*alias) == INVALID
     assert f(*[a if i != 8 else 0 for i, a in enumerate(args)]) == OK  # B = 0

@@ -100,6 +100,29 @@ def test_topk_exact_vs_oracle(ld, k):
         assert np.array_equal(out[b], ref), b
 
 
+def test_topk_pruning_ignores_values_past_n_valid():
+    """Stale values past a row's length must not enter the tile maxima: a
+    row of 40,000 scores with n_valid = 39,873 (not a multiple of 32), 511
+    tiles holding one 1.0 each and 0.0 elsewhere, and 100.0 past n_valid.
+    A tile maximum taken over the stale tail would make exactly k tiles
+    clear the pruning bound with only 511 valid entries above it; the
+    answer is the 511 ones plus the lowest-id zero.  A second row checks
+    the same with N(0,1) scores."""
+    ld, nvalid, k = 40000, 39873, 512
+    rng = np.random.default_rng(77)
+    sc = np.zeros((2, ld), np.float32)
+    tiles = np.sort(rng.choice(nvalid // 32, 511, replace=False))
+    sc[0, tiles * 32 + rng.integers(0, 32, 511)] = 1.0
+    sc[1] = rng.standard_normal(ld).astype(np.float32)
+    sc[:, nvalid:] = 100.0
+    nv = torch.tensor([nvalid, nvalid - 900], dtype=torch.int32, device=DEV)
+    out = csa2.topk(torch.from_numpy(sc).to(DEV), k, n_valid=nv).cpu().numpy()
+    for b, n in enumerate((nvalid, nvalid - 900)):
+        ref = O.topk(sc[b, :n].astype(np.float64), k)
+        assert np.array_equal(out[b], ref), b
+    assert np.all(out >= 0)
+
+
 def test_topk_all_equal_and_short_rows():
     sc = np.zeros((2, 3000), np.float32)
     sc[1, :] = 5.0

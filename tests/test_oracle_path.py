@@ -462,3 +462,48 @@ def test_compress_block_bruteforce():
     for o in (0, 127):
         assert ki[o] == pytest.approx(
             math.fsum(cbar[j] * Wik[o, j] for j in range(512)), rel=1e-12)
+
+
+def test_reuse_layer_ext_composition():
+    """reuse_layer_ext (the reference of every sink / de-rotation GPU test)
+    pinned by closed forms, not by its own formula: no sink and no position
+    give reuse_layer exactly; position 0 gives the sink attention alone; one
+    chosen key and no window give o_h = a_h R_{-t} k with
+    a_h = e^l / (e^l + e^z), the rotation written out by hand for pairs 0
+    and 31 at a non-default theta ("DeepSeek-V4: Towards Highly Efficient
+    Million-Token Context Intelligence", other details: attention-sink and
+    R_{-t} o_t equations)."""
+    c = _case(30, 34)
+    sel = np.array([3, 17, 29, -1, 8])
+    base = O.reuse_layer(c["mc"], c["ms"], sel, c["q"], c["sw"], 100, SCALE)
+    assert np.array_equal(
+        O.reuse_layer_ext(c["mc"], c["ms"], sel, c["q"], c["sw"], 100, SCALE),
+        base)
+    z = np.linspace(-4, 4, 64).astype(np.float32)
+    keys = O.gather_keys(c["mc"], c["ms"], sel, c["sw"], 100)
+    assert np.array_equal(
+        O.reuse_layer_ext(c["mc"], c["ms"], sel, c["q"], c["sw"], 100, SCALE,
+                          sink=z, pos=0),
+        O.mqa_decode_sink(c["q"], keys, SCALE, z))
+    # One key, no window: closed form, head by head.
+    t, theta = 77, 500.0
+    got = O.reuse_layer_ext(c["mc"], c["ms"], np.array([12]), c["q"], c["sw"],
+                            0, SCALE, sink=z, pos=t, theta=theta)
+    k = O.unpack_main(c["mc"][12:13], c["ms"][12:13])[0]
+    q = F.bf16_bits_to_f64(c["q"])
+    for h in (0, 21, 63):
+        l = math.fsum(float(q[h, d]) * float(k[d]) for d in range(512)) * SCALE
+        a = math.exp(l) / (math.exp(l) + math.exp(float(z[h])))
+        want = a * k.copy()
+        for i in (0, 31):
+            ang = -t * theta ** (-2.0 * i / 64)
+            x, y = want[448 + 2 * i], want[449 + 2 * i]
+            want[448 + 2 * i] = x * math.cos(ang) - y * math.sin(ang)
+            want[449 + 2 * i] = x * math.sin(ang) + y * math.cos(ang)
+        for d in (0, 200, 447, 448, 449, 510, 511):
+            assert got[h, d] == pytest.approx(want[d], rel=1e-11, abs=1e-13)
+    # A sink of -inf with a position is the plain attention, de-rotated.
+    assert np.allclose(
+        O.reuse_layer_ext(c["mc"], c["ms"], sel, c["q"], c["sw"], 100, SCALE,
+                          sink=np.full(64, -np.inf), pos=t, theta=theta),
+        O.rope_derotate(base, t, theta), rtol=1e-12, atol=1e-12)
