@@ -62,7 +62,8 @@ struct DecodeLayout {
   int64_t nb = 0, n_cand = 0;
   int kb = 0;
   size_t off_scores = 0, off_tmax = 0, off_bscores = 0,
-         off_pool = 0, off_pscores = 0, off_attn = 0, total = 0;
+         off_pool = 0, off_pscores = 0, off_lcand = 0, off_lbound = 0,
+         off_attn = 0, total = 0;
 };
 
 inline size_t tiles_of(int64_t rows) { return (size_t)((rows + 31) / 32); }
@@ -80,6 +81,12 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     off += align256((size_t)B * round32(n_cap) * 4);
     L.off_tmax = off;
     off += align256((size_t)B * tiles_of(n_cap) * 4);
+    // Local candidates and bounds of the fused selection (at most
+    // kLocalMaxCands pairs and kLocalMaxCands / 8 groups per sequence).
+    L.off_lcand = off;
+    off += align256((size_t)B * csa2::kLocalMaxCands * 8);
+    L.off_lbound = off;
+    off += align256((size_t)B * (csa2::kLocalMaxCands / 8) * 4);
   } else {
     L.nb = (n_cap + pool->block - 1) / pool->block;
     L.kb = (int)std::min<int64_t>(pool->n_blocks_keep, L.nb);
@@ -525,6 +532,27 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
   hipError_t e;
   // Decode-internal buffers hold selection keys (uint32), not scores.
   uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
+  const csa2::LocalPlan lp =
+      pool ? csa2::LocalPlan{}
+           : csa2::local_plan(B, kv->n_cap, k, iq.q_scales != nullptr);
+  if (!pool && lp.ok) {
+    // Scan with per-workgroup local candidates; the selection happens in
+    // the attention workgroups themselves.
+    uint32_t* keys = reinterpret_cast<uint32_t*>(base + L.off_scores);
+    uint2* lcand = reinterpret_cast<uint2*>(base + L.off_lcand);
+    uint32_t* lbound = reinterpret_cast<uint32_t*>(base + L.off_lbound);
+    e = csa2::launch_indexer_local(kv->idx_codes, kv->idx_scales, kv->n_cap,
+                                   kv->n_entries, iq, B, keys, lp, lcand,
+                                   lbound, s);
+    if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    const csa2::FusedSelect fs{lcand, lbound, lp.n_wg, lp.kloc, keys,
+                               round32(kv->n_cap), kv->n_entries, topk_out};
+    e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap,
+                          topk_out, k, q, swa, n_swa, B, scale, out,
+                          base + L.off_attn, s, epi, &fs);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return CSA2_OK;
+  }
   if (!pool) {
     float* scores = reinterpret_cast<float*>(base + L.off_scores);
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,

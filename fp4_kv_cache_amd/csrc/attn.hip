@@ -43,6 +43,8 @@
 // and the partials stay in that XCD's L2.
 #include "common.h"
 #include "internal.h"
+#include "select.h"
+#include "stream_select.h"
 
 namespace csa2 {
 namespace {
@@ -121,7 +123,26 @@ struct AttnArgs {
   int tiles_per_split;
   int n_tiles;
   AttnEpilogue epi;        // sink and de-rotation (final output only)
+  // Fused selection (the decode path): every workgroup selects its
+  // sequence's top-k itself from the indexer's local candidates.
+  const uint2* lcand;      // [B][n_wg][kloc] (key, id), id order
+  const uint32_t* lbound;  // [B][n_wg]
+  int n_wg, kloc;
+  const uint32_t* keys;    // [B][ld] selection keys (exact fallback)
+  int64_t ld;
+  const int32_t* n_entries;
+  int32_t* topk_out;       // [B][k], written by each sequence's split 0
 };
+
+// Shared memory of the fused selection (512 threads), overlaid on the
+// attention's tile buffers, which are not in use yet.
+struct FselSmem {
+  uint32_t key[512 * kStreamPer];   // the exact fallback's streaming store
+  int32_t id[512 * kStreamPer];
+  SelSmem<512, 256> sel;
+  uint32_t lmax[8];
+};
+constexpr int kMaxK = 2048;
 
 // Raw gather registers for the 8 slots this lane dequantises in one tile.
 // They hold the loaded words untouched, so nothing waits for the loads
@@ -141,11 +162,79 @@ __device__ __forceinline__ int slot_of(int quarter, int e) {
 // per-lane (vector) load: a scalar load would share its wait counter with the
 // LDS reads of the products and stall them.  Lane l fetches slot (l & 7) of
 // tile `ta` (l < 8) or `tb` (l >= 8).  Slots past the chosen entries read a
-// clamped, always valid address; their value is unused.
-__device__ __forceinline__ int32_t load_ids(const AttnArgs& p, int b, int ta,
+// clamped, always valid address; their value is unused.  `ids` is the
+// sequence's id row: in global memory, or in LDS after a fused selection.
+__device__ __forceinline__ int32_t load_ids(const AttnArgs& p,
+                                            const int32_t* ids, int ta,
                                             int tb, int quarter, int lane) {
   const int slot = ((lane & 8) ? tb : ta) * kTile + slot_of(quarter, lane & 7);
-  return p.topk[(int64_t)b * p.k + (slot < p.k ? slot : 0)];
+  return ids[slot < p.k ? slot : 0];
+}
+
+// The fused selection: the exact top-k of sequence b from the indexer's
+// local candidates (the k largest pair keys, equal keys to the lower id,
+// since the pairs are in id order), into sel_ids[0..k) ascending with -1
+// padding, and into topk_out by split 0.  It is exact when the k-th largest
+// candidate key is above every group's bound (nothing a group left out can
+// then reach the top k), or, with fewer than k valid candidates, when no
+// group left anything out; otherwise the whole row's selection keys are
+// streamed through the exact block selection instead.  All 512 threads
+// take part; ends with a barrier.
+template <int PER>
+__device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
+                                             int split, int32_t* sel_ids,
+                                             FselSmem& fs) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 8 * 256; i += 512) (&fs.sel.hist[0][0])[i] = 0;
+  const int C = p.n_wg * p.kloc;
+  const uint2* cr = p.lcand + (int64_t)b * C;
+  uint32_t kk[PER];
+  int32_t ci[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid * PER + j;
+    const uint2 v = cr[i < C ? i : C - 1];
+    kk[j] = i < C ? v.x : 0u;
+    ci[j] = (int32_t)v.y;
+  }
+  uint32_t lb = 0u;
+  for (int i = tid; i < p.n_wg; i += 512)
+    lb = max(lb, p.lbound[(int64_t)b * p.n_wg + i]);
+  lb = wave_max_u32(lb);
+  if ((tid & 63) == 0) fs.lmax[tid >> 6] = lb;
+  __syncthreads();
+  uint32_t L = 0u;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) L = max(L, fs.lmax[w]);
+  const SelResult r = block_select<512, PER, 256>(kk, p.k, fs.sel);
+  const bool ok = r.nval >= p.k ? (L < r.thr) : (L == 0u);
+  int32_t* gout = (split == 0 && p.topk_out) ? p.topk_out + (int64_t)b * p.k
+                                             : nullptr;
+  if (ok) {
+    int q = r.pos;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (r.mask & (1u << j)) {
+        sel_ids[q] = ci[j];
+        if (gout) gout[q] = ci[j];
+        ++q;
+      }
+    for (q = r.total + tid; q < p.k; q += 512) {
+      sel_ids[q] = -1;
+      if (gout) gout[q] = -1;
+    }
+  } else {
+    const int32_t ne = p.n_entries[b];
+    const int64_t len = ne <= 0 ? 0 : ((int64_t)ne < p.n_cap ? ne : p.n_cap);
+    const ScoreSrc<false, true> src{p.keys + (int64_t)b * p.ld, nullptr};
+    const int cnt = stream_select<512>(fs, len, p.k, src);
+    for (int q = tid; q < p.k; q += 512) {
+      const int32_t v = q < cnt ? fs.id[q] : -1;
+      sel_ids[q] = v;
+      if (gout) gout[q] = v;
+    }
+  }
+  __syncthreads();
 }
 
 // Per-sequence bases of the gathered planes (wavefront-uniform).
@@ -304,12 +393,12 @@ struct TileState {
 // dequantised into LDS buffer P^1 while the math wavefronts read buffer P.
 template <int P>
 __device__ __forceinline__ void tile_produce(
-    const AttnArgs& p, const Bases& bs, int b, int t, int t1, int quarter,
-    int lane, int nswa, _Float16* bufs, int32_t* valid_base, Raw (&raw)[2],
-    uint32_t (&kinds)[2], int32_t& idn) {
+    const AttnArgs& p, const Bases& bs, const int32_t* ids, int t, int t1,
+    int quarter, int lane, int nswa, _Float16* bufs, int32_t* valid_base,
+    Raw (&raw)[2], uint32_t (&kinds)[2], int32_t& idn) {
   const int tl = t1 - 1;
   const int t3 = t + 3 < t1 ? t + 3 : tl;
-  const int32_t id3 = load_ids(p, b, t3, t3, quarter, lane);
+  const int32_t id3 = load_ids(p, ids, t3, t3, quarter, lane);
   load_rows(p, bs, t + 2 < t1 ? t + 2 : tl, quarter, lane, nswa, idn, 0,
             raw[P], kinds[P]);
   idn = id3;
@@ -433,6 +522,13 @@ __device__ __forceinline__ void tile_math(
 
 }
 
+// Dynamic shared memory: the tile buffers (overlaid by the fused
+// selection's store first), then the selected ids of a fused selection.
+constexpr int kFselBytes = (int)sizeof(FselSmem);
+constexpr int kUnionBytes = (kSmemBytes > kFselBytes ? kSmemBytes : kFselBytes);
+constexpr int kFusedSmemBytes = kUnionBytes + kMaxK * 4;
+
+template <bool FSEL, int CPER>
 __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   _Float16* bufs = reinterpret_cast<_Float16*>(smem_raw);
@@ -475,15 +571,25 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
   int32_t idn = 0;
   TileState st;
   f16x8_t qb[16];
+  // The sequence's id row: global (given top-k) or, after a fused
+  // selection, LDS.
+  int32_t* sel_ids = reinterpret_cast<int32_t*>(smem_raw + kUnionBytes);
+  const int32_t* ids = FSEL ? sel_ids : p.topk + (int64_t)b * p.k;
+  // Q^T operand: head `head`, dims 32s + 8*q4 .. +7.  The raw query is
+  // loaded first, so a fused selection runs while it is in flight.
+  bf16x8_t qraw[16];
   if (is_math) {
-    // Q^T operand: head `head`, dims 32s + 8*q4 .. +7, converted to fp16;
-    // the accumulators are zeroed after the conversion (the raw query is
-    // dead by then).
-    bf16x8_t qraw[16];
     const bf16x8_t* qr = reinterpret_cast<const bf16x8_t*>(
         p.q + ((int64_t)b * kHeads + head) * 512 + 8 * q4);
 #pragma unroll
     for (int s = 0; s < 16; ++s) qraw[s] = qr[4 * s];
+  }
+  if constexpr (FSEL)
+    fused_select<CPER>(p, b, split, sel_ids,
+                       *reinterpret_cast<FselSmem*>(smem_raw));
+  if (is_math) {
+    // The query converted to fp16; the accumulators are zeroed after the
+    // conversion (the raw query is dead by then).
 #pragma unroll
     for (int s = 0; s < 16; ++s)
 #pragma unroll
@@ -498,8 +604,8 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
     // The rows of the first two tiles go out together (a producer holds no
     // accumulators, so nothing else wants their registers); the first is
     // dequantised into buffer 0.
-    const int32_t id01 = load_ids(p, b, ta, tb, wave, lane);
-    idn = load_ids(p, b, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
+    const int32_t id01 = load_ids(p, ids, ta, tb, wave, lane);
+    idn = load_ids(p, ids, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
     load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
     load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
     if (t0 < t1) dequant_store(raw[0], kinds[0], wave, lane, bufs, valid_base);
@@ -523,11 +629,11 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
     }
   } else {
     for (int t = t0; t < t1; t += 2) {
-      tile_produce<0>(p, bs, b, t, t1, wave, lane, nswa, bufs, valid_base,
-                      raw, kinds, idn);
+      tile_produce<0>(p, bs, ids, t, t1, wave, lane, nswa, bufs,
+                      valid_base, raw, kinds, idn);
       __syncthreads();
       if (t + 1 < t1) {
-        tile_produce<1>(p, bs, b, t + 1, t1, wave, lane, nswa, bufs,
+        tile_produce<1>(p, bs, ids, t + 1, t1, wave, lane, nswa, bufs,
                         valid_base, raw, kinds, idn);
         __syncthreads();
       }
@@ -711,17 +817,27 @@ size_t attn_workspace(int B, int k) {
   return ((o + 255) & ~size_t(255)) + ((ml + 255) & ~size_t(255));
 }
 
+namespace {
+template <bool FSEL, int CPER>
+hipError_t launch_attn_kernel(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  const int bytes = FSEL ? kFusedSmemBytes : kSmemBytes;
+  hipError_t e = ensure_lds_limit(
+      reinterpret_cast<const void*>(attn_kernel<FSEL, CPER>), bytes, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_kernel<FSEL, CPER>), dim3(grid), dim3(512), bytes,
+                     s, a);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        int64_t n_cap, const int32_t* topk, int k,
                        const uint16_t* q, const uint8_t* swa,
                        const int32_t* n_swa, int B, float scale,
                        uint16_t* out, void* ws, hipStream_t s,
-                       const AttnEpilogue& epi) {
+                       const AttnEpilogue& epi, const FusedSelect* fsel) {
   if (B == 0) return hipSuccess;
-  static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(attn_kernel),
-                                  kSmemBytes, lds_set);
-  if (e != hipSuccess) return e;
   AttnArgs a{};
   a.main_codes = main_codes;
   a.main_scales = main_scales;
@@ -746,8 +862,26 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   }
   const int groups = (B + 7) / 8;
   const unsigned grid = (unsigned)(8 * groups * a.splits);
-  hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(512), kSmemBytes, s, a);
-  e = hipGetLastError();
+  hipError_t e;
+  if (fsel) {
+    const int C = fsel->n_wg * fsel->kloc;
+    if (k > kMaxK || C < 1 || C > kLocalMaxCands) return hipErrorInvalidValue;
+    a.lcand = fsel->lcand;
+    a.lbound = fsel->lbound;
+    a.n_wg = fsel->n_wg;
+    a.kloc = fsel->kloc;
+    a.keys = fsel->keys;
+    a.ld = fsel->ld;
+    a.n_entries = fsel->n_entries;
+    a.topk_out = fsel->topk_out;
+    // Candidate pairs per thread.
+    if (C <= 512) e = launch_attn_kernel<true, 1>(a, grid, s);
+    else if (C <= 1024) e = launch_attn_kernel<true, 2>(a, grid, s);
+    else if (C <= 2048) e = launch_attn_kernel<true, 4>(a, grid, s);
+    else e = launch_attn_kernel<true, 8>(a, grid, s);
+  } else {
+    e = launch_attn_kernel<false, 1>(a, grid, s);
+  }
   if (e != hipSuccess || a.splits == 1) return e;
   return launch_combine<2>(a.part_o, a.part_ml, a.splits, B, out, epi, s);
 }

@@ -42,6 +42,8 @@
 #include "internal.h"
 #include "select.h"
 
+#include <algorithm>
+
 namespace csa2 {
 namespace {
 
@@ -144,8 +146,15 @@ template <bool SCALED> struct Depth<1, SCALED> {
 // QFP4: the query is MXFP4 planes (codes q[B][32][64], scales
 // q_scales[B][32][4]) instead of bf16 q[B][32][128].  BLK (with KEYS):
 // the block maxima are written too.
+// LOCAL (with KEYS; all rows, no candidates): instead of tile maxima, each
+// workgroup also keeps its own local top-kloc entries as (key, id) pairs,
+// in id order, in lcand[B][gridDim.x][kloc] (key 0 / id -1 padding), and
+// in lbound[B][gridDim.x] a key at or above every valid entry it left out
+// (0 when it left none out).  The union of every workgroup's pairs then
+// holds the row's top-k whenever the k-th largest pair key is above every
+// bound: a selection over the small union is exact under that test.
 template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false, bool CAND = false,
-          int TPW = kTilesPerWave>
+          int TPW = kTilesPerWave, bool LOCAL = false>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
@@ -153,10 +162,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ q_in, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ w, float* __restrict__ scores,
     uint32_t* __restrict__ tmax, uint32_t* __restrict__ bmax,
-    uint32_t* __restrict__ btmax, int n_div) {
+    uint32_t* __restrict__ btmax, int n_div, uint2* __restrict__ lcand,
+    uint32_t* __restrict__ lbound, int kloc) {
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int D = Depth<KEYFMT, kScaledOp>::value;
   constexpr int T = TPW;
+  static_assert(!LOCAL || (KEYS && !BLK && !CAND && KEYFMT == 0),
+                "local candidates: MXFP4 keys, all rows, selection keys");
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -164,7 +176,20 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int half = lane >> 5;
   const int64_t base =
       ((int64_t)blockIdx.x * kWaves + wave) * (T * 32);
-  if (base >= n_rows) return;                  // wave-uniform; no barriers
+  // The local selection: the workgroup's keys in id order, then its
+  // selection histograms (zeroed here; the selection's first barrier comes
+  // long after).  A wavefront past the rows still takes part (its keys are
+  // all invalid), so no wavefront leaves before the selection's barriers.
+  extern __shared__ __align__(16) uint32_t lsm[];
+  uint32_t* kl = lsm;
+  SelSmem<256, 256>& lss =
+      *reinterpret_cast<SelSmem<256, 256>*>(lsm + kWaves * T * 32);
+  if constexpr (LOCAL) {
+    for (int i = threadIdx.x; i < kWaves * 256; i += 256)
+      (&lss.hist[0][0])[i] = 0;
+  } else {
+    if (base >= n_rows) return;                // wave-uniform; no barriers
+  }
   // Valid rows: n_entries[b], or for bf16 block keys ceil(n_entries[b] /
   // n_div) (rows are blocks of n_div entries; 32-bit unsigned, exact for
   // these ranges), never past the cache.  The MXFP4 scan carries no
@@ -179,8 +204,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
                           (int64_t)b * n_cap * (KEYFMT == 0 ? 64 : 256);
   const uint8_t* seq_scales =
       KEYFMT == 0 ? k_scales + (int64_t)b * n_cap * 4 : nullptr;
-  const int nt = (int)((n_rows - base + 31) >> 5) < T
-                     ? (int)((n_rows - base + 31) >> 5) : T;
+  const int64_t nt64 = base < n_rows ? (n_rows - base + 31) >> 5 : 0;
+  const int nt = nt64 < T ? (int)nt64 : T;
 
   // Row (within the sequence) of every tile position this lane will read,
   // with validity; invalid rows are clamped to row 0.  Candidate ids are
@@ -334,9 +359,11 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       m = dpp_max<0x142, 0xa>(m);
       m = dpp_max<0x143, 0xc>(m);
       const uint32_t mx = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
-      if (lane == 0)
+      if (!LOCAL && lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
       if constexpr (BLK) wmax = max(wmax, mx);
+      if constexpr (LOCAL)
+        if (half == 0) kl[wave * T * 32 + 32 * t + col] = key;
     } else {
       if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
     }
@@ -344,6 +371,32 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   if (BLK && lane == 0) {
     const int64_t nbt = (((n_rows + 7) >> 3) + 31) >> 5;
     btmax[(int64_t)b * nbt + (base >> 8)] = wmax;
+  }
+  if constexpr (LOCAL) {
+    // Tiles past the rows hold invalid keys.
+    for (int t = nt; t < T; ++t)
+      if (half == 0) kl[wave * T * 32 + 32 * t + col] = 0u;
+    __syncthreads();
+    // Thread i takes entries PER*i .. PER*i+PER-1 of the workgroup, so the
+    // selection's position order is id order.
+    constexpr int PER = T / 2;
+    const int tid = threadIdx.x;
+    uint32_t kk[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) kk[j] = kl[tid * PER + j];
+    const SelResult r = block_select<256, PER, 256>(kk, kloc, lss);
+    const int64_t wg = (int64_t)b * gridDim.x + blockIdx.x;
+    uint2* co = lcand + wg * kloc;
+    const uint32_t id0 = (uint32_t)(blockIdx.x * (kWaves * T * 32) + tid * PER);
+    int p = r.pos;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (r.mask & (1u << j)) co[p++] = make_uint2(kk[j], id0 + j);
+    for (int q = r.total + tid; q < kloc; q += 256)
+      co[q] = make_uint2(0u, 0xFFFFFFFFu);
+    // Every valid entry left out is <= thr (the selection ends on the k-th
+    // key's own value, or takes exactly the keys >= thr).
+    if (tid == 0) lbound[wg] = r.nval > kloc ? r.thr : 0u;
   }
 }
 
@@ -374,22 +427,23 @@ void launch_one(int B, hipStream_t s, const void* k_codes,
     hipLaunchKernelGGL((indexer_kernel<0, KEYS, false, false, false, 16>),
                        grid_for(16), dim3(256), 0, s, k_codes, k_scales,
                        n_cap, n_entries, cand, n_rows, iq.q, iq.q_scales,
-                       iq.w, scores, tmax, bmax, btmax, n_div);
+                       iq.w, scores, tmax, bmax, btmax, n_div, nullptr,
+                       nullptr, 0);
   else if (KEYS && KEYFMT == 0 && !QFP4 && bmax)
     hipLaunchKernelGGL((indexer_kernel<0, true, false, true>), grid,
                        dim3(256), 0, s, k_codes, k_scales, n_cap, n_entries,
                        cand, n_rows, iq.q, iq.q_scales, iq.w, scores, tmax,
-                       bmax, btmax, n_div);
+                       bmax, btmax, n_div, nullptr, nullptr, 0);
   else if (cand)
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4, false, true>),
                        grid, dim3(256), 0, s, k_codes, k_scales, n_cap,
                        n_entries, cand, n_rows, iq.q, iq.q_scales, iq.w,
-                       scores, tmax, bmax, btmax, n_div);
+                       scores, tmax, bmax, btmax, n_div, nullptr, nullptr, 0);
   else
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256),
                        0, s, k_codes, k_scales, n_cap, n_entries, cand,
                        n_rows, iq.q, iq.q_scales, iq.w, scores, tmax, bmax,
-                       btmax, n_div);
+                       btmax, n_div, nullptr, nullptr, 0);
 }
 template <int KEYFMT, bool KEYS>
 void launch_q(int B, hipStream_t s, const void* k_codes,
@@ -406,7 +460,64 @@ void launch_q(int B, hipStream_t s, const void* k_codes,
                                     n_entries, cand, n_rows, iq, scores, tmax,
                                     bmax, btmax, n_div);
 }
+template <bool QFP4, int T>
+hipError_t launch_local(int B, hipStream_t s, const void* k_codes,
+                        const uint8_t* k_scales, int64_t n_cap,
+                        const int32_t* n_entries, const IndexQuery& iq,
+                        uint32_t* keys, const LocalPlan& lp, uint2* lcand,
+                        uint32_t* lbound) {
+  const int smem = (kWaves * T * 32 + kWaves * 256 + 16) * 4;
+  hipLaunchKernelGGL((indexer_kernel<0, true, QFP4, false, false, T, true>),
+                     dim3((unsigned)lp.n_wg, (unsigned)B), dim3(256), smem, s,
+                     k_codes, k_scales, n_cap, n_entries, nullptr, n_cap,
+                     iq.q, iq.q_scales, iq.w, reinterpret_cast<float*>(keys),
+                     nullptr, nullptr, nullptr, 1, lcand, lbound, lp.kloc);
+  return hipGetLastError();
+}
 }  // namespace
+
+LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4) {
+  LocalPlan lp;
+  if (B < 1 || n_cap < 1 || k < 1) return lp;
+  // The same wavefront length as the plain scan (see kLongScanWaves).
+  const int64_t per8 = (int64_t)kWaves * 8 * 32;
+  const int64_t waves8 = ((n_cap + per8 - 1) / per8) * (int64_t)B * kWaves;
+  lp.tpw = (!qfp4 && waves8 >= kLongScanWaves) ? 16 : 8;
+  const int64_t epw = (int64_t)kWaves * lp.tpw * 32;      // rows per group
+  const int64_t n_wg = (n_cap + epw - 1) / epw;
+  if (n_wg > kLocalMaxCands / 8) return lp;
+  // At least 64 pairs per group (a group expects k * epw / n of the row's
+  // winners), at least 2k pairs in all, at most kLocalMaxCands in all.
+  int64_t kl = std::max<int64_t>(64, (2 * (int64_t)k + n_wg - 1) / n_wg);
+  kl = std::min<int64_t>(kl, epw);
+  kl = std::min<int64_t>(kl, kLocalMaxCands / n_wg);
+  if (kl < 8 || kl * n_wg < 2 * (int64_t)k) return lp;
+  lp.ok = true;
+  lp.n_wg = (int)n_wg;
+  lp.kloc = (int)kl;
+  return lp;
+}
+
+hipError_t launch_indexer_local(const uint8_t* k_codes,
+                                const uint8_t* k_scales, int64_t n_cap,
+                                const int32_t* n_entries,
+                                const IndexQuery& iq, int B, uint32_t* keys,
+                                const LocalPlan& lp, uint2* lcand,
+                                uint32_t* lbound, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  if (!lp.ok) return hipErrorInvalidValue;
+  const bool q4 = iq.q_scales != nullptr;
+  if (q4 && lp.tpw == 8)
+    return launch_local<true, 8>(B, s, k_codes, k_scales, n_cap, n_entries,
+                                 iq, keys, lp, lcand, lbound);
+  if (!q4 && lp.tpw == 8)
+    return launch_local<false, 8>(B, s, k_codes, k_scales, n_cap, n_entries,
+                                  iq, keys, lp, lcand, lbound);
+  if (!q4 && lp.tpw == 16)
+    return launch_local<false, 16>(B, s, k_codes, k_scales, n_cap,
+                                   n_entries, iq, keys, lp, lcand, lbound);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           const uint8_t* k_scales, int64_t n_cap,

@@ -45,6 +45,28 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           uint32_t* tmax = nullptr, uint32_t* bmax = nullptr,
                           uint32_t* btmax = nullptr, int n_div = 1);
 
+// The decode scan with local candidates (indexer_kernel LOCAL, MXFP4 keys):
+// selection keys of every row into keys[B][round32(n_cap)], and per
+// workgroup of tpw * 128 rows its local top-kloc (key, id) pairs into
+// lcand[B][n_wg][kloc] and a bound on what it left out into
+// lbound[B][n_wg].  local_plan() picks the wavefront length and kloc (at
+// least 64 pairs per group, 2k pairs in all, at most kLocalMaxCands); ok is
+// false when the row is too long for that.
+constexpr int kLocalMaxCands = 4096;
+struct LocalPlan {
+  bool ok = false;
+  int tpw = 8;
+  int n_wg = 0;
+  int kloc = 0;
+};
+LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4);
+hipError_t launch_indexer_local(const uint8_t* k_codes,
+                                const uint8_t* k_scales, int64_t n_cap,
+                                const int32_t* n_entries,
+                                const IndexQuery& iq, int B, uint32_t* keys,
+                                const LocalPlan& lp, uint2* lcand,
+                                uint32_t* lbound, hipStream_t s);
+
 // topk.hip
 // Exact per-row top-k (see topk.hip) of float scores (keys == false) or of
 // selection keys (keys == true); rows of n_cols entries at stride ld (keys:
@@ -89,12 +111,27 @@ struct AttnEpilogue {
   const int32_t* pos = nullptr;    // [B] query positions, or null
   double rope_w[32] = {};          // frequencies of the 32 pairs
 };
+// A fused selection: each attention workgroup first selects its sequence's
+// top-k itself from the local candidates of launch_indexer_local (the exact
+// block selection over the whole key row when the candidates cannot be
+// shown to hold it), writes it to topk_out, then attends over it; `topk` is
+// then unused.
+struct FusedSelect {
+  const uint2* lcand;          // [B][n_wg][kloc]
+  const uint32_t* lbound;      // [B][n_wg]
+  int n_wg, kloc;
+  const uint32_t* keys;        // [B][ld] selection keys
+  int64_t ld;
+  const int32_t* n_entries;    // [B]
+  int32_t* topk_out;           // [B][k]
+};
 hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        int64_t n_cap, const int32_t* topk, int k,
                        const uint16_t* q, const uint8_t* swa,
                        const int32_t* n_swa, int B, float scale,
                        uint16_t* out, void* ws, hipStream_t s,
-                       const AttnEpilogue& epi = AttnEpilogue{});
+                       const AttnEpilogue& epi = AttnEpilogue{},
+                       const FusedSelect* fsel = nullptr);
 
 // compress.hip
 // Workspace bytes of launch_compress (slice partials of the projections).

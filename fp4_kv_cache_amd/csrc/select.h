@@ -113,6 +113,8 @@ struct SelResult {
                       // smallest selected key, and at least min(k, valid)
                       // keys are >= thr (0 when no key is valid)
   uint32_t max;       // the largest key (the range's top when known)
+  int nval;           // valid (nonzero) keys in the block (the range's
+                      // count when known)
 };
 
 // Select the top-k (k >= 1) of the NT * PER keys held as key[j] by each
@@ -210,6 +212,7 @@ __device__ __forceinline__ SelResult block_select(
   SelResult res;
   res.thr = nval ? lo : 0u;
   res.max = mx;
+  res.nval = nval;
   if constexpr (BOUND_ONLY) {
     res.mask = 0; res.pos = 0; res.total = 0;
     if (used) {

@@ -24,6 +24,7 @@
 #include "common.h"
 #include "internal.h"
 #include "select.h"
+#include "stream_select.h"
 
 namespace csa2 {
 namespace {
@@ -34,12 +35,10 @@ namespace {
 // 11.9 us at 1024 threads, 13.1 at 512, 17.7 at 256 for 32 rows of 32,768
 // scores).
 constexpr int kNT = 1024;                   // threads per row
-constexpr int kPer = 16;                    // keys per thread
+constexpr int kPer = kStreamPer;            // keys per thread
 constexpr int kCap = kNT * kPer;            // 16384 keys per pass
 constexpr int kNB = 256;                    // bins per selection pass
 constexpr int kTileList = 4000;             // candidate tiles held in LDS
-// Winners (k <= 2048) are staged in the histograms between selections.
-static_assert(kNT / 64 * kNB >= 2048, "staging room for 2048 winners");
 
 struct RowSmem {
   uint32_t key[kCap];
@@ -76,118 +75,6 @@ __device__ __forceinline__ int wave_offset(int wcount, int& total,
   return before;
 }
 
-// Top-k of the `count` (key, id) pairs held in sm.key/sm.id (ids in
-// order): the winners are compacted, still in id order, to the front.
-// Returns their number.  PER keys per thread; count <= kNT * PER.
-template <int PER>
-__device__ __forceinline__ int select_dense(RowSmem& sm, int count, int k) {
-  const int tid = threadIdx.x;
-  uint32_t key[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {       // unconditional reads, then masks
-    const int pos = tid * PER + j;
-    const uint32_t kv = sm.key[pos];
-    key[j] = pos < count ? kv : 0u;
-  }
-  const SelResult r = block_select<kNT, PER, kNB>(key, k, sm.sel);
-  // In-order compaction of the winners (at most k <= kNB).  Every read of
-  // sm.key finished inside the selection, so keys go straight to their
-  // place; ids are staged through the (zero) histogram, which is cleared
-  // again behind them.
-  int32_t* stage = &sm.sel.hist[0][0];
-  int32_t idv[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) idv[j] = sm.id[tid * PER + j];
-  int p = r.pos;
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (r.mask & (1u << j)) {
-      stage[p] = idv[j];
-      sm.key[p] = key[j];
-      ++p;
-    }
-  __syncthreads();
-  for (int q = tid; q < r.total; q += kNT) {
-    sm.id[q] = stage[q];
-    stage[q] = 0;
-  }
-  __syncthreads();
-  return r.total;
-}
-
-__device__ __forceinline__ int select_any(RowSmem& sm, int count, int k) {
-  if (count <= kNT * 2) return select_dense<2>(sm, count, k);
-  if (count <= kNT * 8) return select_dense<8>(sm, count, k);
-  return select_dense<kPer>(sm, count, k);
-}
-
-// Streaming top-k into LDS: feeds src.load(i, value, id) for i < n (ids
-// ascending in i) through passes of up to kCap keys; afterwards
-// key/id[0..count) hold the winners in id order.
-template <typename Src>
-__device__ __forceinline__ int stream_select(RowSmem& sm, int64_t n, int k,
-                                             Src src) {
-  const int tid = threadIdx.x;
-  int count = 0;
-  int64_t pos = 0;
-  bool first = true;
-  while (first || pos < n) {
-    first = false;
-    // Fill the free slots after the current winners: loads of a half pass
-    // are all issued before their stores.
-    const int64_t room = kCap - count;
-    const int fill = (int)(n - pos < room ? n - pos : room);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      constexpr int kH = kCap / kNT / 2;
-      uint32_t fv[kH];
-      int32_t fi[kH];
-#pragma unroll
-      for (int j = 0; j < kH; ++j) {
-        // Unconditional raw loads from a clamped index (n >= 1 whenever
-        // fill > 0); keys are formed only after every load is issued.
-        const int s = (h * kH + j) * kNT + tid;
-        int64_t i = pos + (s - count);
-        i = i < 0 ? 0 : (i >= n ? (n > 0 ? n - 1 : 0) : i);
-        src.load(i, fv[j], fi[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < kH; ++j) {
-        const int s = (h * kH + j) * kNT + tid;
-        if (s >= count && s < count + fill) {
-          sm.key[s] = fi[j] >= 0 ? Src::key(fv[j]) : 0u;
-          sm.id[s] = fi[j];
-        }
-      }
-    }
-    pos += fill;
-    __syncthreads();
-    count = select_any(sm, count + fill, k);
-  }
-  return count;
-}
-
-// Element sources (ids ascending in i): load(i, r, id) reads the raw
-// 32-bit word and id of element i (always a valid index); key(r) turns the
-// word into a selection key -- it already is one when KEYS, else it is a
-// float score.
-template <bool KEYS>
-__device__ __forceinline__ uint32_t word_key(uint32_t r) {
-  if constexpr (KEYS) return r;
-  else return score_key(__uint_as_float(r));
-}
-template <bool HAS_IDS, bool KEYS>
-struct ScoreSrc {                 // a score row; ids = positions or ids[]
-  const uint32_t* row;
-  const int32_t* idrow;
-  __device__ __forceinline__ void load(int64_t i, uint32_t& r, int32_t& id) const {
-    r = row[i];
-    id = HAS_IDS ? idrow[i] : (int32_t)i;
-  }
-  __device__ static __forceinline__ uint32_t key(uint32_t r) {
-    return word_key<KEYS>(r);
-  }
-};
 template <bool KEYS>
 struct TileSrc {                  // tile maxima; ids = tile numbers
   const uint32_t* trow;
@@ -467,7 +354,7 @@ __device__ __forceinline__ void row_select_row(const RowArgs& a, int b) {
   if (count < 0) {
     // Whole-row streaming (short rows, or candidates that overflow).
     __syncthreads();
-    count = stream_select(sm, len, a.k, from_scores);
+    count = stream_select<kNT>(sm, len, a.k, from_scores);
     for (int p = tid; p < count; p += kNT) put(a, ob, lim, p, sm.id[p]);
   }
   for (int64_t p = (int64_t)count * a.block + tid; p < (int64_t)a.k * a.block;
