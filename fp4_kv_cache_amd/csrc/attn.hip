@@ -135,12 +135,21 @@ struct AttnArgs {
 };
 
 // Shared memory of the fused selection (512 threads), overlaid on the
-// attention's tile buffers, which are not in use yet.
+// attention's tile buffers, which are not in use yet: the candidate pass,
+// and over it the exact fallback's streaming store.
+struct CandSmem {
+  int32_t hist[4][256];             // one histogram per narrowing pass
+  uint32_t red[4][8];
+};
 struct FselSmem {
-  uint32_t key[512 * kStreamPer];   // the exact fallback's streaming store
-  int32_t id[512 * kStreamPer];
-  SelSmem<512, 256> sel;
-  uint32_t lmax[8];
+  union {
+    CandSmem cand;
+    struct {
+      uint32_t key[512 * kStreamPer];
+      int32_t id[512 * kStreamPer];
+      SelSmem<512, 256> sel;
+    };
+  };
 };
 constexpr int kMaxK = 2048;
 
@@ -175,17 +184,28 @@ __device__ __forceinline__ int32_t load_ids(const AttnArgs& p,
 // local candidates (the k largest pair keys, equal keys to the lower id,
 // since the pairs are in id order), into sel_ids[0..k) ascending with -1
 // padding, and into topk_out by split 0.  It is exact when the k-th largest
-// candidate key is above every group's bound (nothing a group left out can
+// candidate key is above every group's bound L (nothing a group left out can
 // then reach the top k), or, with fewer than k valid candidates, when no
 // group left anything out; otherwise the whole row's selection keys are
-// streamed through the exact block selection instead.  All 512 threads
-// take part; ends with a barrier.
+// streamed through the exact block selection instead.  So only candidates
+// above L can matter: with at least k of them, their top k is the answer;
+// with fewer, it is all of them when L = 0, else the fallback decides.
+//
+// The k-th key is found by narrowing [lo, hi] = [L + 1, max] with 256-bin
+// histograms (a fresh one per pass, so none is cleared in between): each
+// pass bins the keys still inside, and every wavefront scans the bins and
+// narrows to the bin where the count from the top reaches the number still
+// needed (the first pass also gives the count above L).  It ends on a bin
+// holding exactly that number, or on one key value (ties then go to the
+// lower positions).  One block scan places the chosen pairs in id order.
+// All 512 threads take part; ends with a barrier.
 template <int PER>
 __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
                                              int split, int32_t* sel_ids,
                                              FselSmem& fs) {
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 8 * 256; i += 512) (&fs.sel.hist[0][0])[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  CandSmem& cs = fs.cand;
+  if (tid < 256) reinterpret_cast<int4*>(&cs.hist[0][0])[tid] = make_int4(0, 0, 0, 0);
   const int C = p.n_wg * p.kloc;
   const uint2* cr = p.lcand + (int64_t)b * C;
   uint32_t kk[PER];
@@ -197,33 +217,134 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     kk[j] = i < C ? v.x : 0u;
     ci[j] = (int32_t)v.y;
   }
-  uint32_t lb = 0u;
+  uint32_t lb = 0u, km = 0u;
   for (int i = tid; i < p.n_wg; i += 512)
     lb = max(lb, p.lbound[(int64_t)b * p.n_wg + i]);
-  lb = wave_max_u32(lb);
-  if ((tid & 63) == 0) fs.lmax[tid >> 6] = lb;
-  __syncthreads();
-  uint32_t L = 0u;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) L = max(L, fs.lmax[w]);
-  const SelResult r = block_select<512, PER, 256>(kk, p.k, fs.sel);
-  const bool ok = r.nval >= p.k ? (L < r.thr) : (L == 0u);
+  for (int j = 0; j < PER; ++j) km = max(km, kk[j]);
+  lb = wave_max_u32(lb);
+  km = wave_max_u32(km);
+  if (lane == 0) {
+    cs.red[0][wv] = lb;
+    cs.red[1][wv] = km;
+  }
+  __syncthreads();
+  uint32_t L = 0u, MX = 0u;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    L = max(L, cs.red[0][w]);
+    MX = max(MX, cs.red[1][w]);
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) kk[j] = kk[j] > L ? kk[j] : 0u;
+  const int k = p.k;
+  uint32_t lo = L + 1u, hi = MX;
+  int need = k, n = 0;
+  bool take_all = MX <= L;            // no key above L
+  for (int it = 0; it < 4 && !take_all && lo < hi; ++it) {
+    int32_t* H = cs.hist[it];
+    const int bits = 32 - __builtin_clz(hi - lo);
+    const int shift = bits > 8 ? bits - 8 : 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if ((kk[j] >= lo) & (kk[j] <= hi)) atomicAdd(&H[(hi - kk[j]) >> shift], 1);
+    __syncthreads();
+    // Lane L holds bins 4L .. 4L+3 (bins in key order from the top).
+    const int4 c = reinterpret_cast<const int4*>(H)[lane];
+    const int sc = c.x + c.y + c.z + c.w;
+    const int incl = wave_incl_scan(sc);
+    if (it == 0) {
+      n = __builtin_amdgcn_readlane(incl, 63);
+      if (n <= k) { take_all = true; break; }
+    }
+    const int run = incl - sc;
+    const bool hit = (run < need) & (run + sc >= need);
+    const int hl = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(hit));
+    int bi = 0, before = run, cnt = c.x;
+    if (before + c.x < need) {
+      before += c.x; bi = 1; cnt = c.y;
+      if (before + c.y < need) {
+        before += c.y; bi = 2; cnt = c.z;
+        if (before + c.z < need) { before += c.z; bi = 3; cnt = c.w; }
+      }
+    }
+    const int bs = __builtin_amdgcn_readlane(4 * lane + bi, hl);
+    need -= __builtin_amdgcn_readlane(before, hl);
+    const bool exact = __builtin_amdgcn_readlane(cnt, hl) == need;
+    const uint32_t nhi = hi - ((uint32_t)bs << shift);
+    const uint32_t width = (1u << shift) - 1u;
+    lo = nhi - lo >= width ? nhi - width : lo;
+    hi = nhi;
+    if (exact) { take_all = true; break; }
+  }
+  if (MX > L && lo == hi && !take_all && n == 0) {
+    // One key value above L (the loop never ran): it is the k-th key when
+    // at least k keys hold it.
+    n = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) n += kk[j] != 0u;
+    n = __builtin_amdgcn_readlane(wave_incl_scan(n), 63);
+    if (lane == 0) cs.red[2][wv] = (uint32_t)n;
+    __syncthreads();
+    n = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) n += (int)cs.red[2][w];
+    take_all = n <= k;
+  }
+  const bool ok = take_all ? (n >= k || L == 0u) : true;
   int32_t* gout = (split == 0 && p.topk_out) ? p.topk_out + (int64_t)b * p.k
                                              : nullptr;
   if (ok) {
-    int q = r.pos;
+    // Chosen: take_all -> every key >= lo (all keys above L when the first
+    // pass took them all); else keys > hi (= lo) plus the first `need` keys
+    // equal to lo.  One packed scan (ties << 16 | greater).
+    int ngt = 0, ntie = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (r.mask & (1u << j)) {
+    for (int j = 0; j < PER; ++j) {
+      if (!kk[j]) continue;
+      if (take_all) ngt += kk[j] >= lo;
+      else { ngt += kk[j] > hi; ntie += kk[j] == lo; }
+    }
+    const int x = (ntie << 16) | ngt;
+    const int incl = wave_incl_scan(x);
+    if (lane == 63) cs.red[3][wv] = (uint32_t)incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int t = (int)cs.red[3][w];
+      before += w < wv ? t : 0;
+      tot += t;
+    }
+    const int ex = before + incl - x;
+    const int gt_before = ex & 0xFFFF, tie_before = ex >> 16;
+    int tie_rank = tie_before;
+    int q = gt_before + (take_all ? 0 : min(tie_before, need));
+    const int total = (tot & 0xFFFF) + (take_all ? 0 : min(tot >> 16, need));
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      bool sel = false;
+      if (kk[j]) {
+        if (take_all) sel = kk[j] >= lo;
+        else if (kk[j] > hi) sel = true;
+        else if (kk[j] == lo) { sel = tie_rank < need; ++tie_rank; }
+      }
+      if (sel) {
         sel_ids[q] = ci[j];
         if (gout) gout[q] = ci[j];
         ++q;
       }
-    for (q = r.total + tid; q < p.k; q += 512) {
+    }
+    for (q = total + tid; q < k; q += 512) {
       sel_ids[q] = -1;
       if (gout) gout[q] = -1;
     }
   } else {
+    // The exact streaming selection over the whole key row (its store
+    // overlays the candidate state, so start behind a barrier).
+    __syncthreads();
+    for (int i = tid; i < 8 * 256; i += 512) (&fs.sel.hist[0][0])[i] = 0;
+    __syncthreads();
     const int32_t ne = p.n_entries[b];
     const int64_t len = ne <= 0 ? 0 : ((int64_t)ne < p.n_cap ? ne : p.n_cap);
     const ScoreSrc<false, true> src{p.keys + (int64_t)b * p.ld, nullptr};
@@ -875,9 +996,9 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
     a.n_entries = fsel->n_entries;
     a.topk_out = fsel->topk_out;
     // Candidate pairs per thread.
-    if (C <= 512) e = launch_attn_kernel<true, 1>(a, grid, s);
-    else if (C <= 1024) e = launch_attn_kernel<true, 2>(a, grid, s);
+    if (C <= 1024) e = launch_attn_kernel<true, 2>(a, grid, s);
     else if (C <= 2048) e = launch_attn_kernel<true, 4>(a, grid, s);
+    else if (C <= 2560) e = launch_attn_kernel<true, 5>(a, grid, s);
     else e = launch_attn_kernel<true, 8>(a, grid, s);
   } else {
     e = launch_attn_kernel<false, 1>(a, grid, s);

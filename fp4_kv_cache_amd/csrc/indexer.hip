@@ -147,14 +147,16 @@ template <bool SCALED> struct Depth<1, SCALED> {
 // q_scales[B][32][4]) instead of bf16 q[B][32][128].  BLK (with KEYS):
 // the block maxima are written too.
 // LOCAL (with KEYS; all rows, no candidates): instead of tile maxima, each
-// workgroup also keeps its own local top-kloc entries as (key, id) pairs,
-// in id order, in lcand[B][gridDim.x][kloc] (key 0 / id -1 padding), and
-// in lbound[B][gridDim.x] a key at or above every valid entry it left out
-// (0 when it left none out).  The union of every workgroup's pairs then
-// holds the row's top-k whenever the k-th largest pair key is above every
-// bound: a selection over the small union is exact under that test.
+// group of rows also keeps its own local top-kloc entries as (key, id)
+// pairs, in id order, in lcand[B][groups][kloc] (key 0 / id -1 padding), and
+// in lbound[B][groups] a key at or above every valid entry it left out (0
+// when it left none out).  The union of every group's pairs then holds the
+// row's top-k whenever the k-th largest pair key is above every bound: a
+// selection over the small union is exact under that test.  A group is a
+// wavefront's rows (LOCAL == 1: no barrier, each wavefront selects alone)
+// or a workgroup's (LOCAL == 2: larger groups for long rows).
 template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false, bool CAND = false,
-          int TPW = kTilesPerWave, bool LOCAL = false>
+          int TPW = kTilesPerWave, int LOCAL = 0>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const int32_t* __restrict__ n_entries,
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int D = Depth<KEYFMT, kScaledOp>::value;
   constexpr int T = TPW;
-  static_assert(!LOCAL || (KEYS && !BLK && !CAND && KEYFMT == 0),
+  static_assert(LOCAL == 0 || (KEYS && !BLK && !CAND && KEYFMT == 0),
                 "local candidates: MXFP4 keys, all rows, selection keys");
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -184,7 +186,11 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   uint32_t* kl = lsm;
   SelSmem<256, 256>& lss =
       *reinterpret_cast<SelSmem<256, 256>*>(lsm + kWaves * T * 32);
-  if constexpr (LOCAL) {
+  if constexpr (LOCAL == 1) {
+    // Each wavefront clears its own histogram (its LDS operations take
+    // effect in order, so no barrier is needed before its selection).
+    reinterpret_cast<int4*>(lss.hist[wave])[lane] = make_int4(0, 0, 0, 0);
+  } else if constexpr (LOCAL == 2) {
     for (int i = threadIdx.x; i < kWaves * 256; i += 256)
       (&lss.hist[0][0])[i] = 0;
   } else {
@@ -359,10 +365,10 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       m = dpp_max<0x142, 0xa>(m);
       m = dpp_max<0x143, 0xc>(m);
       const uint32_t mx = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
-      if (!LOCAL && lane == 0)
+      if (LOCAL == 0 && lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
       if constexpr (BLK) wmax = max(wmax, mx);
-      if constexpr (LOCAL)
+      if constexpr (LOCAL != 0)
         if (half == 0) kl[wave * T * 32 + 32 * t + col] = key;
     } else {
       if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
@@ -372,7 +378,29 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const int64_t nbt = (((n_rows + 7) >> 3) + 31) >> 5;
     btmax[(int64_t)b * nbt + (base >> 8)] = wmax;
   }
-  if constexpr (LOCAL) {
+  if constexpr (LOCAL == 1) {
+    // Tiles past the rows hold invalid keys.  Lane i takes the wavefront's
+    // rows PER*i .. PER*i+PER-1 (position order is id order), read back
+    // from the wavefront's own stretch of LDS.
+    for (int t = nt; t < T; ++t)
+      if (half == 0) kl[wave * T * 32 + 32 * t + col] = 0u;
+    constexpr int PER = T / 2;
+    uint32_t kk[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) kk[j] = kl[wave * T * 32 + lane * PER + j];
+    const WaveSelResult r = wave_select<PER>(kk, kloc, lss.hist[wave]);
+    const int64_t grp = ((int64_t)b * gridDim.x + blockIdx.x) * kWaves + wave;
+    uint2* co = lcand + grp * kloc;
+    const uint32_t id0 = (uint32_t)(base + lane * PER);
+    int p = r.pos;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (r.mask & (1u << j)) co[p++] = make_uint2(kk[j], id0 + j);
+    for (int q = r.total + lane; q < kloc; q += 64)
+      co[q] = make_uint2(0u, 0xFFFFFFFFu);
+    if (lane == 0) lbound[grp] = r.nval > kloc ? r.thr : 0u;
+  }
+  if constexpr (LOCAL == 2) {
     // Tiles past the rows hold invalid keys.
     for (int t = nt; t < T; ++t)
       if (half == 0) kl[wave * T * 32 + 32 * t + col] = 0u;
@@ -460,18 +488,20 @@ void launch_q(int B, hipStream_t s, const void* k_codes,
                                     n_entries, cand, n_rows, iq, scores, tmax,
                                     bmax, btmax, n_div);
 }
-template <bool QFP4, int T>
+template <bool QFP4, int T, int LOCAL>
 hipError_t launch_local(int B, hipStream_t s, const void* k_codes,
                         const uint8_t* k_scales, int64_t n_cap,
                         const int32_t* n_entries, const IndexQuery& iq,
                         uint32_t* keys, const LocalPlan& lp, uint2* lcand,
                         uint32_t* lbound) {
   const int smem = (kWaves * T * 32 + kWaves * 256 + 16) * 4;
-  hipLaunchKernelGGL((indexer_kernel<0, true, QFP4, false, false, T, true>),
-                     dim3((unsigned)lp.n_wg, (unsigned)B), dim3(256), smem, s,
-                     k_codes, k_scales, n_cap, n_entries, nullptr, n_cap,
-                     iq.q, iq.q_scales, iq.w, reinterpret_cast<float*>(keys),
-                     nullptr, nullptr, nullptr, 1, lcand, lbound, lp.kloc);
+  const int64_t epb = (int64_t)kWaves * T * 32;
+  hipLaunchKernelGGL(
+      (indexer_kernel<0, true, QFP4, false, false, T, LOCAL>),
+      dim3((unsigned)((n_cap + epb - 1) / epb), (unsigned)B), dim3(256), smem,
+      s, k_codes, k_scales, n_cap, n_entries, nullptr, n_cap, iq.q,
+      iq.q_scales, iq.w, reinterpret_cast<float*>(keys), nullptr, nullptr,
+      nullptr, 1, lcand, lbound, lp.kloc);
   return hipGetLastError();
 }
 }  // namespace
@@ -483,18 +513,28 @@ LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4) {
   const int64_t per8 = (int64_t)kWaves * 8 * 32;
   const int64_t waves8 = ((n_cap + per8 - 1) / per8) * (int64_t)B * kWaves;
   lp.tpw = (!qfp4 && waves8 >= kLongScanWaves) ? 16 : 8;
-  const int64_t epw = (int64_t)kWaves * lp.tpw * 32;      // rows per group
-  const int64_t n_wg = (n_cap + epw - 1) / epw;
-  if (n_wg > kLocalMaxCands / 8) return lp;
-  // At least 64 pairs per group (a group expects k * epw / n of the row's
-  // winners), at least 2k pairs in all, at most kLocalMaxCands in all.
-  int64_t kl = std::max<int64_t>(64, (2 * (int64_t)k + n_wg - 1) / n_wg);
-  kl = std::min<int64_t>(kl, epw);
-  kl = std::min<int64_t>(kl, kLocalMaxCands / n_wg);
-  if (kl < 8 || kl * n_wg < 2 * (int64_t)k) return lp;
-  lp.ok = true;
-  lp.n_wg = (int)n_wg;
-  lp.kloc = (int)kl;
+  const int64_t epb = (int64_t)kWaves * lp.tpw * 32;      // rows per workgroup
+  const int64_t n_wg = (n_cap + epb - 1) / epb;
+  // Groups of one wavefront's rows while every group can keep 20 pairs (a
+  // group expects k * rows / n of the row's winners: 4 for 512 of 32,768
+  // in 256 rows, so 20 are exceeded with probability ~1e-9 on independent
+  // scores), else groups of a workgroup's rows keeping 16 or more.
+  for (int per_wave = 1; per_wave >= 0; --per_wave) {
+    const int64_t groups = per_wave ? n_wg * kWaves : n_wg;
+    const int64_t rows = per_wave ? epb / kWaves : epb;
+    const int64_t kmin = per_wave ? 20 : 16;
+    int64_t kl = std::max<int64_t>(per_wave ? 20 : 64,
+                                   (2 * (int64_t)k + groups - 1) / groups);
+    kl = std::min<int64_t>(kl, rows);
+    kl = std::min<int64_t>(kl, kLocalMaxCands / groups);
+    if (kl < std::min<int64_t>(kmin, rows) || kl * groups < 2 * (int64_t)k)
+      continue;
+    lp.ok = true;
+    lp.per_wave = per_wave != 0;
+    lp.n_wg = (int)groups;
+    lp.kloc = (int)kl;
+    return lp;
+  }
   return lp;
 }
 
@@ -507,15 +547,17 @@ hipError_t launch_indexer_local(const uint8_t* k_codes,
   if (B == 0) return hipSuccess;
   if (!lp.ok) return hipErrorInvalidValue;
   const bool q4 = iq.q_scales != nullptr;
-  if (q4 && lp.tpw == 8)
-    return launch_local<true, 8>(B, s, k_codes, k_scales, n_cap, n_entries,
+#define CSA2_LOCAL(Q, T, L)                                                  \
+  if (q4 == Q && lp.tpw == T && (lp.per_wave ? 1 : 2) == L)                  \
+    return launch_local<Q, T, L>(B, s, k_codes, k_scales, n_cap, n_entries,  \
                                  iq, keys, lp, lcand, lbound);
-  if (!q4 && lp.tpw == 8)
-    return launch_local<false, 8>(B, s, k_codes, k_scales, n_cap, n_entries,
-                                  iq, keys, lp, lcand, lbound);
-  if (!q4 && lp.tpw == 16)
-    return launch_local<false, 16>(B, s, k_codes, k_scales, n_cap,
-                                   n_entries, iq, keys, lp, lcand, lbound);
+  CSA2_LOCAL(true, 8, 1)
+  CSA2_LOCAL(true, 8, 2)
+  CSA2_LOCAL(false, 8, 1)
+  CSA2_LOCAL(false, 8, 2)
+  CSA2_LOCAL(false, 16, 1)
+  CSA2_LOCAL(false, 16, 2)
+#undef CSA2_LOCAL
   return hipErrorInvalidValue;
 }
 

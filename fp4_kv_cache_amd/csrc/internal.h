@@ -46,15 +46,16 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
                           uint32_t* btmax = nullptr, int n_div = 1);
 
 // The decode scan with local candidates (indexer_kernel LOCAL, MXFP4 keys):
-// selection keys of every row into keys[B][round32(n_cap)], and per
-// workgroup of tpw * 128 rows its local top-kloc (key, id) pairs into
-// lcand[B][n_wg][kloc] and a bound on what it left out into
-// lbound[B][n_wg].  local_plan() picks the wavefront length and kloc (at
-// least 64 pairs per group, 2k pairs in all, at most kLocalMaxCands); ok is
-// false when the row is too long for that.
+// selection keys of every row into keys[B][round32(n_cap)], and per group
+// of rows (a wavefront's tpw * 32 rows, or a workgroup's tpw * 128) its
+// local top-kloc (key, id) pairs into lcand[B][n_wg][kloc] and a bound on
+// what it left out into lbound[B][n_wg] (n_wg = groups per row).
+// local_plan() picks the wavefront length, the group and kloc (2k pairs in
+// all, at most kLocalMaxCands); ok is false when the row is too long.
 constexpr int kLocalMaxCands = 4096;
 struct LocalPlan {
   bool ok = false;
+  bool per_wave = false;
   int tpw = 8;
   int n_wg = 0;
   int kloc = 0;

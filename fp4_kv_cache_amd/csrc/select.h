@@ -267,3 +267,108 @@ __device__ __forceinline__ SelResult block_select(
 }
 
 }  // namespace csa2
+
+namespace csa2 {
+
+// ---------------------------------------------------- wavefront select --
+struct WaveSelResult {
+  uint32_t mask;      // selected elements of this lane (bit j)
+  int pos;            // selected elements before this lane
+  int total;          // selected in the wavefront: min(k, valid keys)
+  uint32_t thr;       // as SelResult::thr: every valid key left out is
+                      // <= thr, and thr <= the smallest selected key
+  int nval;           // valid (nonzero) keys in the wavefront
+};
+
+// Top-k (k >= 1) of the 64 * PER keys held as key[j] by the lanes of one
+// wavefront, position = lane * PER + j; larger key first, equal keys to the
+// lower position.  The same interval narrowing as block_select, with no
+// barrier: H is 256 ints of LDS used by this wavefront alone (zero on entry,
+// zero again on return).  The wavefront's own LDS operations take effect in
+// issue order, so each pass reads its histogram after its atomics and each
+// lane clears the four bins it read before the next pass adds to them.
+template <int PER>
+__device__ __forceinline__ WaveSelResult wave_select(const uint32_t (&key)[PER],
+                                                     int k, int32_t* H) {
+  static_assert(PER <= 32, "selection mask is 32 bits");
+  static_assert(64 * PER < 65536, "packed counts are 16 bits");
+  constexpr int kLogNB = 8;
+  const int lane = threadIdx.x & 63;
+  int nval = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (key[j]) { ++nval; mn = min(mn, key[j]); mx = max(mx, key[j]); }
+  nval = __builtin_amdgcn_readlane(wave_incl_scan(nval), 63);
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  uint32_t lo = mn, hi = mx;
+  int need = k;
+  bool take_all = nval <= k;
+  if (!take_all) {
+    for (int it = 0; it < 4 && lo < hi; ++it) {
+      const int bits = 32 - __builtin_clz(hi - lo);
+      const int shift = bits > kLogNB ? bits - kLogNB : 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if ((key[j] >= lo) & (key[j] <= hi))
+          atomicAdd(&H[(hi - key[j]) >> shift], 1);
+      int4* hv = reinterpret_cast<int4*>(H) + lane;
+      const int4 c = *hv;
+      *hv = make_int4(0, 0, 0, 0);
+      const int s = c.x + c.y + c.z + c.w;
+      const int run = wave_incl_scan(s) - s;
+      const bool hit = (run < need) & (run + s >= need);
+      const int hl = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(hit));
+      int b = 0, before = run, cnt = c.x;
+      if (before + c.x < need) {
+        before += c.x; b = 1; cnt = c.y;
+        if (before + c.y < need) {
+          before += c.y; b = 2; cnt = c.z;
+          if (before + c.z < need) { before += c.z; b = 3; cnt = c.w; }
+        }
+      }
+      const int bs = __builtin_amdgcn_readlane(4 * lane + b, hl);
+      need -= __builtin_amdgcn_readlane(before, hl);
+      const bool exact = __builtin_amdgcn_readlane(cnt, hl) == need;
+      const uint32_t nhi = hi - ((uint32_t)bs << shift);
+      const uint32_t width = (1u << shift) - 1u;
+      lo = nhi - lo >= width ? nhi - width : lo;
+      hi = nhi;
+      if (exact) { take_all = true; break; }
+    }
+  }
+  WaveSelResult res;
+  res.thr = nval ? lo : 0u;
+  res.nval = nval;
+  int ngt = 0, ntie = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (!key[j]) continue;
+    if (take_all) ngt += key[j] >= lo;
+    else { ngt += key[j] > hi; ntie += key[j] == lo; }
+  }
+  const int x = (ntie << 16) | ngt;
+  const int incl = wave_incl_scan(x);
+  const int tot = __builtin_amdgcn_readlane(incl, 63);
+  const int ex = incl - x;
+  const int gt_before = ex & 0xFFFF, tie_before = ex >> 16;
+  int tie_rank = tie_before;
+  uint32_t mask = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    bool sel = false;
+    if (key[j]) {
+      if (take_all) sel = key[j] >= lo;
+      else if (key[j] > hi) sel = true;
+      else if (key[j] == lo) { sel = tie_rank < need; ++tie_rank; }
+    }
+    if (sel) mask |= 1u << j;
+  }
+  res.mask = mask;
+  res.pos = gt_before + (take_all ? 0 : min(tie_before, need));
+  res.total = (tot & 0xFFFF) + (take_all ? 0 : min(tot >> 16, need));
+  return res;
+}
+
+}  // namespace csa2
