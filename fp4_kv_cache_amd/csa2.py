@@ -24,6 +24,7 @@ EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
            "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_fp4q",
            "csa2_full_pool_decode", "csa2_reindex_decode", "csa2_reuse_attn",
            "csa2_sparse_attn_decode_ex", "csa2_reuse_attn_ex",
+           "csa2_sparse_attn_decode_noalloc",
            "csa2_compress_append", "csa2_workspace_size", "csa2_entry_bytes",
            "csa2_kv_bytes_per_token", "csa2_last_error", "csa2_version"]
 
@@ -111,6 +112,11 @@ def load(path=None):
                                              ctypes.POINTER(PoolOpts),
                                              ctypes.POINTER(AttnOpts), P, P,
                                              P, SZ, P]),
+        "csa2_sparse_attn_decode_noalloc": (I32, [ctypes.POINTER(CacheDesc),
+                                                  P, P, P, P, P, I32, I32,
+                                                  F32,
+                                                  ctypes.POINTER(PoolOpts), P,
+                                                  P, P]),
         "csa2_reuse_attn_ex": (I32, [P, P, I64, P, I32, P, P, P, I32, F32,
                                      ctypes.POINTER(AttnOpts), P, P, SZ, P]),
         "csa2_compress_append": (I32, [P, I32, I32, I32, P, P, P, P, P, P, P,
@@ -315,6 +321,25 @@ def sparse_attn_decode(cache, q_idx, w, q, swa, n_swa, k, scale, pool=None,
             _ptr(n_swa), B, k, float(scale), ctypes.byref(po) if po else None,
             ctypes.byref(ao), _ptr(out), _ptr(topk_out), _ptr(ws), ws.numel(),
             _stream()))
+    return out, topk_out
+
+
+def sparse_attn_decode_noalloc(cache, q_idx, w, q, swa, n_swa, k, scale,
+                               pool=None, out=None, topk_out=None):
+    """sparse_attn_decode without a workspace: the library's own fixed
+    scratch array (csa2_sparse_attn_decode_noalloc).  The outputs must be
+    given by callers that cannot allocate."""
+    B = q.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
+    if topk_out is None:
+        topk_out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    po = PoolOpts(*pool) if pool is not None else None
+    _check(load().csa2_sparse_attn_decode_noalloc(
+        ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
+        _ptr(n_swa), B, k, float(scale), ctypes.byref(po) if po else None,
+        _ptr(out), _ptr(topk_out), _stream()))
     return out, topk_out
 
 

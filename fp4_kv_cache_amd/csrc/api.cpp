@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "csa2.h"
 #include "internal.h"
@@ -603,6 +604,77 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache* kv,
                                     size_t ws_bytes, void* stream) {
   return decode_impl(kv, csa2::IndexQuery{q_idx, nullptr, w}, q, swa, n_swa,
                      B, k, scale, pool, out, topk_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// The decode workspace of csa2_sparse_attn_decode_noalloc: a fixed device
+// array of the library, one copy per GPU, living until the process ends.
+// Host code never passes `scratch` itself to a kernel (in host code the
+// name is only a stand-in for the symbol): the device address of each GPU's
+// copy is looked up once per device, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on first use).
+csa2_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "no HIP device");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CSA2_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "scratch symbol address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_sparse_attn_decode_noalloc(
+    const csa2_cache* kv, const uint16_t* q_idx, const float* w,
+    const uint16_t* q, const uint8_t* swa, const int32_t* n_swa, int32_t B,
+    int32_t k, float scale, const csa2_pool_opts* pool, uint16_t* out,
+    int32_t* topk_out, void* stream) {
+  if (B < 0 || !kv || kv->n_cap < 0 || kv->n_cap > kMaxCap || k < 1 ||
+      k > kMaxK)
+    return decode_impl(kv, csa2::IndexQuery{q_idx, nullptr, w}, q, swa,
+                       n_swa, B, k, scale, pool, out, topk_out, nullptr, 0,
+                       stream);                 // reports the argument error
+  if (pool && check_pool(pool)) return CSA2_ERR_UNSUPPORTED;
+  // Far beyond the scratch array anyway; keeps the layout sums in range.
+  if ((uint64_t)B * (uint64_t)round32(kv->n_cap) > ((uint64_t)1 << 40))
+    return fail(CSA2_ERR_WORKSPACE, "csa2_sparse_attn_decode_noalloc: B * "
+                "n_cap is far beyond the %zu-byte scratch array",
+                (size_t)CSA2_NOALLOC_SCRATCH_BYTES);
+  const size_t need = decode_layout(B, kv->n_cap, k, pool).total;
+  if (need > CSA2_NOALLOC_SCRATCH_BYTES)
+    return fail(CSA2_ERR_WORKSPACE,
+                "csa2_sparse_attn_decode_noalloc: this call needs %zu bytes "
+                "of scratch, the library holds %zu (use "
+                "csa2_sparse_attn_decode with a workspace)", need,
+                (size_t)CSA2_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  csa2_status st = scratch_for_current_device(&ws);
+  if (st) return st;
+  // Nothing in the decode workspace has to start at zero: every kernel
+  // writes what it later reads in the same call.
+  return decode_impl(kv, csa2::IndexQuery{q_idx, nullptr, w}, q, swa, n_swa,
+                     B, k, scale, pool, out, topk_out, ws,
+                     CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 csa2_status csa2_sparse_attn_decode_fp4q(

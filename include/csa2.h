@@ -29,7 +29,11 @@
  *     any launch; on error nothing is enqueued and csa2_last_error() (a
  *     thread-local string) says why.  No exceptions cross the ABI.
  *   - Outputs must not overlap inputs.  Calls on distinct streams are
- *     thread-safe (the library holds no mutable global state).
+ *     thread-safe.  The library's only mutable global state is a set of
+ *     per-device, set-once flags and addresses (kernel LDS limits, the
+ *     location of csa2_sparse_attn_decode_noalloc's scratch array), plus
+ *     that scratch array itself, which is shared by every call of that one
+ *     entry point on a device (see there).
  *   - Results are bitwise deterministic for fixed inputs and launch shapes.
  *   - bf16 values are passed as uint16_t bit patterns.
  *
@@ -222,6 +226,26 @@ csa2_status csa2_sparse_attn_decode(const csa2_cache *kv,
                                     float scale, const csa2_pool_opts *pool,
                                     uint16_t *out, int32_t *topk_out, void *ws,
                                     size_t ws_bytes, void *stream);
+
+/* csa2_sparse_attn_decode_noalloc -- csa2_sparse_attn_decode for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same call without a
+ * workspace.  Its scratch is a fixed array inside the library, one copy per
+ * GPU, of CSA2_NOALLOC_SCRATCH_BYTES; the library looks up the current
+ * device's copy on the first call on that device and allocates nothing,
+ * ever.  A call whose workspace (csa2_workspace_size(CSA2_OP_DECODE, B,
+ * n_cap, k, pool)) exceeds the array fails with CSA2_ERR_WORKSPACE and
+ * enqueues nothing: 32 MiB covers 32 sequences of 32,768 entries at
+ * k = 512.  Every call on a GPU uses the same array, so calls that overlap
+ * on one GPU (on different streams, or from different threads) race and
+ * must be ordered by the caller; nothing in it needs to start at zero.
+ * Arguments, outputs and errors otherwise as csa2_sparse_attn_decode. */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+csa2_status csa2_sparse_attn_decode_noalloc(
+    const csa2_cache *kv, const uint16_t *q_idx, const float *w,
+    const uint16_t *q, const uint8_t *swa, const int32_t *n_swa, int32_t B,
+    int32_t k, float scale, const csa2_pool_opts *pool, uint16_t *out,
+    int32_t *topk_out, void *stream);
 
 /* csa2_sparse_attn_decode_fp4q -- csa2_sparse_attn_decode with the
  * indexer query in MXFP4 planes (q_codes [B][32][64], q_scales [B][32][4],
