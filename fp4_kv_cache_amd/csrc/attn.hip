@@ -198,11 +198,12 @@ __device__ __forceinline__ int32_t load_ids(const AttnArgs& p,
 // needed (the first pass also gives the count above L).  It ends on a bin
 // holding exactly that number, or on one key value (ties then go to the
 // lower positions).  One block scan places the chosen pairs in id order.
-// All 512 threads take part; ends with a barrier.
+// All 512 threads take part; ends with a barrier.  Only LDS is written here:
+// a global store before that barrier would make every wavefront wait at it
+// for the store to complete, so the ids go to topk_out at the kernel's end.
 template <int PER>
 __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
-                                             int split, int32_t* sel_ids,
-                                             FselSmem& fs) {
+                                             int32_t* sel_ids, FselSmem& fs) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   CandSmem& cs = fs.cand;
   if (tid < 256) reinterpret_cast<int4*>(&cs.hist[0][0])[tid] = make_int4(0, 0, 0, 0);
@@ -292,8 +293,6 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     take_all = n <= k;
   }
   const bool ok = take_all ? (n >= k || L == 0u) : true;
-  int32_t* gout = (split == 0 && p.topk_out) ? p.topk_out + (int64_t)b * p.k
-                                             : nullptr;
   if (ok) {
     // Chosen: take_all -> every key >= lo (all keys above L when the first
     // pass took them all); else keys > hi (= lo) plus the first `need` keys
@@ -329,16 +328,9 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
         else if (kk[j] > hi) sel = true;
         else if (kk[j] == lo) { sel = tie_rank < need; ++tie_rank; }
       }
-      if (sel) {
-        sel_ids[q] = ci[j];
-        if (gout) gout[q] = ci[j];
-        ++q;
-      }
+      if (sel) sel_ids[q++] = ci[j];
     }
-    for (q = total + tid; q < k; q += 512) {
-      sel_ids[q] = -1;
-      if (gout) gout[q] = -1;
-    }
+    for (q = total + tid; q < k; q += 512) sel_ids[q] = -1;
   } else {
     // The exact streaming selection over the whole key row (its store
     // overlays the candidate state, so start behind a barrier).
@@ -349,11 +341,7 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     const int64_t len = ne <= 0 ? 0 : ((int64_t)ne < p.n_cap ? ne : p.n_cap);
     const ScoreSrc<false, true> src{p.keys + (int64_t)b * p.ld, nullptr};
     const int cnt = stream_select<512>(fs, len, p.k, src);
-    for (int q = tid; q < p.k; q += 512) {
-      const int32_t v = q < cnt ? fs.id[q] : -1;
-      sel_ids[q] = v;
-      if (gout) gout[q] = v;
-    }
+    for (int q = tid; q < p.k; q += 512) sel_ids[q] = q < cnt ? fs.id[q] : -1;
   }
   __syncthreads();
 }
@@ -706,8 +694,7 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
     for (int s = 0; s < 16; ++s) qraw[s] = qr[4 * s];
   }
   if constexpr (FSEL)
-    fused_select<CPER>(p, b, split, sel_ids,
-                       *reinterpret_cast<FselSmem*>(smem_raw));
+    fused_select<CPER>(p, b, sel_ids, *reinterpret_cast<FselSmem*>(smem_raw));
   if (is_math) {
     // The query converted to fp16; the accumulators are zeroed after the
     // conversion (the raw query is dead by then).
@@ -829,6 +816,10 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
     p.part_ml[ps * 2 + 0] = m_run;
     p.part_ml[ps * 2 + 1] = l_tot;
   }
+  // The selected ids (still in LDS: the staging above stays below them).
+  if (FSEL && split == 0 && p.topk_out != nullptr)
+    for (int q = threadIdx.x; q < p.k; q += 512)
+      p.topk_out[(int64_t)b * p.k + q] = sel_ids[q];
 }
 
 // Merge of split partials: one wavefront per (sequence, head), lane d8
