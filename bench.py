@@ -1,12 +1,23 @@
 """Benchmark of the CSA2 decode hot path on one MI355X.
 
-A step is one Full-layer decode call (csa2_sparse_attn_decode: indexer scan,
-exact top-512, FP4 gather + dequant, 64-head attention over the selection
-plus the 128-row window) for every sequence of the 64K-context workload
-(32 sequences x 32,768 MXFP4/FP4 entries).  Inputs are resident in HBM
-before timing; the caches are replicated and rotated so the 256 MB
-last-level cache cannot serve one call's data to the next (each call reads
-~83 MB; 8 replicas put >= 512 MB between two uses of one replica).
+A step is one pass of the whole decode path for every sequence of a
+workload: the indexer scan with exact top-512, the FP4 gather + dequant and
+the 64-head attention over the selection plus the 128-row window (one
+csa2_sparse_attn_decode call; for the decoder-group workload, the Full
+layer's call plus its three Reuse layers' csa2_reuse_attn calls).  The
+headline is the 64K-context encoder Full layer (32 sequences x 32,768
+entries); the other full-size workloads are reported in the same line under
+"configs".  Inputs are resident in HBM before timing; the caches are
+replicated and rotated so the 256 MB last-level cache cannot serve one
+call's data to the next (each replica is reused only after >= 512 MB of
+other traffic).
+
+Timing: W eager warmup steps, then one HIP graph of exactly K steps (step i
+on replica i mod R), replayed once untimed and once timed between two
+device synchronisations; the graph's result must equal the eager one bit for
+bit.  Per-kernel durations come from HIP events that the library records
+around each kernel of M eager steps (csa2_set_launch_events), queued behind
+a spin kernel so host enqueue time stays hidden.
 
 Prints ONE JSON line.  `python bench.py --gpus N --steps K --warmup W`.
 """
@@ -24,26 +35,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "indexer_encoder-full-64k_traffic.json")
+HEADLINE = 1
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="1,2,3,4",
+                    help="workload ids; the first is the headline")
     ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--kernel-steps", type=int, default=40,
+                    help="eager steps timed per kernel with launch events")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--query", choices=("bf16", "mxfp4"), default="bf16",
-                    help="indexer query format of the headline step (the "
-                         "other is reported under variants)")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="counter-collection run: plain indexer launches on "
-                         "rotated cache replicas, then a float32 copy kernel "
-                         "of known size (read 256 MiB, write 256 MiB) to "
-                         "calibrate FETCH_SIZE / WRITE_SIZE")
+                    help="counter-collection run: M decode steps of the "
+                         "64K workload on rotated cache replicas, then a "
+                         "float32 copy kernel of known size (read 256 MiB, "
+                         "write 256 MiB) to calibrate FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -57,23 +69,31 @@ def query_bytes(query):
     return 32 * 68 if query == "mxfp4" else 32 * 128 * 2
 
 
+def reuse_bytes(wl):
+    """Bytes one Reuse layer must move per sequence: 288 k (chosen main
+    entries), 512 n_swa (its window), 4 k (the Full layer's ids), 65536
+    (bf16 query) and 65536 (bf16 output)."""
+    return 288 * wl.k + 512 * wl.n_swa + 4 * wl.k + 65536 + 65536
+
+
 def algorithmic_bytes(wl, query="bf16"):
-    """Bytes the method must move for one query through a Full layer:
-    the indexer keys scanned (68 n; hierarchically 256 per bf16 block key
-    plus 68 per pool member), 288 k (chosen main entries), 512 n_swa
-    (window), the indexer query (8192 bf16 or 2176 MXFP4) + 128 (head
-    weights), 65536 (bf16 query), 65536 (bf16 output) and 4 k (top-k ids
-    written)."""
+    """Bytes the method must move per sequence for one step: the indexer
+    keys scanned (68 n; hierarchically 256 per bf16 block key plus 68 per
+    pool member), 288 k (chosen main entries), 512 n_swa (window), the
+    indexer query (8192 bf16 or 2176 MXFP4) + 128 (head weights), 65536
+    (bf16 query), 65536 (bf16 output) and 4 k (top-k ids written); plus the
+    Reuse layers of a decoder group."""
     scan = (256 * n_blocks(wl) + 68 * wl.pool[0] * wl.pool[1] if wl.pool
             else 68 * wl.n)
-    return (scan + 288 * wl.k + 512 * wl.n_swa + query_bytes(query) + 128
+    full = (scan + 288 * wl.k + 512 * wl.n_swa + query_bytes(query) + 128
             + 65536 + 65536 + 4 * wl.k)
+    return full + wl.reuse_layers * reuse_bytes(wl)
 
 
-def indexer_bytes(wl, query="bf16"):
-    """Algorithmic bytes of one launch of the scan kernel the roofline is
-    quoted on: the MXFP4 keys of every visible entry (hierarchically: the
-    bf16 block keys of every block) plus the per-sequence query and
+def scan_bytes(wl, query="bf16"):
+    """Algorithmic bytes of one launch of the step's scan kernel (the
+    roofline kernel): the MXFP4 keys of every visible entry (hierarchically:
+    the bf16 block keys of every block) plus each sequence's query and
     weights."""
     per = 256 * n_blocks(wl) if wl.pool else 68 * wl.n
     return wl.B * (per + query_bytes(query) + 128)
@@ -81,16 +101,16 @@ def indexer_bytes(wl, query="bf16"):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("indexer.hip", "common.h"):
+    for f in ("indexer.hip", "common.h", "select.h"):
         with open(os.path.join(ROOT, "fp4_kv_cache_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(query):
-    """HBM bytes per indexer launch (the scan with a bf16 or an MXFP4 query)
-    from the committed rocprofv3 counter summary, or None when it is absent
-    or the kernel changed since."""
+def traffic_from_profile():
+    """HBM bytes per launch of the in-step scan of the 64K workload from the
+    committed rocprofv3 counter summary, or None when it is absent or the
+    kernel source changed since."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             prof = json.load(f)
@@ -98,7 +118,7 @@ def traffic_from_profile(query):
         return None
     if prof.get("source_hash") != source_hash():
         return None
-    return prof.get("kernels", {}).get(query, {}).get("hbm_bytes_per_launch")
+    return prof.get("hbm_bytes_per_launch")
 
 
 def replicate(st, R):
@@ -120,69 +140,109 @@ def replicate(st, R):
     return reps, planes
 
 
-def time_steps(step, args, R, out, ids):
-    """Eager and HIP-graph time per step of `step(i)` (i picks the cache
-    replica).  The graph holds one step per replica (R steps) and is
-    replayed until at least K steps have run; a replay must reproduce the
-    eager result bit for bit.  After the timed region, further replays are
-    timed one by one with events for the spread (p10 / p50 / p90 of the time
-    per step within a replay)."""
-    import numpy as np
+def graph_time(step, K, W, outs):
+    """W eager warmup steps, then one HIP graph of exactly K steps (step(i)
+    for i < K), replayed once untimed and once timed between device
+    synchronisations.  The replay must reproduce the eager result of step
+    K-1 bit for bit (`outs`: the step's output tensors).  Returns the
+    seconds per step of the timed replay and of K eager steps."""
     import torch
-    for i in range(args.warmup):
+    for i in range(W):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(K):
         step(i)
     torch.cuda.synchronize()
-    eager_s = (time.perf_counter() - t0) / args.steps
-    if args.no_graph:
-        return eager_s, None, args.steps, None
+    eager_s = (time.perf_counter() - t0) / K
+    ref = [o.clone() for o in outs]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for r in range(R):
-            step(r)          # warm the capture path on this stream
+        step(0)                           # warm the capture path
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for r in range(R):
-            step(r)
-    reps_needed = max(1, math.ceil(args.steps / R))
-    steps_run = reps_needed * R
-    for _ in range(max(1, args.warmup // R)):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps_needed):
-        g.replay()
-    torch.cuda.synchronize()
-    graph_s = (time.perf_counter() - t0) / steps_run
-    per_step = []
-    for _ in range(max(10, min(reps_needed, 50))):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        e1.synchronize()
-        per_step.append(e0.elapsed_time(e1) * 1e3 / R)
-    spread = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
-    spread.update(replays=len(per_step), steps_per_replay=R)
-    step(R - 1)
-    torch.cuda.synchronize()
-    e_out, e_ids = out.clone(), ids.clone()
+        for i in range(K):
+            step(i)
     g.replay()
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), e_out.view(torch.int16))
-    assert torch.equal(ids, e_ids)
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t0) / K
+    for o, r in zip(outs, ref):
+        assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), \
+            "graph replay differs from the eager step"
     del g
-    return eager_s, graph_s, steps_run, spread
+    return graph_s, eager_s
 
 
-def run_gpu(args, wl):
+class HipEvents:
+    """Timing events of the HIP runtime, created with
+    hipEventDisableSystemFence (0x20000000): recording one performs no
+    system-scope cache write-back, so it neither costs nor disturbs the
+    kernels it brackets."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            st = self.hip.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000)
+            assert st == 0, f"hipEventCreateWithFlags: {st}"
+            self.ev.append(e)
+
+    def elapsed(self, a, b):
+        ms = self.ct.c_float()
+        st = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[a],
+                                          self.ev[b])
+        assert st == 0, f"hipEventElapsedTime: {st}"
+        return ms.value * 1e-3
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def kernel_times(step, M, names):
+    """Mean duration of each kernel of the step as it runs inside it: M
+    eager steps, each with its own HIP events recorded by the library on
+    the step's stream before its first kernel and after each kernel, all
+    queued behind a spin kernel.  `names`: the step's kernels in launch
+    order."""
+    import torch
+    from fp4_kv_cache_amd import csa2
+    n = len(names) + 1
+    ev = HipEvents(M * n)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)
+    for i in range(M):
+        csa2.set_launch_events(ev.ev[i * n:(i + 1) * n])
+        step(i)
+    csa2.set_launch_events([])
+    torch.cuda.synchronize()
+    out = {}
+    for j, name in enumerate(names):
+        d = [ev.elapsed(i * n + j, i * n + j + 1) for i in range(M)]
+        assert min(d) > 0, (name, min(d))
+        out[name] = sum(d) / M
+    ev.close()
+    return out
+
+
+def decode_kernels(wl):
+    """The kernels of one decode call, in launch order."""
+    if wl.pool:
+        return ["block_scan", "block_topk", "pool_scan", "pool_topk",
+                "attention", "split_merge"]
+    return ["scan_local_topk", "attention_fused_select", "split_merge"]
+
+
+def run_workload(args, wl, headline):
     import torch
     from fp4_kv_cache_amd import csa2, workload
 
@@ -196,14 +256,89 @@ def run_gpu(args, wl):
     ids = torch.empty((wl.B, k), dtype=torch.int32, device=dev)
     ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, wl.B, wl.n, k,
                                             wl.pool), dev)
-    # The MXFP4 indexer query (V4's FP4 indexer query): an input of the
-    # layer call like the bf16 one, packed once outside the timed steps.
-    qc, qs = csa2.pack_query_fp4(st.q_idx)
+    ws_r = csa2.workspace(csa2.workspace_size(csa2.OP_REUSE, wl.B, wl.n, k),
+                          dev)
+    outs_r = [torch.empty_like(out) for _ in range(wl.reuse_layers)]
 
-    def step_bf16(i):
+    def full(i):
         csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
                                 st.swa[0], st.n_swa, k, st.scale,
                                 pool=wl.pool, out=out, topk_out=ids, ws=ws)
+
+    def reuse(i, layer):
+        pl = planes[i % R]
+        csa2.reuse_attn(pl[0], pl[1], ids, st.q[layer], st.swa[layer],
+                        st.n_swa, st.scale, out=outs_r[layer - 1], ws=ws_r)
+
+    def step(i):
+        full(i)
+        for layer in range(1, 1 + wl.reuse_layers):
+            reuse(i, layer)
+
+    K, W = args.steps, args.warmup
+    step_s, eager_s = graph_time(step, K, W, [out, ids] + outs_r)
+    M = args.kernel_steps
+    kern = kernel_times(full, M, decode_kernels(wl))
+    if wl.reuse_layers:
+        r = kernel_times(lambda i: reuse(i, 1), M, ["attention", "split_merge"])
+        kern.update({f"reuse_{n}": v for n, v in r.items()})
+    scan_name = "block_scan" if wl.pool else "scan_local_topk"
+    t_scan = kern[scan_name]
+    achieved = scan_bytes(wl) / t_scan / 1e9
+    layers = 1 + wl.reuse_layers
+    res = {
+        "workload": wl.name,
+        "value": wl.B * layers / step_s,
+        "unit": "query-tokens/s per layer",
+        "ms_per_step": step_s * 1e3,
+        "steps": K,
+        "warmup": W,
+        "layers_per_step": layers,
+        "eager_ms_per_step": eager_s * 1e3,
+        "config": {"global_batch": wl.B, "entries_per_seq": wl.n,
+                   "context": wl.ctx, "m": wl.m, "k": k, "n_swa": wl.n_swa,
+                   "reuse_layers": wl.reuse_layers,
+                   "planted_fraction": wl.planted,
+                   "pool": list(wl.pool) if wl.pool else None,
+                   "cache_replicas": R},
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic_from_profile() if wl.cid == HEADLINE else None,
+            "kernel": (("indexer_kernel<1, true, false, false, false, 8> "
+                        "(bf16 block-key scan)") if wl.pool else
+                       f"indexer_kernel<0, true, false, false, false, T, L> "
+                       f"(MXFP4 scan + local top-k)"),
+            "algorithmic_bytes_per_launch": scan_bytes(wl),
+            "avg_launch_us": t_scan * 1e6,
+            "timed_in_step": True},
+        "step_hbm": {"algorithmic_bytes": per_call,
+                     "achieved_GBs": per_call / step_s / 1e9,
+                     "frac": per_call / step_s / 1e9 / HBM_PEAK_GBS},
+        "kernels_us": {n: v * 1e6 for n, v in kern.items()},
+    }
+    if headline and not args.no_variants:
+        res["variants"] = run_variants(args, wl, st, reps, planes, R, out,
+                                       ids, ws)
+    del reps, planes, st
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_variants(args, wl, st, reps, planes, R, out, ids, ws):
+    """Other calls on the headline workload's caches, each timed as its own
+    K-step graph: the MXFP4 indexer query, the sink + partial-RoPE
+    epilogue, the decoder group's pool layers and the write path."""
+    import torch
+    from fp4_kv_cache_amd import csa2, inputs
+
+    dev = "cuda:0"
+    k = wl.k
+    K, W = args.steps, args.warmup
+    v = {}
+    # The MXFP4 indexer query (V4's FP4 indexer query): an input of the
+    # layer call like the bf16 one, packed once outside the timed steps.
+    qc, qs = csa2.pack_query_fp4(st.q_idx)
 
     def step_mxfp4(i):
         csa2.sparse_attn_decode_fp4q(reps[i % R], qc, qs, st.w, st.q[0],
@@ -211,56 +346,67 @@ def run_gpu(args, wl):
                                      pool=wl.pool, out=out, topk_out=ids,
                                      ws=ws)
 
-    # The V4 attention details on the same step: per-head sink logits and
-    # the partial-RoPE output de-rotation at each sequence's position.
+    s, _ = graph_time(step_mxfp4, K, W, [out, ids])
+    t = kernel_times(step_mxfp4, args.kernel_steps, decode_kernels(wl))
+    a = scan_bytes(wl, "mxfp4") / t["scan_local_topk"] / 1e9
+    v["indexer_query_mxfp4"] = {
+        "value": wl.B / s, "ms_per_step": s * 1e3,
+        "step_hbm_frac": wl.B * algorithmic_bytes(wl, "mxfp4") / s / 1e9 / HBM_PEAK_GBS,
+        "kernels_us": {n: x * 1e6 for n, x in t.items()},
+        "scan_roofline": {"achieved": a, "frac": a / HBM_PEAK_GBS}}
+    # Per-head sink logits and the partial-RoPE output de-rotation.
     g_sink = torch.linspace(-2.0, 2.0, 64, device=dev)
     g_pos = torch.full((wl.B,), wl.ctx - 1, dtype=torch.int32, device=dev)
 
-    def step_epilogue(i):
+    def step_epi(i):
         csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
                                 st.swa[0], st.n_swa, k, st.scale,
                                 pool=wl.pool, out=out, topk_out=ids, ws=ws,
                                 sink=g_sink, pos=g_pos)
 
-    steps = {"bf16": step_bf16, "mxfp4": step_mxfp4,
-             "sink_rope": step_epilogue}
-    if not wl.pool:
-        # The pages' hierarchical decoder group on the same caches: the first
-        # Full layer also emitting the max-of-fine-scores pool (2,048 blocks
-        # of 8), and a Reindex layer scoring only that pool with its own
-        # indexer query.
-        from fp4_kv_cache_amd import inputs
-        group_pool = (2048, 8)
-        pool_ids = torch.empty((wl.B, group_pool[0] * group_pool[1]),
-                               dtype=torch.int32, device=dev)
-        ws_fp = csa2.workspace(csa2.load().csa2_workspace_size(
-            csa2.OP_FULL_POOL, wl.B, wl.n, k,
-            csa2.ctypes.byref(csa2.PoolOpts(*group_pool))), dev)
-        ws_ri = csa2.workspace(csa2.load().csa2_workspace_size(
-            csa2.OP_REINDEX, wl.B, pool_ids.shape[1], k, None), dev)
-        qi1, w1 = (torch.stack(t).contiguous() for t in zip(*[
-            inputs.index_query(wl, b, dev, layer=1) for b in range(wl.B)]))
+    s, _ = graph_time(step_epi, K, W, [out, ids])
+    v["attn_sink_rope"] = {
+        "value": wl.B / s, "ms_per_step": s * 1e3,
+        "what": "the headline step with per-head sink logits and the "
+                "partial-RoPE output de-rotation (csa2_sparse_attn_decode_ex)"}
+    # The pages' hierarchical decoder group on the same caches: a Full layer
+    # also emitting the max-of-fine-scores pool (2,048 blocks of 8), and a
+    # Reindex layer scoring only that pool with its own indexer query.
+    group_pool = (2048, 8)
+    pool_ids = torch.empty((wl.B, group_pool[0] * group_pool[1]),
+                           dtype=torch.int32, device=dev)
+    ws_fp = csa2.workspace(csa2.load().csa2_workspace_size(
+        csa2.OP_FULL_POOL, wl.B, wl.n, k,
+        csa2.ctypes.byref(csa2.PoolOpts(*group_pool))), dev)
+    ws_ri = csa2.workspace(csa2.load().csa2_workspace_size(
+        csa2.OP_REINDEX, wl.B, pool_ids.shape[1], k, None), dev)
+    qi1, w1 = (torch.stack(t).contiguous() for t in zip(*[
+        inputs.index_query(wl, b, dev, layer=1) for b in range(wl.B)]))
 
-        def step_full_pool(i):
-            csa2.full_pool_decode(reps[i % R], st.q_idx, st.w, st.q[0],
-                                  st.swa[0], st.n_swa, k, st.scale,
-                                  pool=group_pool, out=out, topk_out=ids,
-                                  pool_out=pool_ids, ws=ws_fp)
+    def step_full_pool(i):
+        csa2.full_pool_decode(reps[i % R], st.q_idx, st.w, st.q[0],
+                              st.swa[0], st.n_swa, k, st.scale,
+                              pool=group_pool, out=out, topk_out=ids,
+                              pool_out=pool_ids, ws=ws_fp)
 
-        def step_reindex(i):
-            csa2.reindex_decode(reps[i % R], pool_ids, qi1, w1, st.q[0],
-                                st.swa[0], st.n_swa, k, st.scale, out=out,
-                                topk_out=ids, ws=ws_ri)
+    def step_reindex(i):
+        csa2.reindex_decode(reps[i % R], pool_ids, qi1, w1, st.q[0],
+                            st.swa[0], st.n_swa, k, st.scale, out=out,
+                            topk_out=ids, ws=ws_ri)
 
-        steps["full_pool"] = step_full_pool
-        steps["reindex"] = step_reindex
+    fp, _ = graph_time(step_full_pool, K, W, [out, ids, pool_ids])
+    ri, _ = graph_time(step_reindex, K, W, [out, ids])
+    v["decoder_group_pool"] = {
+        "pool": list(group_pool), "unit": "query-tokens/s",
+        "full_pool_layer": {"value": wl.B / fp, "ms_per_step": fp * 1e3},
+        "reindex_layer": {"value": wl.B / ri, "ms_per_step": ri * 1e3,
+                          "scored_entries_per_seq": 2048 * 8}}
     # The write path at decode: one new entry per sequence from the m newest
     # tokens' hidden states (d = 7168, the pages' model width), appended to
     # caches of its own (the timed steps' caches stay as they are).
-    from fp4_kv_cache_amd import inputs as inp
     cm, cd = wl.m, 7168
-    c_h = inp.hidden_states(900, wl.B, cm, cd, dev)
-    c_w = inp.compressor_weights(900, cd, dev)
+    c_h = inputs.hidden_states(900, wl.B, cm, cd, dev)
+    c_w = inputs.compressor_weights(900, cd, dev)
     c_rows = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
     c_slot = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
     c_bufs = [torch.zeros(sh, dtype=torch.uint8, device=dev)
@@ -273,82 +419,25 @@ def run_gpu(args, wl):
         csa2.compress_append(c_h, *c_w, c_rows, *c_bufs[:4], swa=c_bufs[4],
                              swa_slot=c_slot, ws=c_ws)
 
-    steps["compress"] = step_compress
-    compress_bytes = (2 * 512 * cd * 2 + 128 * 512 * 2 + wl.B * cm * cd * 2
-                      + wl.B * (288 + 68 + cm * 512))
-    timing = {q: time_steps(fn, args, R, out, ids) for q, fn in steps.items()}
-
-    # -- per-kernel durations with HIP events on the launch stream: the same
-    # kernels through the component calls, M back-to-back launches of one
-    # kernel queued behind a spin kernel (so host enqueue time is hidden),
-    # rotated over the replicas.
-    # The scan kernel: the MXFP4 indexer over every entry, or, for the
-    # hierarchical workload, the bf16 block-key scan (its top-k keeps
-    # n_keep blocks expanded by the block size).
-    if wl.pool:
-        ld = n_blocks(wl)
-        nvalid = torch.full((wl.B,), ld, dtype=torch.int32, device=dev)
-        tk_k, tk_block = min(wl.pool[0], ld), wl.pool[1]
-    else:
-        ld, nvalid, tk_k, tk_block = wl.n, st.n_entries, k, 1
-    scores = torch.empty((wl.B, ld), dtype=torch.float32, device=dev)
-    tk_out = torch.empty((wl.B, tk_k * tk_block), dtype=torch.int32, device=dev)
-    tk_ws = csa2.workspace(csa2.workspace_size(csa2.OP_TOPK, wl.B, ld, tk_k), dev)
-    at_ws = csa2.workspace(csa2.workspace_size(csa2.OP_REUSE, wl.B, wl.n, k), dev)
-
-    def k_idx(r, query="bf16"):
-        pl = planes[r]
-        kf, kc, ks = ((csa2.KEYS_BF16, pl[4], None) if wl.pool
-                      else (csa2.KEYS_MXFP4, pl[2], pl[3]))
-        if query == "mxfp4":
-            csa2.indexer_score_fp4q(kf, kc, ks, nvalid, qc, qs, st.w,
-                                    out=scores)
-        else:
-            csa2.indexer_score(kf, kc, ks, nvalid, st.q_idx, st.w, out=scores)
-
-    def k_topk(r):
-        csa2.topk(scores, tk_k, n_valid=nvalid, block=tk_block,
-                  limit=st.n_entries if wl.pool else None, out=tk_out,
-                  ws=tk_ws)
-
-    def k_attn(r):
-        csa2.reuse_attn(planes[r][0], planes[r][1], ids, st.q[0],
-                        st.swa[0], st.n_swa, st.scale, out=out, ws=at_ws)
-
-    def timed(fn, M):
-        for r in range(R):
-            fn(r)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(200_000_000)
-        e0.record()
-        for i in range(M):
-            fn(i % R)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / M
-
-    M = max(8, min(args.steps, 200))
-    k_idx(0)
-    t_idx = {"bf16": timed(k_idx, M),
-             "mxfp4": timed(lambda r: k_idx(r, "mxfp4"), M)}
-    t_tk = timed(k_topk, M)
-    t_at = timed(k_attn, M)
-    return dict(timing=timing, t_idx=t_idx, t_topk=t_tk, t_attn=t_at,
-                replicas=R, st=st, compress=(cm, cd, compress_bytes))
+    s, _ = graph_time(step_compress, K, W, c_bufs)
+    cbytes = (2 * 512 * cd * 2 + 128 * 512 * 2 + wl.B * cm * cd * 2
+              + wl.B * (288 + 68 + cm * 512))
+    v["compress_append"] = {
+        "value": wl.B / s, "ms_per_step": s * 1e3, "m": cm, "d": cd,
+        "algorithmic_bytes": cbytes, "achieved_GBs": cbytes / s / 1e9,
+        "what": "csa2_compress_append: one new entry per sequence (C, Z "
+                "projections, softmax pooling, K^I, FP4/MXFP4/E4M3 append)"}
+    return v
 
 
 COPY_ELEMS = 64 << 20          # float32 elements of the calibration copy
 
 
 def run_pmc_pass(args, wl):
-    """Launch sequence for rocprofv3 --pmc: M plain indexer launches with
-    the bf16 query, then M with the MXFP4 query (the roofline kernels, same
-    arguments as the timed ones), then 4 copies
-    y = x * 1 over COPY_ELEMS float32 (a kernel whose HBM bytes are known:
-    4 * COPY_ELEMS read and written), then M eager decode steps with the
-    bf16 query (the counters of the attention, select and merge kernels)."""
+    """Launch sequence for rocprofv3 --pmc: M decode steps of the workload
+    on rotated replicas (the step's own scan, attention and merge kernels),
+    then 4 copies y = x * 1 over COPY_ELEMS float32 (a kernel whose HBM
+    bytes are known: 4 * COPY_ELEMS read and written)."""
     import torch
     from fp4_kv_cache_amd import csa2, workload
 
@@ -356,42 +445,26 @@ def run_pmc_pass(args, wl):
     st = workload.build(wl, dev)
     per_call = wl.B * algorithmic_bytes(wl)
     R = args.replicas or max(1, math.ceil(2 * 256e6 / per_call) + 1)
-    reps, planes = replicate(st, R)
-    scores = torch.empty((wl.B, wl.n), dtype=torch.float32, device=dev)
-    qc, qs = csa2.pack_query_fp4(st.q_idx)
+    reps, _ = replicate(st, R)
+    out = torch.empty((wl.B, 64, 512), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
+    ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, wl.B, wl.n,
+                                            wl.k, wl.pool), dev)
     M = max(8, min(args.steps, 64))
     for i in range(M):
-        pl = planes[i % R]
-        csa2.indexer_score(csa2.KEYS_MXFP4, pl[2], pl[3], st.n_entries,
-                           st.q_idx, st.w, out=scores)
-    for i in range(M):
-        pl = planes[i % R]
-        csa2.indexer_score_fp4q(csa2.KEYS_MXFP4, pl[2], pl[3], st.n_entries,
-                                qc, qs, st.w, out=scores)
+        csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
+                                st.swa[0], st.n_swa, wl.k, st.scale,
+                                pool=wl.pool, out=out, topk_out=ids, ws=ws)
     torch.cuda.synchronize()
     x = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
     for _ in range(4):
         torch.mul(x, 1.0, out=y)
     torch.cuda.synchronize()
-    del x, y
-    if not wl.pool:
-        out = torch.empty((wl.B, 64, 512), dtype=torch.bfloat16, device=dev)
-        ids = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
-        ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, wl.B, wl.n,
-                                                wl.k, None), dev)
-        for i in range(M):
-            csa2.sparse_attn_decode(reps[i % R], st.q_idx, st.w, st.q[0],
-                                    st.swa[0], st.n_swa, wl.k, st.scale,
-                                    out=out, topk_out=ids, ws=ws)
-        torch.cuda.synchronize()
-    print(json.dumps({"pmc_pass": True, "indexer_launches": M,
-                      "decode_steps": 0 if wl.pool else M,
-                      "indexer_algorithmic_bytes": {
-                          q: indexer_bytes(wl, q) for q in ("bf16", "mxfp4")},
-                      "copy_bytes_each_way": 4 * COPY_ELEMS}))
-
-
+    print(json.dumps({"pmc_pass": True, "decode_steps": M,
+                      "scan_algorithmic_bytes": scan_bytes(wl),
+                      "copy_bytes_each_way": 4 * COPY_ELEMS,
+                      "source_hash": source_hash()}))
 def run_cpu(wl, budget_s):
     """The oracle as it stands, on a bounded sample of the same workload:
     whole sequences (indexer over all entries, exact top-k, gather and
@@ -459,100 +532,58 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     from fp4_kv_cache_amd.inputs import WORKLOADS
-    wl = WORKLOADS[args.workload]
+    wids = [int(x) for x in args.workloads.split(",") if x.strip()]
     if args.pmc_pass:
-        run_pmc_pass(args, wl)
+        run_pmc_pass(args, WORKLOADS[wids[0]])
         return
-    g = run_gpu(args, wl)
-    scan_name = ("indexer_kernel<1, *, Q> (bf16 block-key scan)" if wl.pool
-                 else "indexer_kernel<0, *, Q> (MXFP4 scan)")
-
-    def summary(query):
-        eager_s, graph_s, steps_run, spread = g["timing"][query]
-        step_s = graph_s if graph_s is not None else eager_s
-        idx_alg = indexer_bytes(wl, query)
-        achieved = idx_alg / g["t_idx"][query] / 1e9
-        per_call = wl.B * algorithmic_bytes(wl, query)
-        qf = "true" if query == "mxfp4" else "false"
-        return dict(
-            step_s=step_s, eager_s=eager_s, graph_s=graph_s,
-            steps_run=steps_run, per_call=per_call, spread=spread,
-            roofline={"bound": "hbm", "achieved": achieved,
-                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": achieved / HBM_PEAK_GBS,
-                      "traffic": (traffic_from_profile(query)
-                                  if args.workload == 1 else None),
-                      "kernel": scan_name.replace("Q", qf),
-                      "algorithmic_bytes_per_launch": idx_alg,
-                      "avg_launch_us": g["t_idx"][query] * 1e6})
-
-    head = summary(args.query)
-    other = "mxfp4" if args.query == "bf16" else "bf16"
-    alt = summary(other)
-    step_s = head["step_s"]
+    results = []
+    for i, w in enumerate(wids):
+        results.append(run_workload(args, WORKLOADS[w], i == 0))
+        print(f"bench: {WORKLOADS[w].name} done "
+              f"({results[-1]['ms_per_step']:.4f} ms/step)", file=sys.stderr,
+              flush=True)
+    head = results[0]
+    wl = WORKLOADS[wids[0]]
+    step_s = head["ms_per_step"] * 1e-3
+    per_step = head["step_hbm"]["algorithmic_bytes"]
     line = {
         "metric": "CSA2 decode query-tokens/s per layer at 64K ctx; "
                   "achieved HBM GB/s vs peak",
-        "value": wl.B / step_s,
+        "value": head["value"],
         "unit": "query-tokens/s",
         "n_gpus": 1,
-        "steps": head["steps_run"],
+        "steps": args.steps,
+        "steps_requested": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_s * 1e3,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 scan MFMA + fp16 attention MFMA, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) latents packed to FP4/MXFP4/E4M3)",
-        "config": {"workload": wl.name, "global_batch": wl.B,
-                   "entries_per_seq": wl.n, "context": wl.ctx, "m": wl.m,
-                   "k": wl.k, "n_swa": wl.n_swa, "heads": 64,
-                   "head_dim": 512, "indexer": "32 heads x 128, MXFP4 keys",
-                   "indexer_query": args.query,
-                   "pool": list(wl.pool) if wl.pool else None,
-                   "cache_replicas": g["replicas"],
-                   "launch": "hip-graph" if head["graph_s"] else "eager"},
+        "config": dict({"workload": wl.name}, **head["config"],
+                       heads=64, head_dim=512,
+                       indexer="32 heads x 128, MXFP4 keys, bf16 query",
+                       launch="hip-graph of exactly `steps` steps"),
         "roofline": head["roofline"],
-        "step_hbm": {"algorithmic_bytes": head["per_call"],
-                     "achieved_GBs": head["per_call"] / step_s / 1e9,
-                     "frac": head["per_call"] / step_s / 1e9 / HBM_PEAK_GBS},
-        "kernels_us": {"indexer": g["t_idx"][args.query] * 1e6,
-                       "topk": g["t_topk"] * 1e6,
-                       "attention": g["t_attn"] * 1e6},
-        "eager_ms_per_step": head["eager_s"] * 1e3,
-        "graph_step_us_spread": head["spread"],
-        "variants": {f"indexer_query_{other}": {
-            "value": wl.B / alt["step_s"], "ms_per_step": alt["step_s"] * 1e3,
-            "roofline": alt["roofline"]}},
+        "roofline_step": {
+            "bound": "hbm", "achieved": per_step / step_s / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": per_step / step_s / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_step": per_step,
+            "what": "whole decode step (all kernels) at algorithmic bytes"},
+        "step_hbm": head["step_hbm"],
+        "kernels_us": head["kernels_us"],
+        "eager_ms_per_step": head["eager_ms_per_step"],
+        "configs": {r["workload"]: {x: r[x] for x in (
+            "value", "unit", "ms_per_step", "steps", "warmup",
+            "layers_per_step", "config", "step_hbm", "roofline",
+            "kernels_us", "eager_ms_per_step")} for r in results[1:]},
     }
-    ep = g["timing"]["sink_rope"]
-    ep_s = ep[1] if ep[1] is not None else ep[0]
-    line["variants"]["attn_sink_rope"] = {
-        "value": wl.B / ep_s, "ms_per_step": ep_s * 1e3,
-        "what": "the headline step with per-head sink logits and the "
-                "partial-RoPE output de-rotation (csa2_sparse_attn_decode_ex)"}
-    cp = g["timing"]["compress"]
-    cp_s = cp[1] if cp[1] is not None else cp[0]
-    cm, cd, cbytes = g["compress"]
-    line["variants"]["compress_append"] = {
-        "value": wl.B / cp_s, "ms_per_step": cp_s * 1e3, "m": cm, "d": cd,
-        "algorithmic_bytes": cbytes,
-        "achieved_GBs": cbytes / cp_s / 1e9,
-        "what": "csa2_compress_append: one new entry per sequence (C, Z "
-                "projections, softmax pooling, K^I, FP4/MXFP4/E4M3 append)"}
-    if "full_pool" in g["timing"]:
-        fp, ri = (g["timing"][x] for x in ("full_pool", "reindex"))
-        fp_s = fp[1] if fp[1] is not None else fp[0]
-        ri_s = ri[1] if ri[1] is not None else ri[0]
-        line["variants"]["decoder_group_pool"] = {
-            "pool": [2048, 8],
-            "full_pool_layer": {"value": wl.B / fp_s, "ms_per_step": fp_s * 1e3},
-            "reindex_layer": {"value": wl.B / ri_s, "ms_per_step": ri_s * 1e3,
-                              "scored_entries_per_seq": 2048 * 8},
-            "unit": "query-tokens/s"}
+    if "variants" in head:
+        line["variants"] = head["variants"]
     if not args.no_cpu:
-        cpu = run_cpu(wl, args.cpu_seconds)
-        line["cpu_baseline"] = cpu
+        line["cpu_baseline"] = run_cpu(wl, args.cpu_seconds)
     print(json.dumps(line))
 
 

@@ -26,7 +26,8 @@ EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
            "csa2_sparse_attn_decode_ex", "csa2_reuse_attn_ex",
            "csa2_sparse_attn_decode_noalloc",
            "csa2_compress_append", "csa2_workspace_size", "csa2_entry_bytes",
-           "csa2_kv_bytes_per_token", "csa2_last_error", "csa2_version"]
+           "csa2_kv_bytes_per_token", "csa2_set_launch_events",
+           "csa2_last_error", "csa2_version"]
 
 
 class Csa2Error(RuntimeError):
@@ -128,6 +129,8 @@ def load(path=None):
         "csa2_entry_bytes": (I32, [I32]),
         "csa2_kv_bytes_per_token": (ctypes.c_double,
                                     [ctypes.POINTER(I32), I32]),
+        "csa2_set_launch_events": (I32, [ctypes.POINTER(ctypes.c_void_p),
+                                         I32]),
         "csa2_last_error": (ctypes.c_char_p, []),
         "csa2_version": (ctypes.c_char_p, []),
     }
@@ -138,6 +141,16 @@ def load(path=None):
     if path is None:
         _lib = lib
     return lib
+
+
+def set_launch_events(events):
+    """Benchmark hook: the next calls of the decode and reuse entry points
+    record these HIP events (hipEvent_t handles as ctypes.c_void_p or int)
+    before their first kernel and after each kernel; pass [] to clear."""
+    arr = (ctypes.c_void_p * max(1, len(events)))(
+        *[e if isinstance(e, ctypes.c_void_p) else ctypes.c_void_p(e)
+          for e in events])
+    _check(load().csa2_set_launch_events(arr, len(events)))
 
 
 def _check(status):

@@ -29,6 +29,14 @@ csa2_status hip_fail(hipError_t e, const char* what) {
   return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Records the next launch event (csa2_set_launch_events), if one is set.
+#define CSA2_MARK(lm)                                                   \
+  do {                                                                  \
+    const hipError_t me_ = (lm).mark();                                 \
+    if (me_ != hipSuccess) return hip_fail(me_, "launch event record"); \
+  } while (0)
+
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline bool aligned(const void* p, size_t a) {
@@ -195,6 +203,32 @@ csa2_status check_attn_common(const uint8_t* main_codes,
 }
 
 }  // namespace
+
+extern "C" {
+
+// csa2_set_launch_events: the caller's events for the next calls.
+namespace {
+constexpr int kMaxLaunchEvents = 16;
+void* g_launch_events[kMaxLaunchEvents] = {};
+int g_n_launch_events = 0;
+}  // namespace
+
+csa2_status csa2_set_launch_events(void* const* events, int32_t n) {
+  if (n < 0 || n > kMaxLaunchEvents || (n > 0 && !events))
+    return fail(CSA2_ERR_INVALID_ARG, "launch events: need 0 <= n <= %d and "
+                "an array when n > 0", kMaxLaunchEvents);
+  for (int i = 0; i < n; ++i) g_launch_events[i] = events[i];
+  g_n_launch_events = n;
+  return CSA2_OK;
+}
+
+}  // extern "C"
+
+hipError_t csa2::LaunchMarks::mark() {
+  const int j = i++;
+  if (j >= g_n_launch_events) return hipSuccess;
+  return hipEventRecord(static_cast<hipEvent_t>(g_launch_events[j]), s);
+}
 
 extern "C" {
 
@@ -486,9 +520,12 @@ csa2_status csa2_reuse_attn_ex(const uint8_t* main_codes,
                 "workspace (got %zu)", need, ws_bytes);
   st = need_device();
   if (st) return st;
+  csa2::LaunchMarks lm{static_cast<hipStream_t>(stream)};
+  CSA2_MARK(lm);
   hipError_t e = csa2::launch_attn(main_codes, main_scales, n_cap, topk, k, q,
                                    swa, n_swa, B, scale, out, ws,
-                                   static_cast<hipStream_t>(stream), epi);
+                                   static_cast<hipStream_t>(stream), epi,
+                                   nullptr, &lm);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "csa2_reuse_attn launch");
 }
 
@@ -531,6 +568,8 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   hipError_t e;
+  csa2::LaunchMarks lm{s};
+  CSA2_MARK(lm);
   // Decode-internal buffers hold selection keys (uint32), not scores.
   uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
   const csa2::LocalPlan lp =
@@ -546,11 +585,12 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
                                    kv->n_entries, iq, B, keys, lp, lcand,
                                    lbound, s);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    CSA2_MARK(lm);
     const csa2::FusedSelect fs{lcand, lbound, lp.n_wg, lp.kloc, keys,
                                round32(kv->n_cap), kv->n_entries, topk_out};
     e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap,
                           topk_out, k, q, swa, n_swa, B, scale, out,
-                          base + L.off_attn, s, epi, &fs);
+                          base + L.off_attn, s, epi, &fs, &lm);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     return CSA2_OK;
   }
@@ -560,10 +600,12 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
                              kv->n_cap, kv->n_entries, nullptr, kv->n_cap,
                              iq, B, scores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    CSA2_MARK(lm);
     e = csa2::launch_row_select(scores, tmax, true, round32(kv->n_cap),
                                 kv->n_cap, kv->n_entries, nullptr, B, k, 1,
                                 nullptr, topk_out, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    CSA2_MARK(lm);
   } else {
     float* bscores = reinterpret_cast<float*>(base + L.off_bscores);
     int32_t* pool_ids = reinterpret_cast<int32_t*>(base + L.off_pool);
@@ -574,22 +616,26 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
                              kv->n_entries, nullptr, L.nb, iq, B, bscores, s,
                              tmax, nullptr, nullptr, pool->block);
     if (e != hipSuccess) return hip_fail(e, "block indexer launch");
+    CSA2_MARK(lm);
     e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb,
                                 kv->n_entries, nullptr, B, L.kb, pool->block,
                                 kv->n_entries, pool_ids, s, pool->block);
     if (e != hipSuccess) return hip_fail(e, "block top-k launch");
+    CSA2_MARK(lm);
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, pool_ids, L.n_cand,
                              iq, B, pscores, s, tmax);
     if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
+    CSA2_MARK(lm);
     e = csa2::launch_row_select(pscores, tmax, true, round32(L.n_cand),
                                 L.n_cand, nullptr, pool_ids, B, k, 1, nullptr,
                                 topk_out, s);
     if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
+    CSA2_MARK(lm);
   }
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
                         k, q, swa, n_swa, B, scale, out, base + L.off_attn, s,
-                        epi);
+                        epi, nullptr, &lm);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return CSA2_OK;
 }

@@ -948,7 +948,8 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        const uint16_t* q, const uint8_t* swa,
                        const int32_t* n_swa, int B, float scale,
                        uint16_t* out, void* ws, hipStream_t s,
-                       const AttnEpilogue& epi, const FusedSelect* fsel) {
+                       const AttnEpilogue& epi, const FusedSelect* fsel,
+                       LaunchMarks* marks) {
   if (B == 0) return hipSuccess;
   AttnArgs a{};
   a.main_codes = main_codes;
@@ -994,8 +995,11 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   } else {
     e = launch_attn_kernel<false, 1>(a, grid, s);
   }
+  if (e == hipSuccess && marks) e = marks->mark();
   if (e != hipSuccess || a.splits == 1) return e;
-  return launch_combine<2>(a.part_o, a.part_ml, a.splits, B, out, epi, s);
+  e = launch_combine<2>(a.part_o, a.part_ml, a.splits, B, out, epi, s);
+  if (e == hipSuccess && marks) e = marks->mark();
+  return e;
 }
 
 }  // namespace csa2

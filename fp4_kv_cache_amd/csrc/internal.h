@@ -101,6 +101,14 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int32_t* limit, int32_t* out, void* ws,
                        hipStream_t s);
 
+// Benchmark hook of csa2_set_launch_events: the caller's events, recorded
+// on the call's stream before its first kernel and after each kernel.
+struct LaunchMarks {
+  hipStream_t s;
+  int i = 0;
+  hipError_t mark();            // records the next event, if one is set
+};
+
 // attn.hip
 int attn_splits(int B, int k);
 size_t attn_workspace(int B, int k);
@@ -132,7 +140,8 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        const int32_t* n_swa, int B, float scale,
                        uint16_t* out, void* ws, hipStream_t s,
                        const AttnEpilogue& epi = AttnEpilogue{},
-                       const FusedSelect* fsel = nullptr);
+                       const FusedSelect* fsel = nullptr,
+                       LaunchMarks* marks = nullptr);
 
 // compress.hip
 // Workspace bytes of launch_compress (slice partials of the projections).

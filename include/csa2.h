@@ -31,9 +31,10 @@
  *   - Outputs must not overlap inputs.  Calls on distinct streams are
  *     thread-safe.  The library's only mutable global state is a set of
  *     per-device, set-once flags and addresses (kernel LDS limits, the
- *     location of csa2_sparse_attn_decode_noalloc's scratch array), plus
- *     that scratch array itself, which is shared by every call of that one
- *     entry point on a device (see there).
+ *     location of csa2_sparse_attn_decode_noalloc's scratch array), that
+ *     scratch array itself, which is shared by every call of that one entry
+ *     point on a device (see there), and the benchmark timing hook of
+ *     csa2_set_launch_events (unset unless a caller sets it).
  *   - Results are bitwise deterministic for fixed inputs and launch shapes.
  *   - bf16 values are passed as uint16_t bit patterns.
  *
@@ -399,6 +400,19 @@ int32_t csa2_entry_bytes(int32_t fmt);
  * such layer's compression ratio m_l.  For the V4.1 plan {2, 2, 2, 1} this
  * is 890. */
 double csa2_kv_bytes_per_token(const int32_t *m_of_kv_layers, int32_t n);
+
+/* Per-kernel timing hook for benchmarks (not part of the method).  While set
+ * (n > 0), each call of csa2_sparse_attn_decode(_fp4q/_ex/_noalloc) and
+ * csa2_reuse_attn(_ex) records events[0] on its stream just before its first
+ * kernel and events[i] right after its i-th kernel, for i < n (further
+ * kernels of the call record nothing), so the time between consecutive
+ * events is one kernel of that call as it runs inside the step.  The events
+ * are the caller's hipEvent_t handles (created with timing enabled and
+ * owned by the caller).  Process-wide setting, for single-threaded
+ * benchmarking only: set it, make one call, set the next events or clear
+ * with n = 0.  Returns CSA2_ERR_INVALID_ARG for n < 0, n > 16 or a null
+ * array with n > 0; a failed record makes the call return CSA2_ERR_HIP. */
+csa2_status csa2_set_launch_events(void *const *events, int32_t n);
 
 /* Thread-local message of the last failed call on this thread. */
 const char *csa2_last_error(void);

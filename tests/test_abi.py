@@ -139,3 +139,13 @@ def test_valid_call_without_device_reports_hip_error(L):
     st = L.csa2_pack_kv(0, A, 1, A * 4, A * 8, None)
     assert st == HIP
     assert _err()
+
+
+def test_launch_event_hook_arguments(L):
+    f = L.csa2_set_launch_events
+    arr = (ctypes.c_void_p * 16)()
+    assert f(arr, -1) == INVALID
+    assert f(arr, 17) == INVALID
+    assert f(None, 2) == INVALID
+    assert f(None, 0) == OK
+    assert f(arr, 0) == OK
