@@ -208,14 +208,26 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def kernel_times(step, M, names):
+def kernel_times(step, M, choices):
     """Mean duration of each kernel of the step as it runs inside it: M
     eager steps, each with its own HIP events recorded by the library on
     the step's stream before its first kernel and after each kernel, all
-    queued behind a spin kernel.  `names`: the step's kernels in launch
-    order."""
+    queued behind a spin kernel.  `choices`: the possible kernel sequences
+    of the call in launch order; the one whose length matches the number
+    of kernels the call launches (read from a first, untimed call) names
+    them."""
     import torch
     from fp4_kv_cache_amd import csa2
+    probe = HipEvents(16)
+    csa2.set_launch_events(probe.ev)
+    step(0)
+    csa2.set_launch_events([])
+    torch.cuda.synchronize()
+    n_k = csa2.launch_events_recorded() - 1
+    probe.close()
+    names = [c for c in choices if len(c) == n_k]
+    assert names, (n_k, choices)
+    names = names[0]
     n = len(names) + 1
     ev = HipEvents(M * n)
     torch.cuda.synchronize()
@@ -235,11 +247,16 @@ def kernel_times(step, M, names):
 
 
 def decode_kernels(wl):
-    """The kernels of one decode call, in launch order."""
+    """The possible kernel sequences of one decode call, in launch order
+    (top-k selections in one workgroup per row, or in two stages)."""
     if wl.pool:
-        return ["block_scan", "block_topk", "pool_scan", "pool_topk",
-                "attention", "split_merge"]
-    return ["scan_local_topk", "attention_fused_select", "split_merge"]
+        return [["block_scan", "block_topk", "pool_scan", "pool_topk",
+                 "attention", "split_merge"],
+                ["block_scan", "block_chunk_select", "block_union_select",
+                 "pool_scan", "pool_chunk_select", "pool_union_select",
+                 "attention", "split_merge"]]
+    return [["scan_local_topk", "attention_fused_select", "split_merge"],
+            ["scan_local_topk", "attention_fused_select"]]
 
 
 def run_workload(args, wl, headline):
@@ -280,7 +297,8 @@ def run_workload(args, wl, headline):
     M = args.kernel_steps
     kern = kernel_times(full, M, decode_kernels(wl))
     if wl.reuse_layers:
-        r = kernel_times(lambda i: reuse(i, 1), M, ["attention", "split_merge"])
+        r = kernel_times(lambda i: reuse(i, 1), M,
+                         [["attention", "split_merge"], ["attention"]])
         kern.update({f"reuse_{n}": v for n, v in r.items()})
     scan_name = "block_scan" if wl.pool else "scan_local_topk"
     t_scan = kern[scan_name]

@@ -27,6 +27,7 @@ EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
            "csa2_sparse_attn_decode_noalloc",
            "csa2_compress_append", "csa2_workspace_size", "csa2_entry_bytes",
            "csa2_kv_bytes_per_token", "csa2_set_launch_events",
+           "csa2_launch_events_recorded",
            "csa2_last_error", "csa2_version"]
 
 
@@ -131,6 +132,7 @@ def load(path=None):
                                     [ctypes.POINTER(I32), I32]),
         "csa2_set_launch_events": (I32, [ctypes.POINTER(ctypes.c_void_p),
                                          I32]),
+        "csa2_launch_events_recorded": (I32, []),
         "csa2_last_error": (ctypes.c_char_p, []),
         "csa2_version": (ctypes.c_char_p, []),
     }
@@ -151,6 +153,11 @@ def set_launch_events(events):
         *[e if isinstance(e, ctypes.c_void_p) else ctypes.c_void_p(e)
           for e in events])
     _check(load().csa2_set_launch_events(arr, len(events)))
+
+
+def launch_events_recorded():
+    """Events recorded by the latest call made under set_launch_events."""
+    return load().csa2_launch_events_recorded()
 
 
 def _check(status):

@@ -72,7 +72,7 @@ struct DecodeLayout {
   int kb = 0;
   size_t off_scores = 0, off_tmax = 0, off_bscores = 0,
          off_pool = 0, off_pscores = 0, off_lcand = 0, off_lbound = 0,
-         off_attn = 0, total = 0;
+         off_split = 0, off_attn = 0, total = 0;
 };
 
 inline size_t tiles_of(int64_t rows) { return (size_t)((rows + 31) / 32); }
@@ -96,6 +96,9 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     off += align256((size_t)B * csa2::kLocalMaxCands * 8);
     L.off_lbound = off;
     off += align256((size_t)B * (csa2::kLocalMaxCands / 8) * 4);
+    // The two-stage selection, for rows the fused selection cannot take.
+    L.off_split = off;
+    off += csa2::split_workspace(B, n_cap, k);
   } else {
     L.nb = (n_cap + pool->block - 1) / pool->block;
     L.kb = (int)std::min<int64_t>(pool->n_blocks_keep, L.nb);
@@ -109,6 +112,11 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     off += align256((size_t)B * round32(L.n_cand) * 4);
     L.off_tmax = off;
     off += align256((size_t)B * std::max(tiles_of(L.nb), tiles_of(L.n_cand)) * 4);
+    // The two-stage selections of the blocks, then of the pool (one after
+    // the other, so they share the space).
+    L.off_split = off;
+    off += std::max(csa2::split_workspace(B, L.nb, L.kb),
+                    csa2::split_workspace(B, L.n_cand, k));
   }
   L.off_attn = off;
   off += align256(csa2::attn_workspace(B, k));
@@ -121,9 +129,9 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
 struct FullPoolLayout {
   int64_t nb = 0;
   size_t off_scores = 0, off_tmax = 0, off_bmax = 0, off_btmax = 0,
-         off_attn = 0, total = 0;
+         off_split = 0, off_split_b = 0, off_attn = 0, total = 0;
 };
-FullPoolLayout full_pool_layout(int B, int64_t n_cap, int k) {
+FullPoolLayout full_pool_layout(int B, int64_t n_cap, int k, int kb) {
   FullPoolLayout L;
   L.nb = (n_cap + 7) / 8;
   size_t off = 0;
@@ -135,6 +143,11 @@ FullPoolLayout full_pool_layout(int B, int64_t n_cap, int k) {
   off += align256((size_t)B * round32(L.nb) * 4);
   L.off_btmax = off;
   off += align256((size_t)B * tiles_of(L.nb) * 4);
+  // The two-stage selections of the layer's top-k and of the blocks.
+  L.off_split = off;
+  off += csa2::split_workspace(B, n_cap, k);
+  L.off_split_b = off;
+  off += csa2::split_workspace(B, L.nb, kb);
   L.off_attn = off;
   off += align256(csa2::attn_workspace(B, k));
   L.total = off;
@@ -143,7 +156,7 @@ FullPoolLayout full_pool_layout(int B, int64_t n_cap, int k) {
 
 // Workspace of csa2_reindex_decode: pool keys, their tile maxima, attention.
 struct ReindexLayout {
-  size_t off_scores = 0, off_tmax = 0, off_attn = 0, total = 0;
+  size_t off_scores = 0, off_tmax = 0, off_split = 0, off_attn = 0, total = 0;
 };
 ReindexLayout reindex_layout(int B, int64_t n_pool, int k) {
   ReindexLayout L;
@@ -152,6 +165,8 @@ ReindexLayout reindex_layout(int B, int64_t n_pool, int k) {
   off += align256((size_t)B * round32(n_pool) * 4);
   L.off_tmax = off;
   off += align256((size_t)B * tiles_of(n_pool) * 4);
+  L.off_split = off;
+  off += csa2::split_workspace(B, n_pool, k);
   L.off_attn = off;
   off += align256(csa2::attn_workspace(B, k));
   L.total = off;
@@ -211,6 +226,7 @@ namespace {
 constexpr int kMaxLaunchEvents = 16;
 void* g_launch_events[kMaxLaunchEvents] = {};
 int g_n_launch_events = 0;
+int g_n_recorded = 0;           // events recorded by the latest call
 }  // namespace
 
 csa2_status csa2_set_launch_events(void* const* events, int32_t n) {
@@ -222,11 +238,15 @@ csa2_status csa2_set_launch_events(void* const* events, int32_t n) {
   return CSA2_OK;
 }
 
+int32_t csa2_launch_events_recorded(void) { return g_n_recorded; }
+
 }  // extern "C"
 
 hipError_t csa2::LaunchMarks::mark() {
   const int j = i++;
+  if (j == 0) g_n_recorded = 0;
   if (j >= g_n_launch_events) return hipSuccess;
+  g_n_recorded = j + 1;
   return hipEventRecord(static_cast<hipEvent_t>(g_launch_events[j]), s);
 }
 
@@ -266,7 +286,7 @@ size_t csa2_workspace_size(int32_t op, int32_t B, int64_t n_cap, int32_t k,
   if (B < 0 || n_cap < 0 || n_cap > kMaxCap || k < 1 || k > kMaxK) return 0;
   switch (op) {
     case CSA2_OP_TOPK:
-      return csa2::topk_workspace(B, n_cap);
+      return csa2::topk_workspace(B, n_cap, k);
     case CSA2_OP_DECODE:
       if (pool && (pool->block < 1 || pool->block > kMaxBlock ||
                    pool->n_blocks_keep < 1))
@@ -278,7 +298,7 @@ size_t csa2_workspace_size(int32_t op, int32_t B, int64_t n_cap, int32_t k,
       if (!pool || pool->block != 8 || pool->n_blocks_keep < 1 ||
           pool->n_blocks_keep > kMaxK)
         return 0;
-      return full_pool_layout(B, n_cap, k).total;
+      return full_pool_layout(B, n_cap, k, pool->n_blocks_keep).total;
     case CSA2_OP_REINDEX:
       if (n_cap < 1 || n_cap > kMaxPool) return 0;
       return reindex_layout(B, n_cap, k).total;
@@ -474,7 +494,7 @@ csa2_status csa2_topk(const float* scores, int64_t ld, const int32_t* n_valid,
   if (!scores || !out) return fail(CSA2_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(scores, 4) || !aligned(out, 4))
     return fail(CSA2_ERR_ALIGNMENT, "scores and out need 4-byte alignment");
-  const size_t need = csa2::topk_workspace(B, ld);
+  const size_t need = csa2::topk_workspace(B, ld, k);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
     return fail(CSA2_ERR_WORKSPACE, "topk needs %zu bytes of 256-byte aligned "
                 "workspace (got %zu)", need, ws_bytes);
@@ -603,7 +623,7 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
     CSA2_MARK(lm);
     e = csa2::launch_row_select(scores, tmax, true, round32(kv->n_cap),
                                 kv->n_cap, kv->n_entries, nullptr, B, k, 1,
-                                nullptr, topk_out, s);
+                                nullptr, topk_out, s, 1, base + L.off_split);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     CSA2_MARK(lm);
   } else {
@@ -619,7 +639,8 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
     CSA2_MARK(lm);
     e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb,
                                 kv->n_entries, nullptr, B, L.kb, pool->block,
-                                kv->n_entries, pool_ids, s, pool->block);
+                                kv->n_entries, pool_ids, s, pool->block,
+                                base + L.off_split);
     if (e != hipSuccess) return hip_fail(e, "block top-k launch");
     CSA2_MARK(lm);
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
@@ -629,7 +650,7 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
     CSA2_MARK(lm);
     e = csa2::launch_row_select(pscores, tmax, true, round32(L.n_cand),
                                 L.n_cand, nullptr, pool_ids, B, k, 1, nullptr,
-                                topk_out, s);
+                                topk_out, s, 1, base + L.off_split);
     if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
     CSA2_MARK(lm);
   }
@@ -767,7 +788,8 @@ csa2_status csa2_full_pool_decode(const csa2_cache* kv, const uint16_t* q_idx,
   const int64_t n_pool = (int64_t)pool->n_blocks_keep * 8;
   if (overlap(pool_out, (size_t)B * n_pool * 4, topk_out, (size_t)B * k * 4))
     return fail(CSA2_ERR_INVALID_ARG, "pool_out overlaps topk_out");
-  const FullPoolLayout L = full_pool_layout(B, kv->n_cap, k);
+  const FullPoolLayout L =
+      full_pool_layout(B, kv->n_cap, k, pool->n_blocks_keep);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return fail(CSA2_ERR_WORKSPACE, "full-pool decode needs %zu bytes of "
                 "256-byte aligned workspace (got %zu)", L.total, ws_bytes);
@@ -792,7 +814,20 @@ csa2_status csa2_full_pool_decode(const csa2_cache* kv, const uint16_t* q_idx,
                           kv->n_entries, k, 1, nullptr, topk_out};
   const csa2::KeyRows blocks{bmax, btmax, round32(L.nb), L.nb, nullptr,
                              pool->n_blocks_keep, 8, kv->n_entries, pool_out};
-  e = csa2::launch_row_select_pair(own, blocks, B, s);
+  if (csa2::split_plan(B, kv->n_cap, k).ok &&
+      csa2::split_plan(B, L.nb, pool->n_blocks_keep).ok) {
+    // Rows long enough for the two-stage selection: one after the other.
+    e = csa2::launch_row_select(scores, nullptr, true, own.ld, own.n_cols,
+                                own.n_valid, nullptr, B, own.k, own.block,
+                                own.limit, own.out, s, 1, base + L.off_split);
+    if (e == hipSuccess)
+      e = csa2::launch_row_select(bmax, nullptr, true, blocks.ld,
+                                  blocks.n_cols, blocks.n_valid, nullptr, B,
+                                  blocks.k, blocks.block, blocks.limit,
+                                  blocks.out, s, 1, base + L.off_split_b);
+  } else {
+    e = csa2::launch_row_select_pair(own, blocks, B, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "top-k and pool launch");
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
                         k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
@@ -840,7 +875,8 @@ csa2_status csa2_reindex_decode(const csa2_cache* kv, const int32_t* pool,
       scores, s, tmax);
   if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
   e = csa2::launch_row_select(scores, tmax, true, round32(n_pool), n_pool,
-                              nullptr, pool, B, k, 1, nullptr, topk_out, s);
+                              nullptr, pool, B, k, 1, nullptr, topk_out, s, 1,
+                              base + L.off_split);
   if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
                         k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);

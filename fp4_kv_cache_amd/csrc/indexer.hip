@@ -130,12 +130,12 @@ __device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
 constexpr int kFmtFp4 = 4;          // E2M1 in the op's format fields
 
 // Tiles of loads kept in flight ahead of the matrix work (the scaled-op
-// path does little per tile, so it keeps one more).
+// path does little per tile, so it keeps one more).  The bf16 block keys
+// (8 KB per wavefront tile) keep two as well, at 2 wavefronts per SIMD
+// instead of 4: the 8 x 131,072-block scan's decode step measured 122.8
+// against 125.0 us with one.
 template <int KEYFMT, bool SCALED> struct Depth {
   static constexpr int value = SCALED ? 3 : 2;
-};
-template <bool SCALED> struct Depth<1, SCALED> {
-  static constexpr int value = 1;
 };
 
 // KEYS: write selection keys (see score_key) instead of float scores, and

@@ -75,11 +75,20 @@ hipError_t launch_indexer_local(const uint8_t* k_codes,
 // [B][ceil(n_cols/32)] in the same form, nullable) enables tile pruning.
 // A row's length is min(n_cols, ceil(n_valid[b] / valid_div)) when n_valid
 // is given.
+// With split_ws (split_workspace() bytes) and a row long enough to split
+// (split_plan), the two-stage selection runs instead (see topk.hip).
 hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
                              int64_t ld, int64_t n_cols, const int32_t* n_valid,
                              const int32_t* ids, int B, int k, int block,
                              const int32_t* limit, int32_t* out,
-                             hipStream_t s, int valid_div = 1);
+                             hipStream_t s, int valid_div = 1,
+                             void* split_ws = nullptr);
+struct SplitPlan {
+  bool ok = false;
+  int G = 0, kl = 0;          // chunks per row, pairs kept per chunk
+};
+SplitPlan split_plan(int B, int64_t n_cols, int k);
+size_t split_workspace(int B, int64_t n_cols, int k);
 
 // Two key selections (no ids) over the same B rows in one launch, side by
 // side: rows of r0 on workgroups 0..B-1, rows of r1 on B..2B-1.
@@ -94,8 +103,9 @@ struct KeyRows {
 };
 hipError_t launch_row_select_pair(const KeyRows& r0, const KeyRows& r1, int B,
                                   hipStream_t s);
-// Standalone top-k over a score array (computes tile maxima in `ws`).
-size_t topk_workspace(int B, int64_t ld);
+// Standalone top-k over a score array (the two-stage selection, or tile
+// maxima in `ws` for the one-workgroup-per-row selection).
+size_t topk_workspace(int B, int64_t ld, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int32_t* ids, int B, int k, int block,
                        const int32_t* limit, int32_t* out, void* ws,

@@ -376,6 +376,154 @@ __global__ __launch_bounds__(kNT) void row_select_pair_kernel(RowArgs a0,
   else row_select_row<false, true>(a1, (int)blockIdx.x - B0);
 }
 
+// ------------------------------------------------- two-stage selection --
+// Long rows with few of them (too little parallelism for one workgroup per
+// row) split into chunks of kChunk entries.  Stage 1 (a workgroup per
+// chunk) keeps each chunk's top kl (key, id) pairs in id order and a bound
+// on what it left out: every valid key not kept is <= the selection's
+// threshold (0 when the chunk kept all its valid keys).  Stage 2 (a
+// workgroup per row) selects the row's top k from the union of its chunks'
+// pairs: with L the largest bound, when at least k pairs have keys above L
+// their top k is the row's (anything left out is <= L), and with fewer the
+// union is the whole answer only when L = 0; otherwise the row streams
+// through the exact selection instead.
+constexpr int kChunkNT = 256;
+constexpr int kChunk = kChunkNT * kPer;     // 4096 entries per chunk
+constexpr int kSplitCap = kNT * 8;          // union pairs per row (8,192)
+
+struct SplitArgs {
+  RowArgs a;
+  int G;                    // chunks per row
+  int kl;                   // pairs kept per chunk
+  uint2* cand;              // [B][G][kl] (key, id), id order
+  uint32_t* bound;          // [B][G]
+};
+
+struct ChunkSmem {
+  uint32_t key[kChunk];
+  int32_t id[kChunk];
+  SelSmem<kChunkNT, kNB> sel;
+};
+
+__device__ __forceinline__ int64_t row_len(const RowArgs& a, int b) {
+  int64_t len = a.n_cols;
+  if (a.n_valid) {
+    const int32_t v = a.n_valid[b];
+    const int64_t nv = v <= 0 ? 0 : ((int64_t)v + a.valid_div - 1) / a.valid_div;
+    len = nv < len ? nv : len;
+  }
+  return len;
+}
+
+// Stage 1: chunk blockIdx.x of row blockIdx.y.  Entries are read coalesced
+// into LDS (an entry past the row or with a negative id has key 0), then
+// thread t takes entries 16t .. 16t+15 of the chunk, so the selection's
+// position order is id order.
+template <bool HAS_IDS, bool KEYS>
+__global__ __launch_bounds__(kChunkNT) void chunk_select_kernel(SplitArgs sa) {
+  __shared__ ChunkSmem sm;
+  const RowArgs& a = sa.a;
+  const int b = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < kChunkNT / 64 * kNB; i += kChunkNT)
+    (&sm.sel.hist[0][0])[i] = 0;
+  const int64_t len = row_len(a, b);
+  const int64_t base = (int64_t)g * kChunk;
+  const uint32_t* row = static_cast<const uint32_t*>(a.scores) + (int64_t)b * a.ld;
+  const int32_t* idr = HAS_IDS ? a.ids + (int64_t)b * a.n_cols : nullptr;
+  uint32_t w[kPer];
+  int32_t iv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t i = base + j * kChunkNT + tid;
+    const int64_t ic = i < len ? i : (len > 0 ? len - 1 : 0);
+    w[j] = len > 0 ? row[ic] : 0u;
+    iv[j] = HAS_IDS ? (len > 0 ? idr[ic] : -1) : (int32_t)i;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t i = base + j * kChunkNT + tid;
+    const bool ok = i < len && iv[j] >= 0;
+    sm.key[j * kChunkNT + tid] = ok ? word_key<KEYS>(w[j]) : 0u;
+    sm.id[j * kChunkNT + tid] = iv[j];
+  }
+  __syncthreads();
+  uint32_t kk[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) kk[j] = sm.key[tid * kPer + j];
+  const SelResult r = block_select<kChunkNT, kPer, kNB>(kk, sa.kl, sm.sel);
+  const int64_t grp = (int64_t)b * sa.G + g;
+  uint2* co = sa.cand + grp * sa.kl;
+  int p = r.pos;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (r.mask & (1u << j))
+      co[p++] = make_uint2(kk[j], (uint32_t)sm.id[tid * kPer + j]);
+  for (int q = r.total + tid; q < sa.kl; q += kChunkNT)
+    co[q] = make_uint2(0u, 0xFFFFFFFFu);
+  if (tid == 0) sa.bound[grp] = r.nval > sa.kl ? r.thr : 0u;
+}
+
+// Stage 2 for row blockIdx.x: PER union pairs per thread (thread t holds
+// pairs PER*t .. PER*t+PER-1, in id order).
+template <int PER, bool HAS_IDS, bool KEYS>
+__device__ __forceinline__ void union_row(const SplitArgs& sa, int b) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
+  const RowArgs& a = sa.a;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < kNT / 64 * kNB; i += kNT) (&sm.sel.hist[0][0])[i] = 0;
+  const int U = sa.G * sa.kl;
+  const uint2* cr = sa.cand + (int64_t)b * U;
+  uint32_t kk[PER];
+  int32_t ci[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid * PER + j;
+    const uint2 v = cr[i < U ? i : U - 1];
+    kk[j] = i < U ? v.x : 0u;
+    ci[j] = (int32_t)v.y;
+  }
+  uint32_t lb = 0u;
+  for (int i = tid; i < sa.G; i += kNT)
+    lb = max(lb, sa.bound[(int64_t)b * sa.G + i]);
+  lb = wave_max_u32(lb);
+  if (lane == 0) sm.sel.red[0][wv] = lb;
+  __syncthreads();
+  uint32_t L = 0u;
+#pragma unroll
+  for (int w = 0; w < kNT / 64; ++w) L = max(L, sm.sel.red[0][w]);
+  __syncthreads();                  // red[] is the selection's scratch too
+#pragma unroll
+  for (int j = 0; j < PER; ++j) kk[j] = kk[j] > L ? kk[j] : 0u;
+  const SelResult r = block_select<kNT, PER, kNB>(kk, a.k, sm.sel);
+  const int64_t ob = (int64_t)b * a.k * a.block;
+  const int64_t lim = a.limit ? (int64_t)a.limit[b] : INT64_MAX;
+  int count;
+  if (r.nval >= a.k || L == 0u) {
+    int p = r.pos;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (r.mask & (1u << j)) put(a, ob, lim, p++, ci[j]);
+    count = r.total;
+  } else {
+    // Not provably exact: the whole row through the streaming selection.
+    const ScoreSrc<HAS_IDS, KEYS> from_scores{
+        static_cast<const uint32_t*>(a.scores) + (int64_t)b * a.ld,
+        HAS_IDS ? a.ids + (int64_t)b * a.n_cols : nullptr};
+    __syncthreads();
+    count = stream_select<kNT>(sm, row_len(a, b), a.k, from_scores);
+    for (int p = tid; p < count; p += kNT) put(a, ob, lim, p, sm.id[p]);
+  }
+  for (int64_t p = (int64_t)count * a.block + tid; p < (int64_t)a.k * a.block;
+       p += kNT)
+    a.out[ob + p] = -1;
+}
+
+template <int PER, bool HAS_IDS, bool KEYS>
+__global__ __launch_bounds__(kNT) void union_select_kernel(SplitArgs sa) {
+  union_row<PER, HAS_IDS, KEYS>(sa, blockIdx.x);
+}
+
 // Tile maxima of a plain score array.  Entries at or past the row's length
 // (n_valid[b] when given) and entries with a negative id count as -inf, so a
 // tile maximum is always the maximum of scores the selection may choose: a
@@ -406,9 +554,70 @@ __global__ void tilemax_kernel(const float* __restrict__ scores, int64_t ld,
 
 }  // namespace
 
-size_t topk_workspace(int B, int64_t ld) {
-  if (ld <= kCap) return 0;
-  return (((size_t)B * ((ld + 31) >> 5) * 4) + 255) & ~size_t(255);
+SplitPlan split_plan(int B, int64_t n_cols, int k) {
+  SplitPlan sp;
+  // Worth it when one workgroup per row leaves most of the GPU idle and
+  // the row spans several chunks.
+  if (B < 1 || B > 128 || k < 1 || k > 2048 || n_cols < 2 * kChunk)
+    return sp;
+  const int64_t G = (n_cols + kChunk - 1) / kChunk;
+  // A chunk expects mu = k * kChunk / n_cols of the row's winners; it keeps
+  // 2 mu + 24 (on independent scores more than that is many standard
+  // deviations away: for mu = 2, P(X > 28) < 1e-15), at most the chunk.
+  int64_t kl = 2 * (((int64_t)k * kChunk + n_cols - 1) / n_cols) + 24;
+  kl = std::min<int64_t>(kl, kChunk);
+  if (G * kl > kSplitCap) return sp;
+  sp.ok = true;
+  sp.G = (int)G;
+  sp.kl = (int)kl;
+  return sp;
+}
+
+size_t split_workspace(int B, int64_t n_cols, int k) {
+  const SplitPlan sp = split_plan(B, n_cols, k);
+  if (!sp.ok) return 0;
+  return ((((size_t)B * sp.G * sp.kl * 8) + 255) & ~size_t(255)) +
+         ((((size_t)B * sp.G * 4) + 255) & ~size_t(255));
+}
+
+size_t topk_workspace(int B, int64_t ld, int k) {
+  const size_t tm = ld <= kCap ? 0
+      : (((size_t)B * ((ld + 31) >> 5) * 4) + 255) & ~size_t(255);
+  return tm + split_workspace(B, ld, k);
+}
+
+template <int PER, bool HAS_IDS, bool KEYS>
+hipError_t launch_union(const SplitArgs& sa, int B, hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(
+      reinterpret_cast<const void*>(union_select_kernel<PER, HAS_IDS, KEYS>),
+      (int)sizeof(RowSmem), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((union_select_kernel<PER, HAS_IDS, KEYS>), dim3((unsigned)B),
+                     dim3(kNT), sizeof(RowSmem), s, sa);
+  return hipGetLastError();
+}
+
+template <bool HAS_IDS, bool KEYS>
+hipError_t launch_split(const RowArgs& a, const SplitPlan& sp, void* ws,
+                        int B, hipStream_t s) {
+  SplitArgs sa;
+  sa.a = a;
+  sa.G = sp.G;
+  sa.kl = sp.kl;
+  sa.cand = static_cast<uint2*>(ws);
+  sa.bound = reinterpret_cast<uint32_t*>(
+      static_cast<uint8_t*>(ws) +
+      ((((size_t)B * sp.G * sp.kl * 8) + 255) & ~size_t(255)));
+  hipLaunchKernelGGL((chunk_select_kernel<HAS_IDS, KEYS>),
+                     dim3((unsigned)sp.G, (unsigned)B), dim3(kChunkNT), 0, s,
+                     sa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int U = sp.G * sp.kl;
+  if (U <= kNT * 2) return launch_union<2, HAS_IDS, KEYS>(sa, B, s);
+  if (U <= kNT * 4) return launch_union<4, HAS_IDS, KEYS>(sa, B, s);
+  return launch_union<8, HAS_IDS, KEYS>(sa, B, s);
 }
 
 template <bool HAS_IDS, bool KEYS>
@@ -445,13 +654,21 @@ hipError_t launch_row_select(const void* scores, const void* tmax, bool keys,
                              int64_t ld, int64_t n_cols,
                              const int32_t* n_valid, const int32_t* ids, int B,
                              int k, int block, const int32_t* limit,
-                             int32_t* out, hipStream_t s, int valid_div) {
+                             int32_t* out, hipStream_t s, int valid_div,
+                             void* split_ws) {
   if (B == 0) return hipSuccess;
   if (n_cols > ld || (keys && !ids && (ld & 31)) || valid_div < 1)
     return hipErrorInvalidValue;
   RowArgs a = row_args(scores, tmax, ld, n_cols, n_valid, ids, k, block,
                        limit, out);
   a.valid_div = valid_div;
+  const SplitPlan sp = split_plan(B, n_cols, k);
+  if (split_ws && sp.ok) {
+    if (ids) return keys ? launch_split<true, true>(a, sp, split_ws, B, s)
+                         : launch_split<true, false>(a, sp, split_ws, B, s);
+    return keys ? launch_split<false, true>(a, sp, split_ws, B, s)
+                : launch_split<false, false>(a, sp, split_ws, B, s);
+  }
   if (ids) return keys ? launch_rows<true, true>(a, B, s)
                        : launch_rows<true, false>(a, B, s);
   return keys ? launch_rows<false, true>(a, B, s)
@@ -482,6 +699,9 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int32_t* limit, int32_t* out, void* ws,
                        hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (split_plan(B, ld, k).ok)        // the two-stage selection
+    return launch_row_select(scores, nullptr, false, ld, ld, n_valid, ids, B,
+                             k, block, limit, out, s, 1, ws);
   float* tmax = nullptr;
   if (ld > kCap) {
     tmax = static_cast<float*>(ws);

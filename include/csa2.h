@@ -414,6 +414,10 @@ double csa2_kv_bytes_per_token(const int32_t *m_of_kv_layers, int32_t n);
  * array with n > 0; a failed record makes the call return CSA2_ERR_HIP. */
 csa2_status csa2_set_launch_events(void *const *events, int32_t n);
 
+/* Events recorded by the latest call made while csa2_set_launch_events was
+ * set (its kernel count + 1 when enough events were given). */
+int32_t csa2_launch_events_recorded(void);
+
 /* Thread-local message of the last failed call on this thread. */
 const char *csa2_last_error(void);
 

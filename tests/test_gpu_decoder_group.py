@@ -122,6 +122,22 @@ def test_group_full_size_sampled():
         _check_group_one(wl, st, b, ne[b], 2048, 512, one)
 
 
+def test_group_1m_sampled():
+    """The decoder Full layer at the 1M limit with m = 1 (8 sequences x
+    1,048,576 entries): its own top-512 over every visible position and the
+    pool of 2,048 blocks of 8 (131,072 block maxima) both take the
+    two-stage selection; one Reindex layer on the pool; sequences 0 and 7
+    checked."""
+    wl = dataclasses.replace(WORKLOADS[4], pool=None, reuse_layers=1)
+    st = workload.build(wl, DEV)
+    res = _run(wl, st, 2048, 512, (1,))
+    (o, i, p), r = res
+    for b in (0, wl.B - 1):
+        one = ((o[b:b + 1], i[b:b + 1], p[b:b + 1]),
+               {l: (x[b:b + 1], y[b:b + 1]) for l, (x, y) in r.items()})
+        _check_group_one(wl, st, b, wl.n, 2048, 512, one)
+
+
 def _check_group_one(wl, st, b, n, n_keep, k, res):
     """The checks of _check_group for one sequence b whose results sit at
     index 0."""

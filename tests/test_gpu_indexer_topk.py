@@ -208,3 +208,35 @@ def test_indexer_scores_long_scan_sampled():
             np.testing.assert_allclose(sc[b, rows], ref, rtol=SCORE_RTOL,
                                        atol=1e-4)
         assert np.all(np.isneginf(sc[b, n:])), b
+
+
+def test_topk_two_stage_crowded_chunk_ties_and_ids():
+    """Rows long enough for the two-stage selection (chunks of 4,096 keep
+    their top few pairs; the row's top k comes from their union when the
+    chunks' bounds prove it).  Row 0 crowds 1,500 of its top 2,048 into one
+    chunk, far more than a chunk keeps, so the union proves nothing and the
+    row streams through the exact selection; row 1's scores tie in steps
+    of 0.5 across every chunk boundary; row 2 is ragged (n_valid).  Then
+    explicit ids with -1 holes over 12,000 scores."""
+    ld, k = 60000, 2048
+    rng = np.random.default_rng(31)
+    sc = rng.standard_normal((3, ld)).astype(np.float32)
+    sc[0, 8192:8192 + 1500] = 10.0 + rng.random(1500).astype(np.float32)
+    sc[1] = np.round(sc[1] * 2) / 2
+    nv = [ld, ld, 33333]
+    out = csa2.topk(torch.from_numpy(sc).to(DEV), k,
+                    n_valid=torch.tensor(nv, dtype=torch.int32, device=DEV))
+    out = out.cpu().numpy()
+    for b in range(3):
+        ref = O.topk(sc[b, :nv[b]].astype(np.float64), k)
+        assert np.array_equal(out[b], ref), b
+    ids = np.sort(rng.choice(10 ** 7, (2, 12000), replace=False), axis=1)
+    ids = ids.astype(np.int32)
+    ids[:, ::97] = -1
+    sc2 = rng.standard_normal((2, 12000)).astype(np.float32)
+    out2 = csa2.topk(torch.from_numpy(sc2).to(DEV), 512,
+                     ids=torch.from_numpy(ids).to(DEV)).cpu().numpy()
+    for b in range(2):
+        ok = ids[b] >= 0
+        ref = O.topk(sc2[b][ok].astype(np.float64), 512, ids=ids[b][ok])
+        assert np.array_equal(out2[b], ref), b
