@@ -25,6 +25,8 @@ EXPORTS = ["csa2_pack_kv", "csa2_unpack_kv", "csa2_build_block_keys",
            "csa2_full_pool_decode", "csa2_reindex_decode", "csa2_reuse_attn",
            "csa2_sparse_attn_decode_ex", "csa2_reuse_attn_ex",
            "csa2_sparse_attn_decode_noalloc",
+           "csa2_sparse_attn_decode_fp4q_ex", "csa2_full_pool_decode_ex",
+           "csa2_reindex_decode_ex",
            "csa2_compress_append", "csa2_workspace_size", "csa2_entry_bytes",
            "csa2_kv_bytes_per_token", "csa2_set_launch_events",
            "csa2_launch_events_recorded",
@@ -109,6 +111,20 @@ def load(path=None):
         "csa2_reindex_decode": (I32, [ctypes.POINTER(CacheDesc), P, I64, P,
                                       P, P, P, P, I32, I32, F32, P, P, P, SZ,
                                       P]),
+        "csa2_sparse_attn_decode_fp4q_ex": (I32, [ctypes.POINTER(CacheDesc),
+                                                  P, P, P, P, P, P, I32, I32,
+                                                  F32, ctypes.POINTER(PoolOpts),
+                                                  ctypes.POINTER(AttnOpts), P,
+                                                  P, P, SZ, P]),
+        "csa2_full_pool_decode_ex": (I32, [ctypes.POINTER(CacheDesc), P, P, P,
+                                           P, P, I32, I32, F32,
+                                           ctypes.POINTER(PoolOpts),
+                                           ctypes.POINTER(AttnOpts), P, P, P,
+                                           P, SZ, P]),
+        "csa2_reindex_decode_ex": (I32, [ctypes.POINTER(CacheDesc), P, I64, P,
+                                         P, P, P, P, I32, I32, F32,
+                                         ctypes.POINTER(AttnOpts), P, P, P,
+                                         SZ, P]),
         "csa2_sparse_attn_decode_ex": (I32, [ctypes.POINTER(CacheDesc), P, P,
                                              P, P, P, I32, I32, F32,
                                              ctypes.POINTER(PoolOpts),
@@ -365,7 +381,7 @@ def sparse_attn_decode_noalloc(cache, q_idx, w, q, swa, n_swa, k, scale,
 
 def sparse_attn_decode_fp4q(cache, q_codes, q_scales, w, q, swa, n_swa, k,
                             scale, pool=None, out=None, topk_out=None,
-                            ws=None):
+                            ws=None, sink=None, pos=None, rope_theta=10000.0):
     """sparse_attn_decode with an MXFP4 indexer query (pack_query_fp4
     planes)."""
     B = q.shape[0]
@@ -381,17 +397,25 @@ def sparse_attn_decode_fp4q(cache, q_codes, q_scales, w, q, swa, n_swa, k,
         need = load().csa2_workspace_size(OP_DECODE, B, cache.n_cap, k,
                                           ctypes.byref(po) if po else None)
         ws = workspace(need, dev)
-    _check(load().csa2_sparse_attn_decode_fp4q(
-        ctypes.byref(cache), _ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(q),
-        _ptr(swa), _ptr(n_swa), B, k, float(scale),
-        ctypes.byref(po) if po else None, _ptr(out), _ptr(topk_out), _ptr(ws),
-        ws.numel(), _stream()))
+    ao = _attn_opts(sink, pos, rope_theta)
+    if ao is None:
+        _check(load().csa2_sparse_attn_decode_fp4q(
+            ctypes.byref(cache), _ptr(q_codes), _ptr(q_scales), _ptr(w),
+            _ptr(q), _ptr(swa), _ptr(n_swa), B, k, float(scale),
+            ctypes.byref(po) if po else None, _ptr(out), _ptr(topk_out),
+            _ptr(ws), ws.numel(), _stream()))
+    else:
+        _check(load().csa2_sparse_attn_decode_fp4q_ex(
+            ctypes.byref(cache), _ptr(q_codes), _ptr(q_scales), _ptr(w),
+            _ptr(q), _ptr(swa), _ptr(n_swa), B, k, float(scale),
+            ctypes.byref(po) if po else None, ctypes.byref(ao), _ptr(out),
+            _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
     return out, topk_out
 
 
 def full_pool_decode(cache, q_idx, w, q, swa, n_swa, k, scale,
                      pool=(2048, 8), out=None, topk_out=None, pool_out=None,
-                     ws=None):
+                     ws=None, sink=None, pos=None, rope_theta=10000.0):
     """First Full layer of a hierarchical decoder group: returns (out bf16
     [B,64,512], topk [B,k], pool [B, n_blocks_keep*8])."""
     B = q.shape[0]
@@ -408,15 +432,24 @@ def full_pool_decode(cache, q_idx, w, q, swa, n_swa, k, scale,
         need = load().csa2_workspace_size(OP_FULL_POOL, B, cache.n_cap, k,
                                           ctypes.byref(po))
         ws = workspace(need, dev)
-    _check(load().csa2_full_pool_decode(
-        ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
-        _ptr(n_swa), B, k, float(scale), ctypes.byref(po), _ptr(out),
-        _ptr(topk_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream()))
+    ao = _attn_opts(sink, pos, rope_theta)
+    if ao is None:
+        _check(load().csa2_full_pool_decode(
+            ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
+            _ptr(n_swa), B, k, float(scale), ctypes.byref(po), _ptr(out),
+            _ptr(topk_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream()))
+    else:
+        _check(load().csa2_full_pool_decode_ex(
+            ctypes.byref(cache), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(swa),
+            _ptr(n_swa), B, k, float(scale), ctypes.byref(po),
+            ctypes.byref(ao), _ptr(out), _ptr(topk_out), _ptr(pool_out),
+            _ptr(ws), ws.numel(), _stream()))
     return out, topk_out, pool_out
 
 
 def reindex_decode(cache, pool_ids, q_idx, w, q, swa, n_swa, k, scale,
-                   out=None, topk_out=None, ws=None):
+                   out=None, topk_out=None, ws=None, sink=None, pos=None,
+                   rope_theta=10000.0):
     """Reindex layer over a pool [B, n_pool]: returns (out, topk)."""
     B, n_pool = pool_ids.shape
     dev = q.device
@@ -428,10 +461,18 @@ def reindex_decode(cache, pool_ids, q_idx, w, q, swa, n_swa, k, scale,
     if ws is None:
         need = load().csa2_workspace_size(OP_REINDEX, B, n_pool, k, None)
         ws = workspace(need, dev)
-    _check(load().csa2_reindex_decode(
-        ctypes.byref(cache), _ptr(pool_ids), n_pool, _ptr(q_idx), _ptr(w),
-        _ptr(q), _ptr(swa), _ptr(n_swa), B, k, float(scale), _ptr(out),
-        _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
+    ao = _attn_opts(sink, pos, rope_theta)
+    if ao is None:
+        _check(load().csa2_reindex_decode(
+            ctypes.byref(cache), _ptr(pool_ids), n_pool, _ptr(q_idx), _ptr(w),
+            _ptr(q), _ptr(swa), _ptr(n_swa), B, k, float(scale), _ptr(out),
+            _ptr(topk_out), _ptr(ws), ws.numel(), _stream()))
+    else:
+        _check(load().csa2_reindex_decode_ex(
+            ctypes.byref(cache), _ptr(pool_ids), n_pool, _ptr(q_idx), _ptr(w),
+            _ptr(q), _ptr(swa), _ptr(n_swa), B, k, float(scale),
+            ctypes.byref(ao), _ptr(out), _ptr(topk_out), _ptr(ws), ws.numel(),
+            _stream()))
     return out, topk_out
 
 

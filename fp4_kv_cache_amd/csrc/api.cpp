@@ -757,6 +757,19 @@ csa2_status csa2_sparse_attn_decode_fp4q(
                      stream);
 }
 
+csa2_status csa2_sparse_attn_decode_fp4q_ex(
+    const csa2_cache* kv, const uint8_t* q_codes, const uint8_t* q_scales,
+    const float* w, const uint16_t* q, const uint8_t* swa,
+    const int32_t* n_swa, int32_t B, int32_t k, float scale,
+    const csa2_pool_opts* pool, const csa2_attn_opts* opts, uint16_t* out,
+    int32_t* topk_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_scales && q_codes)
+    return fail(CSA2_ERR_INVALID_ARG, "an MXFP4 query needs q_scales");
+  return decode_impl(kv, csa2::IndexQuery{q_codes, q_scales, w}, q, swa,
+                     n_swa, B, k, scale, pool, out, topk_out, ws, ws_bytes,
+                     stream, opts);
+}
+
 }  // extern "C"
 
 csa2_status csa2_full_pool_decode(const csa2_cache* kv, const uint16_t* q_idx,
@@ -766,6 +779,20 @@ csa2_status csa2_full_pool_decode(const csa2_cache* kv, const uint16_t* q_idx,
                                   const csa2_pool_opts* pool, uint16_t* out,
                                   int32_t* topk_out, int32_t* pool_out,
                                   void* ws, size_t ws_bytes, void* stream) {
+  return csa2_full_pool_decode_ex(kv, q_idx, w, q, swa, n_swa, B, k, scale,
+                                  pool, nullptr, out, topk_out, pool_out, ws,
+                                  ws_bytes, stream);
+}
+
+csa2_status csa2_full_pool_decode_ex(
+    const csa2_cache* kv, const uint16_t* q_idx, const float* w,
+    const uint16_t* q, const uint8_t* swa, const int32_t* n_swa, int32_t B,
+    int32_t k, float scale, const csa2_pool_opts* pool,
+    const csa2_attn_opts* opts, uint16_t* out, int32_t* topk_out,
+    int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
+  csa2::AttnEpilogue epi;
+  csa2_status est = make_epilogue(opts, epi);
+  if (est) return est;
   if (!kv) return fail(CSA2_ERR_INVALID_ARG, "null cache descriptor");
   csa2_status st = check_attn_common(kv->main_codes, kv->main_scales,
                                      kv->n_cap, q, swa, n_swa, B, k, scale, out);
@@ -830,7 +857,8 @@ csa2_status csa2_full_pool_decode(const csa2_cache* kv, const uint16_t* q_idx,
   }
   if (e != hipSuccess) return hip_fail(e, "top-k and pool launch");
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
-                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
+                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s,
+                        epi);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return CSA2_OK;
 }
@@ -842,6 +870,20 @@ csa2_status csa2_reindex_decode(const csa2_cache* kv, const int32_t* pool,
                                 int32_t B, int32_t k, float scale,
                                 uint16_t* out, int32_t* topk_out, void* ws,
                                 size_t ws_bytes, void* stream) {
+  return csa2_reindex_decode_ex(kv, pool, n_pool, q_idx, w, q, swa, n_swa, B,
+                                k, scale, nullptr, out, topk_out, ws,
+                                ws_bytes, stream);
+}
+
+csa2_status csa2_reindex_decode_ex(
+    const csa2_cache* kv, const int32_t* pool, int64_t n_pool,
+    const uint16_t* q_idx, const float* w, const uint16_t* q,
+    const uint8_t* swa, const int32_t* n_swa, int32_t B, int32_t k,
+    float scale, const csa2_attn_opts* opts, uint16_t* out,
+    int32_t* topk_out, void* ws, size_t ws_bytes, void* stream) {
+  csa2::AttnEpilogue epi;
+  csa2_status est = make_epilogue(opts, epi);
+  if (est) return est;
   if (!kv) return fail(CSA2_ERR_INVALID_ARG, "null cache descriptor");
   csa2_status st = check_attn_common(kv->main_codes, kv->main_scales,
                                      kv->n_cap, q, swa, n_swa, B, k, scale, out);
@@ -879,7 +921,8 @@ csa2_status csa2_reindex_decode(const csa2_cache* kv, const int32_t* pool,
                               base + L.off_split);
   if (e != hipSuccess) return hip_fail(e, "pool top-k launch");
   e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap, topk_out,
-                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s);
+                        k, q, swa, n_swa, B, scale, out, base + L.off_attn, s,
+                        epi);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return CSA2_OK;
 }

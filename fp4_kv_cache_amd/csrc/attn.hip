@@ -29,8 +29,8 @@
 // multiply is one packed fp16 multiply after the FP4->fp16 convert (the
 // hardware convert applies only the exponent of its scale operand).  E4M3
 // window values are exact in fp16 too.  The bf16 queries are converted to
-// fp16 once (exact for |q| >= 2^-14; below that the absolute error is under
-// 2^-25), and probabilities in fp16 keep 11 significant bits.
+// fp16 once, each head prescaled by a power of two (exact; see the kernel),
+// and probabilities in fp16 keep 11 significant bits.
 //
 // The S^T output layout equals the P^T operand layout, so probabilities never
 // leave registers.  Softmax is online in float32 with the exp2 reference
@@ -492,6 +492,8 @@ struct TileState {
   f32x4 acc[32];           // O^T accumulators: dims 16*blk + 4*q4 + r
   float m_run;             // exp2 reference point (log2 units)
   float l_run;             // running sum of this lane's weights
+  float scale;             // logit scale of this lane's head (log2 units,
+                           // times the head's query prescale)
 };
 
 // Producer side of one key tile (wavefronts 4..7, `quarter` = wavefront - 4).
@@ -564,8 +566,8 @@ __device__ __forceinline__ void tile_math(
   float x[8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    x[r] = valid[4 * q4 + r] ? s0[r] * p.scale_log2 : -__builtin_inff();
-    x[4 + r] = valid[16 + 4 * q4 + r] ? s1[r] * p.scale_log2 : -__builtin_inff();
+    x[r] = valid[4 * q4 + r] ? s0[r] * st.scale : -__builtin_inff();
+    x[4 + r] = valid[16 + 4 * q4 + r] ? s1[r] * st.scale : -__builtin_inff();
   }
   float mt = x[0];
 #pragma unroll
@@ -696,12 +698,29 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
   if constexpr (FSEL)
     fused_select<CPER>(p, b, sel_ids, *reinterpret_cast<FselSmem*>(smem_raw));
   if (is_math) {
-    // The query converted to fp16; the accumulators are zeroed after the
+    // The query converted to fp16 after a power-of-two prescale per head
+    // (exact): the head's largest |q| lands in [2^14, 2^15), so no bf16
+    // value overflows fp16 and values within 2^28 of the largest convert
+    // exactly; the logit scale takes the inverse factor.  The prescale
+    // exponent is clamped to [-100, 64] (heads with max |q| >= 2^79 are
+    // outside the supported range).  The accumulators are zeroed after the
     // conversion (the raw query is dead by then).
+    float amax = 0.0f;
 #pragma unroll
     for (int s = 0; s < 16; ++s)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)(float)qraw[s][j];
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)qraw[s][j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    int ex = 0;
+    if (amax > 0.0f) frexpf(amax, &ex);          // amax < 2^ex
+    const int e = amax > 0.0f ? min(max(ex - 15, -100), 64) : 0;
+    const float qs = ldexpf(1.0f, -e);
+    st.scale = p.scale_log2 * ldexpf(1.0f, e);
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qb[s][j] = (_Float16)((float)qraw[s][j] * qs);
 #pragma unroll
     for (int s = 0; s < 16; ++s) asm volatile("" : : "v"(qb[s]));
 #pragma unroll

@@ -219,7 +219,15 @@ csa2_status csa2_topk(const float *scores, int64_t ld, const int32_t *n_valid,
  *   topk_out  [B][k] chosen ids ascending, -1 padded (for Reuse layers)
  *   n_cap     <= 2^24 here (CSA2_ERR_UNSUPPORTED beyond)
  * Keys/values are dequantised exactly (to fp16); logits, softmax and
- * accumulation are float32; probabilities enter the P.V product as fp16. */
+ * accumulation are float32; probabilities enter the P.V product as fp16.
+ * The query products run in fp16 too: each head's bf16 query is first
+ * scaled by a power of two that brings its largest |q| into [2^14, 2^15)
+ * (the logit scale takes the inverse), so every value within 2^28 of the
+ * head's largest converts exactly and none overflows.  Supported: max |q|
+ * per head below 2^79 (the prescale exponent is clamped to [-100, 64]);
+ * beyond that the output is undefined.  The same holds for every call that
+ * runs the attention (reuse, full-pool, reindex, the _ex and _fp4q
+ * variants). */
 csa2_status csa2_sparse_attn_decode(const csa2_cache *kv,
                                     const uint16_t *q_idx, const float *w,
                                     const uint16_t *q, const uint8_t *swa,
@@ -348,6 +356,31 @@ csa2_status csa2_reuse_attn_ex(const uint8_t *main_codes,
                                const int32_t *n_swa, int32_t B, float scale,
                                const csa2_attn_opts *opts, uint16_t *out,
                                void *ws, size_t ws_bytes, void *stream);
+
+/* csa2_sparse_attn_decode_fp4q_ex / csa2_full_pool_decode_ex /
+ * csa2_reindex_decode_ex -- the MXFP4-query decode and the two layer calls
+ * of the hierarchical decoder group with the same csa2_attn_opts details
+ * ([V4] 2.3 other details: they apply to every CSA head); opts NULL:
+ * identical to the plain calls, whose arguments, workspaces and outputs
+ * they share. */
+csa2_status csa2_sparse_attn_decode_fp4q_ex(
+    const csa2_cache *kv, const uint8_t *q_codes, const uint8_t *q_scales,
+    const float *w, const uint16_t *q, const uint8_t *swa,
+    const int32_t *n_swa, int32_t B, int32_t k, float scale,
+    const csa2_pool_opts *pool, const csa2_attn_opts *opts, uint16_t *out,
+    int32_t *topk_out, void *ws, size_t ws_bytes, void *stream);
+csa2_status csa2_full_pool_decode_ex(
+    const csa2_cache *kv, const uint16_t *q_idx, const float *w,
+    const uint16_t *q, const uint8_t *swa, const int32_t *n_swa, int32_t B,
+    int32_t k, float scale, const csa2_pool_opts *pool,
+    const csa2_attn_opts *opts, uint16_t *out, int32_t *topk_out,
+    int32_t *pool_out, void *ws, size_t ws_bytes, void *stream);
+csa2_status csa2_reindex_decode_ex(
+    const csa2_cache *kv, const int32_t *pool, int64_t n_pool,
+    const uint16_t *q_idx, const float *w, const uint16_t *q,
+    const uint8_t *swa, const int32_t *n_swa, int32_t B, int32_t k,
+    float scale, const csa2_attn_opts *opts, uint16_t *out,
+    int32_t *topk_out, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * csa2_compress_append -- the CSA2 write path at decode time ([KVC] 4.1

@@ -15,6 +15,17 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
+def head_rel_l2_max(a, b):
+    """The largest per-head relative L2 error of a [64][512] output (the
+    per-sequence tolerance's diagnostic); heads whose reference is all zero
+    are skipped."""
+    a = np.asarray(a, np.float64).reshape(64, -1)
+    b = np.asarray(b, np.float64).reshape(64, -1)
+    nb = np.linalg.norm(b, axis=1)
+    e = np.linalg.norm(a - b, axis=1)[nb > 0] / nb[nb > 0]
+    return float(e.max()) if e.size else 0.0
+
+
 def bf16_bits(t):
     return t.cpu().view(torch.int16).numpy().view(np.uint16)
 

@@ -106,3 +106,47 @@ def test_decode_ex_sink_and_derotation():
         e = rel_l2(out[b], ref)
         assert e <= REL_L2_TOL, (b, e)
         print(b, msg, f"rel-L2 {e:.2e}", flush=True)
+
+
+def test_group_and_fp4q_ex_sink_and_derotation():
+    """The sink and de-rotation through the other layer calls: the decoder
+    group's Full layer with its pool (csa2_full_pool_decode_ex), a Reindex
+    layer on that pool (csa2_reindex_decode_ex) and the MXFP4-query decode
+    (csa2_sparse_attn_decode_fp4q_ex); each output against the oracle's
+    attention with the same details over the call's own ids."""
+    wl = dataclasses.replace(WORKLOADS[2], cid=402, B=3, n=7000,
+                             reuse_layers=1)
+    st = workload.build(wl, DEV)
+    rng = np.random.default_rng(47)
+    sink = torch.from_numpy(rng.normal(0, 1, 64).astype(np.float32)).to(DEV)
+    pos = torch.tensor([7, 654321, 3 * 7000 - 1], dtype=torch.int32,
+                       device=DEV)
+    out0, ids0, pool = csa2.full_pool_decode(
+        st.cache, st.q_idx, st.w, st.q[0], st.swa[0], st.n_swa, wl.k,
+        st.scale, pool=(64, 8), sink=sink, pos=pos)
+    qi1, w1 = (torch.stack(t).contiguous() for t in zip(*[
+        inputs.index_query(wl, b, DEV, layer=1) for b in range(wl.B)]))
+    out1, ids1 = csa2.reindex_decode(st.cache, pool, qi1, w1, st.q[1],
+                                     st.swa[1], st.n_swa, wl.k, st.scale,
+                                     sink=sink, pos=pos)
+    qc, qs = csa2.pack_query_fp4(st.q_idx)
+    out2, ids2 = csa2.sparse_attn_decode_fp4q(
+        st.cache, qc, qs, st.w, st.q[0], st.swa[0], st.n_swa, wl.k, st.scale,
+        sink=sink, pos=pos)
+    torch.cuda.synchronize()
+    sk = sink.cpu().numpy()
+    for b in range(wl.B):
+        x = inputs.main_latents(wl, b, 0, wl.n, DEV).cpu().numpy()
+        mc, ms = O.pack_main(x)
+        for name, o, i, layer in (("full_pool", out0, ids0, 0),
+                                  ("reindex", out1, ids1, 1),
+                                  ("fp4q", out2, ids2, 0)):
+            sw = O.pack_swa(inputs.window_latents(wl, b, layer, DEV).cpu().numpy())
+            ib = i[b].cpu().numpy()
+            assert np.all(np.diff(ib[ib >= 0]) > 0), (name, b)
+            ref = O.reuse_layer_ext(mc, ms, ib, bf16_bits(st.q[layer][b]), sw,
+                                    wl.n_swa, st.scale, sink=sk,
+                                    pos=int(pos[b]))
+            e = rel_l2(o[b].float().cpu().numpy(), ref)
+            assert e <= REL_L2_TOL, (name, b, e)
+            print(name, b, f"rel-L2 {e:.2e}", flush=True)
