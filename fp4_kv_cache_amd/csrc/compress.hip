@@ -111,7 +111,9 @@ __global__ __launch_bounds__(kWaves * 64) void compress_gemm_kernel(
         part[((int64_t)slice * M + m0 + row) * kN + col0 + c] = v;
       }
     }
-    __syncthreads();
+    // The next pass reuses `red` (no barrier after the last pass: one
+    // behind global stores would hold every wavefront until they land).
+    if (m0 + kMChunk < M) __syncthreads();
   }
 }
 
@@ -119,11 +121,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// One workgroup of 512 threads per sequence, thread c owning channel c.
-// Everything it reads -- its quarter of a W^IK row (K^I output c / 4) and
-// the slice partials of its channel -- is requested at the start, so the
-// kernel waits for memory about once.  MT: a bound on m known at compile
-// time (the tokens' loads unrolled), or 0 for a loop over tokens.
+// Four workgroups of 512 threads per sequence (blockIdx.y = j), thread c
+// owning channel c: each forms the pooled row C_bar and computes MX block j
+// of K^I (outputs 32j .. 32j+31); workgroup 0 also writes the main entry
+// and the window rows.  Everything a workgroup reads -- the slice partials
+// of its channels and its 32 rows of W^IK (thread c: 32 weights of output
+// 32j + c/16) -- is requested at the start, so it waits for memory about
+// once.  MT: a bound on m known at compile time (the tokens' loads
+// unrolled), or 0 for a loop over tokens.
 template <int MT>
 __global__ __launch_bounds__(512) void compress_epilogue_kernel(
     const float* __restrict__ part, int M, int m, int S,
@@ -135,28 +140,29 @@ __global__ __launch_bounds__(512) void compress_epilogue_kernel(
     float* __restrict__ ki_out, float* __restrict__ c_out) {
   __shared__ __align__(16) float cbar[512];
   __shared__ float kpart[512];
-  __shared__ float ki[128];
-  const int b = blockIdx.x, c = threadIdx.x;
-  const int o = c >> 2, qt = c & 3;         // K^I output, quarter of its dot
+  const int b = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
+  const bool lead = j == 0;                 // writes the main entry, window
+  const int o = 32 * j + (c >> 4), sx = c & 15;   // output, its sixteenth
   const u32x4* wr =
-      reinterpret_cast<const u32x4*>(w_ik + (int64_t)o * 512 + 128 * qt);
-  u32x4 wv[16];
+      reinterpret_cast<const u32x4*>(w_ik + (int64_t)o * 512 + 32 * sx);
+  u32x4 wv[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) wv[j] = wr[j];
+  for (int i = 0; i < 4; ++i) wv[i] = wr[i];
   const int slot = swa != nullptr ? swa_slot[b] : 0;
 
   // C and Z of this channel for each token: the slices summed in order.
+  // Every slice's load is issued unconditionally (slices past S read slice
+  // S-1 and are not summed), so they are all in flight at once.
   float cv[kMaxM], zv[kMaxM];
   auto token = [&](int i) {
     const int64_t row = (int64_t)b * m + i;
     float pc[kMaxS], pz[kMaxS];
 #pragma unroll
     for (int s = 0; s < kMaxS; ++s) {
-      if (s < S) {                      // S is uniform: no divergence
-        const int64_t at = ((int64_t)s * M + row) * kN + c;
-        pc[s] = part[at];
-        pz[s] = part[at + 512];
-      }
+      const int sl = s < S ? s : S - 1;
+      const int64_t at = ((int64_t)sl * M + row) * kN + c;
+      pc[s] = part[at];
+      pz[s] = part[at + 512];
     }
     float cs = 0.0f, zs = 0.0f;
 #pragma unroll
@@ -183,60 +189,80 @@ __global__ __launch_bounds__(512) void compress_epilogue_kernel(
   }
   const float v = num / den;
   cbar[c] = v;
-  if (cbar_out) cbar_out[(int64_t)b * 512 + c] = v;
-  for (int i = 0; i < m; ++i) {
-    if (c_out) c_out[((int64_t)b * m + i) * 512 + c] = cv[i];
-    if (swa) {
-      const int w = ((slot + i) % kWindow + kWindow) % kWindow;
-      swa[((int64_t)b * kWindow + w) * 512 + c] =
-          (uint8_t)e4m3_from_f64((double)cv[i]);
+  if (lead) {
+    if (cbar_out) cbar_out[(int64_t)b * 512 + c] = v;
+    for (int i = 0; i < m; ++i) {
+      if (c_out) c_out[((int64_t)b * m + i) * 512 + c] = cv[i];
+      if (swa) {
+        const int w = ((slot + i) % kWindow + kWindow) % kWindow;
+        swa[((int64_t)b * kWindow + w) * 512 + c] =
+            (uint8_t)e4m3_from_f64((double)cv[i]);
+      }
     }
   }
   __syncthreads();
-  // K^I = C_bar W^IK: a quarter of output o's dot per thread, then the four
-  // quarters in order.
+  // K^I = C_bar W^IK: a sixteenth of output o's dot per thread (channels
+  // 32sx .. 32sx+31), then the sixteen in order.
   float acc = 0.0f;
-  const float4* cb4 = reinterpret_cast<const float4*>(cbar + 128 * qt);
+  const float4* cb4 = reinterpret_cast<const float4*>(cbar + 32 * sx);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float4 x0 = cb4[2 * j], x1 = cb4[2 * j + 1];
+  for (int i = 0; i < 4; ++i) {
+    const float4 x0 = cb4[2 * i], x1 = cb4[2 * i + 1];
     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc += bf16_bits_to_f32(wv[j][e] & 0xFFFFu) * xs[2 * e];
-      acc += bf16_bits_to_f32(wv[j][e] >> 16) * xs[2 * e + 1];
+      acc += bf16_bits_to_f32(wv[i][e] & 0xFFFFu) * xs[2 * e];
+      acc += bf16_bits_to_f32(wv[i][e] >> 16) * xs[2 * e + 1];
     }
   }
   kpart[c] = acc;
   __syncthreads();
-  if (c < 128)
-    ki[c] = ((kpart[4 * c] + kpart[4 * c + 1]) + kpart[4 * c + 2]) +
-            kpart[4 * c + 3];
-  __syncthreads();
   const int64_t row = rows[b];
   const bool ok = row >= 0 && row < n_cap;   // other rows are not written
   const int64_t er = (int64_t)b * n_cap + row;
-  if (c < 32 && ok) {
-    float x[16];
+  // The append, one value per thread (the same arithmetic as
+  // quant_main_group / quant_idx_block, spread over lanes): a group's
+  // amax over its lanes, each lane's code, and 8 codes OR-ed into a word.
+  auto or8 = [](uint32_t x) {
+    x |= __shfl_xor(x, 1);
+    x |= __shfl_xor(x, 2);
+    return x | __shfl_xor(x, 4);
+  };
+  if (lead) {
+    // Main row: channel c in group c / 16 (16 lanes of one wavefront).
+    const float x = cbar[c];
+    float amax = fabsf(x);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = cbar[16 * c + i];
-    uint32_t w[2], sc;
-    quant_main_group(x, w, sc);
-    *reinterpret_cast<uint2*>(main_codes + er * 256 + 8 * c) =
-        make_uint2(w[0], w[1]);
-    main_scales[er * 32 + c] = (uint8_t)sc;
-  } else if (c >= 64 && c < 68 && ok) {
-    const int blk = c - 64;
-    float x[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = ki[32 * blk + i];
-    uint32_t w[4], sb;
-    quant_idx_block(x, w, sb);
-    *reinterpret_cast<uint4*>(idx_codes + er * 64 + 16 * blk) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-    idx_scales[er * 4 + blk] = (uint8_t)sb;
+    for (int sh = 1; sh < 16; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+    const uint32_t sc = e4m3_from_f64((double)amax / 6.0);
+    const float sg = e4m3_to_f32(sc);
+    const uint32_t code = sg > 0.0f ? e2m1_code_scaled(x, sg)
+                                    : (signbit(x) ? 8u : 0u);
+    const uint32_t word = or8(code << (4 * (c & 7)));
+    if (ok && (c & 7) == 0)
+      *reinterpret_cast<uint32_t*>(main_codes + er * 256 + 4 * (c >> 3)) = word;
+    if (ok && (c & 15) == 0) main_scales[er * 32 + (c >> 4)] = (uint8_t)sc;
   }
-  if (ki_out && c < 128) ki_out[(int64_t)b * 128 + c] = ki[c];
+  if (c < 32) {                           // lanes of wavefront 0
+    // Indexer key: output 32j + c of MX block j.
+    float x = kpart[16 * c];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) x += kpart[16 * c + i];
+    float amax = fabsf(x);
+#pragma unroll
+    for (int sh = 1; sh < 32; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+    int e = -127;
+    if (amax > 0.0f) {
+      e = ilogb((double)amax) - 2;          // largest E2M1 exponent is 2
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    const uint32_t code = e2m1_code_f64((double)x * ldexp(1.0, -e));
+    const uint32_t word = or8(code << (4 * (c & 7)));
+    if (ok && (c & 7) == 0)
+      *reinterpret_cast<uint32_t*>(idx_codes + er * 64 + 16 * j + 4 * (c >> 3)) = word;
+    if (ok && c == 0) idx_scales[er * 4 + j] = (uint8_t)(e + 127);
+    if (ki_out) ki_out[(int64_t)b * 128 + 32 * j + c] = x;
+  }
 }
 
 }  // namespace
@@ -266,7 +292,7 @@ hipError_t launch_compress(const uint16_t* h, int B, int m, int d,
   auto epi = m <= 2 ? compress_epilogue_kernel<2>
              : m <= 4 ? compress_epilogue_kernel<4>
                       : compress_epilogue_kernel<0>;
-  hipLaunchKernelGGL(epi, dim3((unsigned)B), dim3(512), 0, s, part, M, m, S,
+  hipLaunchKernelGGL(epi, dim3((unsigned)B, 4), dim3(512), 0, s, part, M, m, S,
                      w_ik, rows, n_cap, main_codes, main_scales, idx_codes,
                      idx_scales, swa, swa_slot, cbar_out, ki_out, c_out);
   return hipGetLastError();
