@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     uint32_t kk[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) kk[j] = kl[wave * T * 32 + lane * PER + j];
-    const WaveSelResult r = wave_select<PER>(kk, kloc, lss.hist[wave]);
+    const WaveCut r = wave_cut<PER>(kk, kloc, lss.hist[wave]);
     const int64_t grp = ((int64_t)b * gridDim.x + blockIdx.x) * kWaves + wave;
     uint2* co = lcand + grp * kloc;
     const uint32_t id0 = (uint32_t)(base + lane * PER);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       if (r.mask & (1u << j)) co[p++] = make_uint2(kk[j], id0 + j);
     for (int q = r.total + lane; q < kloc; q += 64)
       co[q] = make_uint2(0u, 0xFFFFFFFFu);
-    if (lane == 0) lbound[grp] = r.nval > kloc ? r.thr : 0u;
+    if (lane == 0) lbound[grp] = r.bound;
   }
   if constexpr (LOCAL == 2) {
     // Tiles past the rows hold invalid keys.

@@ -371,4 +371,95 @@ __device__ __forceinline__ WaveSelResult wave_select(const uint32_t (&key)[PER],
   return res;
 }
 
+// A cut of the wavefront's 64 * PER keys (position = lane * PER + j) that
+// keeps at most `cap` of them -- every key >= a threshold t -- and bounds
+// the rest: every valid key left out is <= bound (0 when nothing valid is
+// left out).  Unlike wave_select it does not find the cap-th key exactly:
+// one binning pass over [min, max] and the cut at the lowest bin boundary
+// with at most cap keys above it, so the kept count may fall short of cap.
+// When the top bin alone holds more than cap keys, the exact wave_select
+// decides instead (its threshold is such a bound too).  H as in wave_select.
+struct WaveCut {
+  uint32_t mask;      // kept elements of this lane (bit j)
+  int pos;            // kept elements before this lane
+  int total;          // kept in the wavefront
+  uint32_t bound;     // every valid key left out is <= bound
+};
+template <int PER>
+__device__ __forceinline__ WaveCut wave_cut(const uint32_t (&key)[PER],
+                                            int cap, int32_t* H) {
+  constexpr int kLogNB = 8;
+  const int lane = threadIdx.x & 63;
+  int nval = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (key[j]) { ++nval; mn = min(mn, key[j]); mx = max(mx, key[j]); }
+  nval = __builtin_amdgcn_readlane(wave_incl_scan(nval), 63);
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  uint32_t t = 1u;                      // keep every valid key
+  uint32_t bound = 0u;
+  if (nval > cap && mx == mn) {
+    // One key value held by more than cap keys: the exact selection.
+    const WaveSelResult r = wave_select<PER>(key, cap, H);
+    WaveCut w;
+    w.mask = r.mask;
+    w.pos = r.pos;
+    w.total = r.total;
+    w.bound = r.thr;
+    return w;
+  }
+  if (nval > cap) {
+    const int bits = 32 - __builtin_clz(mx - mn);
+    const int shift = bits > kLogNB ? bits - kLogNB : 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (key[j] >= mn) atomicAdd(&H[(mx - key[j]) >> shift], 1);
+    int4* hv = reinterpret_cast<int4*>(H) + lane;
+    const int4 c = *hv;
+    *hv = make_int4(0, 0, 0, 0);
+    // Bins from the top (bin 0 holds mx): the last bin whose running count
+    // (through it) is still <= cap.
+    const int s = c.x + c.y + c.z + c.w;
+    const int run = wave_incl_scan(s) - s;        // keys in earlier bins
+    int last = -1;                                // within this lane
+    if (run + c.x <= cap) last = 0;
+    if (run + c.x + c.y <= cap) last = 1;
+    if (run + c.x + c.y + c.z <= cap) last = 2;
+    if (run + s <= cap) last = 3;
+    const uint64_t any = __builtin_amdgcn_ballot_w64(last >= 0);
+    if (any == 0) {
+      // The top bin alone holds more than cap keys.
+      const WaveSelResult r = wave_select<PER>(key, cap, H);
+      WaveCut w;
+      w.mask = r.mask;
+      w.pos = r.pos;
+      w.total = r.total;
+      w.bound = r.nval > cap ? r.thr : 0u;
+      return w;
+    }
+    // Running counts only grow, so the qualifying bins are a prefix: the
+    // highest qualifying lane holds the cut.
+    const int hl = 63 - (int)__builtin_clzll(any);
+    const int b = 4 * hl + __builtin_amdgcn_readlane(last, hl);
+    // Bin b holds keys in [mx - ((b+1) << shift) + 1, mx - (b << shift)].
+    const int64_t low = (int64_t)mx - ((int64_t)(b + 1) << shift) + 1;
+    t = low <= (int64_t)mn ? mn : (uint32_t)low;
+    bound = t - 1u;                       // keys left out are < t
+  }
+  int cnt = 0;
+  uint32_t mask = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (key[j] != 0u && key[j] >= t) { mask |= 1u << j; ++cnt; }
+  const int incl = wave_incl_scan(cnt);
+  WaveCut w;
+  w.mask = mask;
+  w.pos = incl - cnt;
+  w.total = __builtin_amdgcn_readlane(incl, 63);
+  w.bound = nval > cap && w.total < nval ? bound : 0u;
+  return w;
+}
+
 }  // namespace csa2
