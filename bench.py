@@ -338,6 +338,29 @@ def run_workload(args, wl, headline):
     if headline and not args.no_variants:
         res["variants"] = run_variants(args, wl, st, reps, planes, R, out,
                                        ids, ws)
+    if wl.pool and not args.no_variants:
+        # The pages' decoder Full layer at this length (m = 1, every visible
+        # position scored, its own top-k and the pool of the best blocks).
+        pool_ids = torch.empty((wl.B, wl.pool[0] * wl.pool[1]),
+                               dtype=torch.int32, device=dev)
+        ws_fp = csa2.workspace(csa2.load().csa2_workspace_size(
+            csa2.OP_FULL_POOL, wl.B, wl.n, k,
+            csa2.ctypes.byref(csa2.PoolOpts(*wl.pool))), dev)
+
+        def step_full_pool(i):
+            csa2.full_pool_decode(reps[i % R], st.q_idx, st.w, st.q[0],
+                                  st.swa[0], st.n_swa, k, st.scale,
+                                  pool=wl.pool, out=out, topk_out=ids,
+                                  pool_out=pool_ids, ws=ws_fp)
+
+        fp_s, _ = graph_time(step_full_pool, K, W, [out, ids, pool_ids])
+        res["variants"] = {"full_pool_layer": {
+            "value": wl.B / fp_s, "ms_per_step": fp_s * 1e3,
+            "what": "csa2_full_pool_decode on these caches: scores over all "
+                    f"{wl.n} positions, its own top-{k} and the pool of "
+                    f"{wl.pool[0]} blocks of {wl.pool[1]} (two-stage "
+                    "selections)"}}
+        del ws_fp, pool_ids
     del reps, planes, st
     torch.cuda.empty_cache()
     return res
@@ -596,7 +619,9 @@ def main():
         "configs": {r["workload"]: {x: r[x] for x in (
             "value", "unit", "ms_per_step", "steps", "warmup",
             "layers_per_step", "config", "step_hbm", "roofline",
-            "kernels_us", "eager_ms_per_step")} for r in results[1:]},
+            "kernels_us", "eager_ms_per_step") if x in r}
+            | ({"variants": r["variants"]} if "variants" in r else {})
+            for r in results[1:]},
     }
     if "variants" in head:
         line["variants"] = head["variants"]
