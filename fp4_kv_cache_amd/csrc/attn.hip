@@ -105,34 +105,42 @@ __device__ __forceinline__ void rotate_pair(float& x, float& y, float c,
   y = ny;
 }
 
+// Kernel arguments.  A workgroup's first accesses to this block miss the
+// scalar cache one 64-byte line at a time, each a full memory latency, so
+// what the start of the kernel needs (the workgroup mapping, the query, the
+// window length and the fused selection's candidates) shares the first
+// line, and the epilogue's rotation table comes last.
 struct AttnArgs {
+  int B;
+  int splits;
+  int k;
+  int n_wg, kloc;          // fused selection: groups and pairs per group
+  int tiles_per_split;
+  const uint16_t* q;
+  const int32_t* n_swa;
+  const uint2* lcand;      // [B][n_wg][kloc] (key, id), id order
+  const uint32_t* lbound;  // [B][n_wg]
+  // -- 64 bytes
   const uint8_t* main_codes;
   const uint8_t* main_scales;
   int64_t n_cap;
   const int32_t* topk;
-  int k;
-  const uint16_t* q;
   const uint8_t* swa;
-  const int32_t* n_swa;
   float scale_log2;        // scale * log2(e)
+  int n_tiles;
   uint16_t* out;           // final output when splits == 1
   uint16_t* part_o;        // [B][S][64][512] fp16, normalised per split
   float* part_ml;          // [B][S][64][2] (max in log2 units, sum)
-  int B;
-  int splits;
-  int tiles_per_split;
-  int n_tiles;
-  AttnEpilogue epi;        // sink and de-rotation (final output only)
   // Fused selection (the decode path): every workgroup selects its
   // sequence's top-k itself from the indexer's local candidates.
-  const uint2* lcand;      // [B][n_wg][kloc] (key, id), id order
-  const uint32_t* lbound;  // [B][n_wg]
-  int n_wg, kloc;
   const uint32_t* keys;    // [B][ld] selection keys (exact fallback)
   int64_t ld;
   const int32_t* n_entries;
   int32_t* topk_out;       // [B][k], written by each sequence's split 0
+  AttnEpilogue epi;        // sink and de-rotation (final output only)
 };
+static_assert(offsetof(AttnArgs, lbound) + sizeof(void*) <= 64,
+              "the kernel's first accesses share one line");
 
 // Shared memory of the fused selection (512 threads), overlaid on the
 // attention's tile buffers, which are not in use yet: the candidate pass,
@@ -140,6 +148,7 @@ struct AttnArgs {
 struct CandSmem {
   int32_t hist[4][256];             // one histogram per narrowing pass
   uint32_t red[4][8];
+  uint2 stage[4096];                // the candidates, in their global order
 };
 struct FselSmem {
   union {
@@ -209,20 +218,27 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
   if (tid < 256) reinterpret_cast<int4*>(&cs.hist[0][0])[tid] = make_int4(0, 0, 0, 0);
   const int C = p.n_wg * p.kloc;
   const uint2* cr = p.lcand + (int64_t)b * C;
-  uint32_t kk[PER];
-  int32_t ci[PER];
+  // The candidates arrive in coalesced passes (pass j: pairs 512j + tid)
+  // and go through LDS, so that thread tid then holds pairs PER*tid ..
+  // PER*tid+PER-1, consecutive in id order.  Read straight into that order,
+  // every wavefront load would touch 32 cache lines for 512 bytes.
+  uint2 v[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = tid * PER + j;
-    const uint2 v = cr[i < C ? i : C - 1];
-    kk[j] = i < C ? v.x : 0u;
-    ci[j] = (int32_t)v.y;
+    const int i = 512 * j + tid;
+    v[j] = cr[i < C ? i : C - 1];
   }
-  uint32_t lb = 0u, km = 0u;
-  for (int i = tid; i < p.n_wg; i += 512)
-    lb = max(lb, p.lbound[(int64_t)b * p.n_wg + i]);
+  // One bound per thread (n_wg <= kLocalMaxCands / 8 = 512), loaded
+  // unconditionally from a clamped index so nothing waits for it yet.
+  static_assert(kLocalMaxCands / 8 <= 512, "one bound per thread");
+  const uint32_t lbv =
+      p.lbound[(int64_t)b * p.n_wg + (tid < p.n_wg ? tid : p.n_wg - 1)];
+  uint32_t lb = tid < p.n_wg ? lbv : 0u, km = 0u;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) km = max(km, kk[j]);
+  for (int j = 0; j < PER; ++j) {
+    if (512 * j + tid < C) km = max(km, v[j].x);
+    cs.stage[512 * j + tid] = v[j];
+  }
   lb = wave_max_u32(lb);
   km = wave_max_u32(km);
   if (lane == 0) {
@@ -230,6 +246,15 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     cs.red[1][wv] = km;
   }
   __syncthreads();
+  uint32_t kk[PER];
+  int32_t ci[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid * PER + j;
+    const uint2 w = cs.stage[i];
+    kk[j] = i < C ? w.x : 0u;
+    ci[j] = (int32_t)w.y;
+  }
   uint32_t L = 0u, MX = 0u;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
@@ -297,12 +322,14 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     // Chosen: take_all -> every key >= lo (all keys above L when the first
     // pass took them all); else keys > hi (= lo) plus the first `need` keys
     // equal to lo.  One packed scan (ties << 16 | greater).
+    // (lo >= L + 1 >= 1 here, so a zeroed key is never chosen; the loops
+    // below are branch-free: a key's place, or a spare slot past k.)
     int ngt = 0, ntie = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      if (!kk[j]) continue;
-      if (take_all) ngt += kk[j] >= lo;
-      else { ngt += kk[j] > hi; ntie += kk[j] == lo; }
+      const uint32_t key = kk[j];
+      ngt += (key != 0u) & (take_all ? key >= lo : key > hi);
+      ntie += (key != 0u) & !take_all & (key == lo);
     }
     const int x = (ntie << 16) | ngt;
     const int incl = wave_incl_scan(x);
@@ -322,13 +349,13 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     const int total = (tot & 0xFFFF) + (take_all ? 0 : min(tot >> 16, need));
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      bool sel = false;
-      if (kk[j]) {
-        if (take_all) sel = kk[j] >= lo;
-        else if (kk[j] > hi) sel = true;
-        else if (kk[j] == lo) { sel = tie_rank < need; ++tie_rank; }
-      }
-      if (sel) sel_ids[q++] = ci[j];
+      const uint32_t key = kk[j];
+      const bool gt = (key != 0u) & (take_all ? key >= lo : key > hi);
+      const bool tie = (key != 0u) & !take_all & (key == lo);
+      const bool sel = gt | (tie & (tie_rank < need));
+      tie_rank += tie;
+      sel_ids[sel ? q : kMaxK] = ci[j];
+      q += sel;
     }
     for (q = total + tid; q < k; q += 512) sel_ids[q] = -1;
   } else {
@@ -478,8 +505,9 @@ __device__ __forceinline__ void dequant_store(const Raw& raw, uint32_t kinds,
 }
 
 // Workgroup -> (sequence, split), placing all splits of a sequence on one
-// XCD: workgroups are dealt to the 8 XCDs round-robin by their linear id,
-// so id % 8 picks the XCD and sequences b with b % 8 == id % 8 live there.
+// XCD: workgroups are dealt to the 8 XCDs round-robin by their linear id
+// (from a starting XCD that rotates between launches), so the ids of one
+// sequence, which agree mod 8, land on one XCD.
 __device__ __forceinline__ bool map_workgroup(int id, int B, int S, int& b,
                                               int& split) {
   const int xcd = id & 7, slot = id >> 3;
@@ -637,7 +665,7 @@ __device__ __forceinline__ void tile_math(
 // selection's store first), then the selected ids of a fused selection.
 constexpr int kFselBytes = (int)sizeof(FselSmem);
 constexpr int kUnionBytes = (kSmemBytes > kFselBytes ? kSmemBytes : kFselBytes);
-constexpr int kFusedSmemBytes = kUnionBytes + kMaxK * 4;
+constexpr int kFusedSmemBytes = kUnionBytes + (kMaxK + 64) * 4;  // + spare
 
 template <bool FSEL, int CPER>
 __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
@@ -659,7 +687,13 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
   const int col = lane & 15;          // head within the wave / row in A
   const int q4 = lane >> 4;           // k-slot group
   const int head = 16 * wave + col;
-  const int nswa_raw = p.n_swa[b];
+  // The window length is loaded per lane (the zero offset is hidden from
+  // the compiler, which would otherwise use a scalar load and wait for it
+  // at once to free its register): its latency then overlaps the
+  // selection instead of delaying the candidate loads.
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  const int nswa_raw = p.n_swa[b + zero];
   const int nswa = nswa_raw < 0 ? 0 : (nswa_raw > kWindow ? kWindow : nswa_raw);
 
   const int t0 = split * p.tiles_per_split;

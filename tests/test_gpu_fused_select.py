@@ -5,8 +5,10 @@ whole key row when the candidates cannot be shown to hold the top k.
 
 Cases: sequences whose winners are spread (the candidate path), all-equal
 scores (every group ties at its bound: fallback), one group holding far
-more winners than it keeps (fallback), rows shorter than k, and the
-top-k ids written to topk_out by the same call."""
+more winners than it keeps (fallback), rows shorter than k, the top-k ids
+written to topk_out by the same call, and every split count the attention
+plans, each sequence of the batch checked, twice in a row on the same
+workspace."""
 import dataclasses
 
 import numpy as np
@@ -16,7 +18,8 @@ import torch
 from oracle import csa2 as O
 from fp4_kv_cache_amd import csa2, inputs, workload
 from fp4_kv_cache_amd.inputs import WORKLOADS
-from _util import REL_L2_TOL, bf16_bits, rel_l2, topk_set_ok
+from _util import (REL_L2_TOL, bf16_bits, planned_splits, rel_l2,
+                   split_parts_bytes, topk_set_ok)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -103,3 +106,40 @@ def test_fused_select_crowded_group():
     for b in range(wl.B):
         print(b, _check(st, out, ids, b, wl.n))
         assert set(range(100, 300)) <= set(ids[b].tolist())
+
+
+def _split_shape(S):
+    best = None
+    for B in range(1, 41):
+        for k in (64, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048):
+            if planned_splits(B, k) == S and (best is None or
+                                              B * k < best[0] * best[1]):
+                best = (B, k)
+    return best
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 6, 7, 8, 9, 10, 12, 16])
+def test_fused_decode_every_split_count(S):
+    """The decode call at a batch and k the split planner maps to S splits
+    (confirmed through the attention part of the workspace), every sequence
+    against the oracle; the call runs twice on one workspace and must give
+    the same bits."""
+    B, k = _split_shape(S)
+    n = max(4 * k, 4096)
+    wl = dataclasses.replace(WORKLOADS[1], cid=210 + S, B=B, n=n, k=k)
+    st = workload.build(wl, DEV)
+    ws_b = csa2.workspace_size(csa2.OP_REUSE, B, n, k)
+    assert ws_b == split_parts_bytes(B, S), (B, k, ws_b)
+    ws = csa2.workspace(csa2.workspace_size(csa2.OP_DECODE, B, n, k), DEV)
+    res = []
+    for _ in range(2):
+        out, ids = csa2.sparse_attn_decode(st.cache, st.q_idx, st.w, st.q[0],
+                                           st.swa[0], st.n_swa, k, st.scale,
+                                           ws=ws)
+        torch.cuda.synchronize()
+        res.append((out.float().cpu().numpy(), ids.cpu().numpy()))
+    assert np.array_equal(res[0][1], res[1][1])
+    assert np.array_equal(res[0][0], res[1][0])
+    out, ids = res[1]
+    for b in range(B):
+        _check(st, out, ids, b, n)
