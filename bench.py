@@ -250,7 +250,14 @@ def decode_kernels(wl):
     """The possible kernel sequences of one decode call, in launch order
     (top-k selections in one workgroup per row, or in two stages)."""
     if wl.pool:
-        return [["block_scan", "block_topk", "pool_scan", "pool_topk",
+        # The pool scan keeps local candidates and the attention selects
+        # from them (one sequence per block selection variant), or, for
+        # pools the fused selection cannot take, a separate selection.
+        return [["block_scan", "block_topk", "pool_scan_local",
+                 "attention_fused_select", "split_merge"],
+                ["block_scan", "block_chunk_select", "block_union_select",
+                 "pool_scan_local", "attention_fused_select", "split_merge"],
+                ["block_scan", "block_topk", "pool_scan", "pool_topk",
                  "attention", "split_merge"],
                 ["block_scan", "block_chunk_select", "block_union_select",
                  "pool_scan", "pool_chunk_select", "pool_union_select",

@@ -117,6 +117,11 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     L.off_split = off;
     off += std::max(csa2::split_workspace(B, L.nb, L.kb),
                     csa2::split_workspace(B, L.n_cand, k));
+    // Local candidates of the pool scan for the fused selection.
+    L.off_lcand = off;
+    off += align256((size_t)B * csa2::kLocalMaxCands * 8);
+    L.off_lbound = off;
+    off += align256((size_t)B * (csa2::kLocalMaxCands / 8) * 4);
   }
   L.off_attn = off;
   off += align256(csa2::attn_workspace(B, k));
@@ -156,7 +161,8 @@ FullPoolLayout full_pool_layout(int B, int64_t n_cap, int k, int kb) {
 
 // Workspace of csa2_reindex_decode: pool keys, their tile maxima, attention.
 struct ReindexLayout {
-  size_t off_scores = 0, off_tmax = 0, off_split = 0, off_attn = 0, total = 0;
+  size_t off_scores = 0, off_tmax = 0, off_split = 0, off_lcand = 0,
+         off_lbound = 0, off_attn = 0, total = 0;
 };
 ReindexLayout reindex_layout(int B, int64_t n_pool, int k) {
   ReindexLayout L;
@@ -167,6 +173,10 @@ ReindexLayout reindex_layout(int B, int64_t n_pool, int k) {
   off += align256((size_t)B * tiles_of(n_pool) * 4);
   L.off_split = off;
   off += csa2::split_workspace(B, n_pool, k);
+  L.off_lcand = off;
+  off += align256((size_t)B * csa2::kLocalMaxCands * 8);
+  L.off_lbound = off;
+  off += align256((size_t)B * (csa2::kLocalMaxCands / 8) * 4);
   L.off_attn = off;
   off += align256(csa2::attn_workspace(B, k));
   L.total = off;
@@ -643,6 +653,29 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
                                 base + L.off_split);
     if (e != hipSuccess) return hip_fail(e, "block top-k launch");
     CSA2_MARK(lm);
+    const csa2::LocalPlan pp = csa2::local_plan(B, L.n_cand, k,
+                                                iq.q_scales != nullptr, true);
+    if (pp.ok) {
+      // The pool scan keeps local candidates; the attention workgroups
+      // select the pool's top-k themselves.
+      uint32_t* pkeys = reinterpret_cast<uint32_t*>(pscores);
+      uint2* lcand = reinterpret_cast<uint2*>(base + L.off_lcand);
+      uint32_t* lbound = reinterpret_cast<uint32_t*>(base + L.off_lbound);
+      e = csa2::launch_indexer_local(kv->idx_codes, kv->idx_scales, kv->n_cap,
+                                     kv->n_entries, iq, B, pkeys, pp, lcand,
+                                     lbound, s, pool_ids, L.n_cand);
+      if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
+      CSA2_MARK(lm);
+      csa2::FusedSelect fs{lcand, lbound, pp.n_wg, pp.kloc, pkeys,
+                           round32(L.n_cand), nullptr, topk_out};
+      fs.ids = pool_ids;
+      fs.n_ids = L.n_cand;
+      e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap,
+                            topk_out, k, q, swa, n_swa, B, scale, out,
+                            base + L.off_attn, s, epi, &fs, &lm);
+      if (e != hipSuccess) return hip_fail(e, "attention launch");
+      return CSA2_OK;
+    }
     e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
                              kv->n_cap, kv->n_entries, pool_ids, L.n_cand,
                              iq, B, pscores, s, tmax);
@@ -911,10 +944,31 @@ csa2_status csa2_reindex_decode_ex(
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* scores = reinterpret_cast<float*>(base + L.off_scores);
   uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
-  hipError_t e = csa2::launch_indexer(
-      CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales, kv->n_cap,
-      kv->n_entries, pool, n_pool, csa2::IndexQuery{q_idx, nullptr, w}, B,
-      scores, s, tmax);
+  const csa2::IndexQuery iq{q_idx, nullptr, w};
+  hipError_t e;
+  const csa2::LocalPlan pp = csa2::local_plan(B, n_pool, k, false, true);
+  if (pp.ok) {
+    // Local candidates of the pool, selected inside the attention.
+    uint32_t* keys = reinterpret_cast<uint32_t*>(scores);
+    uint2* lcand = reinterpret_cast<uint2*>(base + L.off_lcand);
+    uint32_t* lbound = reinterpret_cast<uint32_t*>(base + L.off_lbound);
+    e = csa2::launch_indexer_local(kv->idx_codes, kv->idx_scales, kv->n_cap,
+                                   kv->n_entries, iq, B, keys, pp, lcand,
+                                   lbound, s, pool, n_pool);
+    if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
+    csa2::FusedSelect fs{lcand, lbound, pp.n_wg, pp.kloc, keys,
+                         round32(n_pool), nullptr, topk_out};
+    fs.ids = pool;
+    fs.n_ids = n_pool;
+    e = csa2::launch_attn(kv->main_codes, kv->main_scales, kv->n_cap,
+                          topk_out, k, q, swa, n_swa, B, scale, out,
+                          base + L.off_attn, s, epi, &fs);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return CSA2_OK;
+  }
+  e = csa2::launch_indexer(CSA2_KEYS_MXFP4, kv->idx_codes, kv->idx_scales,
+                           kv->n_cap, kv->n_entries, pool, n_pool, iq, B,
+                           scores, s, tmax);
   if (e != hipSuccess) return hip_fail(e, "pool indexer launch");
   e = csa2::launch_row_select(scores, tmax, true, round32(n_pool), n_pool,
                               nullptr, pool, B, k, 1, nullptr, topk_out, s, 1,

@@ -136,6 +136,8 @@ struct AttnArgs {
   const uint32_t* keys;    // [B][ld] selection keys (exact fallback)
   int64_t ld;
   const int32_t* n_entries;
+  const int32_t* fb_ids;   // [B][fb_n] entry ids of the key rows, or null
+  int64_t fb_n;
   int32_t* topk_out;       // [B][k], written by each sequence's split 0
   AttnEpilogue epi;        // sink and de-rotation (final output only)
 };
@@ -188,6 +190,20 @@ __device__ __forceinline__ int32_t load_ids(const AttnArgs& p,
   const int slot = ((lane & 8) ? tb : ta) * kTile + slot_of(quarter, lane & 7);
   return ids[slot < p.k ? slot : 0];
 }
+
+// Key rows of the fused selection's exact fallback: positions are the entry
+// ids, or `idrow` names them (a pool's rows; ids ascending where valid, -1
+// rows taking key 0).
+struct FallbackSrc {
+  const uint32_t* row;
+  const int32_t* idrow;
+  __device__ __forceinline__ void load(int64_t i, uint32_t& r,
+                                       int32_t& id) const {
+    r = row[i];
+    id = idrow ? idrow[i] : (int32_t)i;
+  }
+  __device__ static __forceinline__ uint32_t key(uint32_t r) { return r; }
+};
 
 // The fused selection: the exact top-k of sequence b from the indexer's
 // local candidates (the k largest pair keys, equal keys to the lower id,
@@ -364,9 +380,13 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     __syncthreads();
     for (int i = tid; i < 8 * 256; i += 512) (&fs.sel.hist[0][0])[i] = 0;
     __syncthreads();
-    const int32_t ne = p.n_entries[b];
-    const int64_t len = ne <= 0 ? 0 : ((int64_t)ne < p.n_cap ? ne : p.n_cap);
-    const ScoreSrc<false, true> src{p.keys + (int64_t)b * p.ld, nullptr};
+    int64_t len = p.fb_n;
+    if (p.fb_ids == nullptr) {
+      const int32_t ne = p.n_entries[b];
+      len = ne <= 0 ? 0 : ((int64_t)ne < p.n_cap ? ne : p.n_cap);
+    }
+    const FallbackSrc src{p.keys + (int64_t)b * p.ld,
+                          p.fb_ids ? p.fb_ids + (int64_t)b * p.fb_n : nullptr};
     const int cnt = stream_select<512>(fs, len, p.k, src);
     for (int q = tid; q < p.k; q += 512) sel_ids[q] = q < cnt ? fs.id[q] : -1;
   }
@@ -1040,6 +1060,8 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
     a.ld = fsel->ld;
     a.n_entries = fsel->n_entries;
     a.topk_out = fsel->topk_out;
+    a.fb_ids = fsel->ids;
+    a.fb_n = fsel->n_ids;
     // Candidate pairs per thread.
     if (C <= 1024) e = launch_attn_kernel<true, 2>(a, grid, s);
     else if (C <= 2048) e = launch_attn_kernel<true, 4>(a, grid, s);

@@ -138,6 +138,24 @@ template <int KEYFMT, bool SCALED> struct Depth {
   static constexpr int value = SCALED ? 3 : 2;
 };
 
+// Entry ids of rows id0 .. id0+PER-1 of a local-candidate group: the rows
+// themselves, or with candidate ids the entries they name (rows past the end
+// read the last row; their keys are 0, so they are never kept).
+template <bool CAND, int PER>
+__device__ __forceinline__ void entry_ids(const int32_t* cand, int b,
+                                          int64_t n_rows, uint32_t id0,
+                                          uint32_t (&eid)[PER]) {
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if constexpr (CAND) {
+      const int64_t i = (int64_t)id0 + j;
+      eid[j] = (uint32_t)cand[(int64_t)b * n_rows + (i < n_rows ? i : n_rows - 1)];
+    } else {
+      eid[j] = id0 + j;
+    }
+  }
+}
+
 // KEYS: write selection keys (see score_key) instead of float scores, and
 // each 32-row tile's largest key to tmax[B][ceil(n_rows/32)]; with `bmax`
 // also each 8-row block's largest key to bmax[B][round32(nb)] (nb =
@@ -146,9 +164,11 @@ template <int KEYFMT, bool SCALED> struct Depth {
 // QFP4: the query is MXFP4 planes (codes q[B][32][64], scales
 // q_scales[B][32][4]) instead of bf16 q[B][32][128].  BLK (with KEYS):
 // the block maxima are written too.
-// LOCAL (with KEYS; all rows, no candidates): instead of tile maxima, each
-// group of rows also keeps its own local top-kloc entries as (key, id)
-// pairs, in id order, in lcand[B][groups][kloc] (key 0 / id -1 padding), and
+// LOCAL (with KEYS): instead of tile maxima, each group of rows also keeps
+// its own local top-kloc entries as (key, id) pairs, in row order, in
+// lcand[B][groups][kloc] (key 0 / id -1 padding; the id is the row, or with
+// CAND the entry the row names, so ids run in row order whenever the
+// candidate ids ascend), and
 // in lbound[B][groups] a key at or above every valid entry it left out (0
 // when it left none out).  The union of every group's pairs then holds the
 // row's top-k whenever the k-th largest pair key is above every bound: a
@@ -169,8 +189,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int D = Depth<KEYFMT, kScaledOp>::value;
   constexpr int T = TPW;
-  static_assert(LOCAL == 0 || (KEYS && !BLK && !CAND && KEYFMT == 0),
-                "local candidates: MXFP4 keys, all rows, selection keys");
+  static_assert(LOCAL == 0 || (KEYS && !BLK && KEYFMT == 0),
+                "local candidates: MXFP4 keys, selection keys");
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -388,14 +408,16 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     uint32_t kk[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) kk[j] = kl[wave * T * 32 + lane * PER + j];
+    const uint32_t id0 = (uint32_t)(base + lane * PER);
+    uint32_t eid[PER];
+    entry_ids<CAND, PER>(cand, b, n_rows, id0, eid);
     const WaveCut r = wave_cut<PER>(kk, kloc, lss.hist[wave]);
     const int64_t grp = ((int64_t)b * gridDim.x + blockIdx.x) * kWaves + wave;
     uint2* co = lcand + grp * kloc;
-    const uint32_t id0 = (uint32_t)(base + lane * PER);
     int p = r.pos;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      if (r.mask & (1u << j)) co[p++] = make_uint2(kk[j], id0 + j);
+      if (r.mask & (1u << j)) co[p++] = make_uint2(kk[j], eid[j]);
     for (int q = r.total + lane; q < kloc; q += 64)
       co[q] = make_uint2(0u, 0xFFFFFFFFu);
     if (lane == 0) lbound[grp] = r.bound;
@@ -412,14 +434,16 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     uint32_t kk[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) kk[j] = kl[tid * PER + j];
+    const uint32_t id0 = (uint32_t)(blockIdx.x * (kWaves * T * 32) + tid * PER);
+    uint32_t eid[PER];
+    entry_ids<CAND, PER>(cand, b, n_rows, id0, eid);
     const SelResult r = block_select<256, PER, 256>(kk, kloc, lss);
     const int64_t wg = (int64_t)b * gridDim.x + blockIdx.x;
     uint2* co = lcand + wg * kloc;
-    const uint32_t id0 = (uint32_t)(blockIdx.x * (kWaves * T * 32) + tid * PER);
     int p = r.pos;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      if (r.mask & (1u << j)) co[p++] = make_uint2(kk[j], id0 + j);
+      if (r.mask & (1u << j)) co[p++] = make_uint2(kk[j], eid[j]);
     for (int q = r.total + tid; q < kloc; q += 256)
       co[q] = make_uint2(0u, 0xFFFFFFFFu);
     // Every valid entry left out is <= thr (the selection ends on the k-th
@@ -488,31 +512,32 @@ void launch_q(int B, hipStream_t s, const void* k_codes,
                                     n_entries, cand, n_rows, iq, scores, tmax,
                                     bmax, btmax, n_div);
 }
-template <bool QFP4, int T, int LOCAL>
+template <bool QFP4, int T, int LOCAL, bool CAND>
 hipError_t launch_local(int B, hipStream_t s, const void* k_codes,
                         const uint8_t* k_scales, int64_t n_cap,
-                        const int32_t* n_entries, const IndexQuery& iq,
-                        uint32_t* keys, const LocalPlan& lp, uint2* lcand,
-                        uint32_t* lbound) {
+                        const int32_t* n_entries, const int32_t* cand,
+                        int64_t n_rows, const IndexQuery& iq, uint32_t* keys,
+                        const LocalPlan& lp, uint2* lcand, uint32_t* lbound) {
   const int smem = (kWaves * T * 32 + kWaves * 256 + 16) * 4;
   const int64_t epb = (int64_t)kWaves * T * 32;
   hipLaunchKernelGGL(
-      (indexer_kernel<0, true, QFP4, false, false, T, LOCAL>),
-      dim3((unsigned)((n_cap + epb - 1) / epb), (unsigned)B), dim3(256), smem,
-      s, k_codes, k_scales, n_cap, n_entries, nullptr, n_cap, iq.q,
+      (indexer_kernel<0, true, QFP4, false, CAND, T, LOCAL>),
+      dim3((unsigned)((n_rows + epb - 1) / epb), (unsigned)B), dim3(256),
+      smem, s, k_codes, k_scales, n_cap, n_entries, cand, n_rows, iq.q,
       iq.q_scales, iq.w, reinterpret_cast<float*>(keys), nullptr, nullptr,
       nullptr, 1, lcand, lbound, lp.kloc);
   return hipGetLastError();
 }
 }  // namespace
 
-LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4) {
+LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4, bool cand) {
   LocalPlan lp;
   if (B < 1 || n_cap < 1 || k < 1) return lp;
-  // The same wavefront length as the plain scan (see kLongScanWaves).
+  // The same wavefront length as the plain scan (see kLongScanWaves); a
+  // scan of candidate rows keeps 8 tiles.
   const int64_t per8 = (int64_t)kWaves * 8 * 32;
   const int64_t waves8 = ((n_cap + per8 - 1) / per8) * (int64_t)B * kWaves;
-  lp.tpw = (!qfp4 && waves8 >= kLongScanWaves) ? 16 : 8;
+  lp.tpw = (!qfp4 && !cand && waves8 >= kLongScanWaves) ? 16 : 8;
   const int64_t epb = (int64_t)kWaves * lp.tpw * 32;      // rows per workgroup
   const int64_t n_wg = (n_cap + epb - 1) / epb;
   // Groups of one wavefront's rows while every group can keep 20 pairs (a
@@ -543,20 +568,29 @@ hipError_t launch_indexer_local(const uint8_t* k_codes,
                                 const int32_t* n_entries,
                                 const IndexQuery& iq, int B, uint32_t* keys,
                                 const LocalPlan& lp, uint2* lcand,
-                                uint32_t* lbound, hipStream_t s) {
+                                uint32_t* lbound, hipStream_t s,
+                                const int32_t* cand, int64_t n_rows) {
   if (B == 0) return hipSuccess;
   if (!lp.ok) return hipErrorInvalidValue;
   const bool q4 = iq.q_scales != nullptr;
-#define CSA2_LOCAL(Q, T, L)                                                  \
-  if (q4 == Q && lp.tpw == T && (lp.per_wave ? 1 : 2) == L)                  \
-    return launch_local<Q, T, L>(B, s, k_codes, k_scales, n_cap, n_entries,  \
-                                 iq, keys, lp, lcand, lbound);
-  CSA2_LOCAL(true, 8, 1)
-  CSA2_LOCAL(true, 8, 2)
-  CSA2_LOCAL(false, 8, 1)
-  CSA2_LOCAL(false, 8, 2)
-  CSA2_LOCAL(false, 16, 1)
-  CSA2_LOCAL(false, 16, 2)
+  const bool c = cand != nullptr;
+  if (!c) n_rows = n_cap;
+  if (n_rows < 1) return hipErrorInvalidValue;
+#define CSA2_LOCAL(Q, T, L, C)                                               \
+  if (q4 == Q && lp.tpw == T && (lp.per_wave ? 1 : 2) == L && c == C)        \
+    return launch_local<Q, T, L, C>(B, s, k_codes, k_scales, n_cap,          \
+                                    n_entries, cand, n_rows, iq, keys, lp,    \
+                                    lcand, lbound);
+  CSA2_LOCAL(true, 8, 1, false)
+  CSA2_LOCAL(true, 8, 2, false)
+  CSA2_LOCAL(false, 8, 1, false)
+  CSA2_LOCAL(false, 8, 2, false)
+  CSA2_LOCAL(false, 16, 1, false)
+  CSA2_LOCAL(false, 16, 2, false)
+  CSA2_LOCAL(true, 8, 1, true)
+  CSA2_LOCAL(true, 8, 2, true)
+  CSA2_LOCAL(false, 8, 1, true)
+  CSA2_LOCAL(false, 8, 2, true)
 #undef CSA2_LOCAL
   return hipErrorInvalidValue;
 }

@@ -52,6 +52,9 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
 // what it left out into lbound[B][n_wg] (n_wg = groups per row).
 // local_plan() picks the wavefront length, the group and kloc (2k pairs in
 // all, at most kLocalMaxCands); ok is false when the row is too long.
+// With candidate ids (cand [B][n_rows], as launch_indexer's) the rows are
+// the candidates, the keys go to keys[B][round32(n_rows)] and the pairs
+// carry the entry ids.
 constexpr int kLocalMaxCands = 4096;
 struct LocalPlan {
   bool ok = false;
@@ -60,13 +63,16 @@ struct LocalPlan {
   int n_wg = 0;
   int kloc = 0;
 };
-LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4);
+LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4,
+                     bool cand = false);
 hipError_t launch_indexer_local(const uint8_t* k_codes,
                                 const uint8_t* k_scales, int64_t n_cap,
                                 const int32_t* n_entries,
                                 const IndexQuery& iq, int B, uint32_t* keys,
                                 const LocalPlan& lp, uint2* lcand,
-                                uint32_t* lbound, hipStream_t s);
+                                uint32_t* lbound, hipStream_t s,
+                                const int32_t* cand = nullptr,
+                                int64_t n_rows = 0);
 
 // topk.hip
 // Exact per-row top-k (see topk.hip) of float scores (keys == false) or of
@@ -143,6 +149,10 @@ struct FusedSelect {
   int64_t ld;
   const int32_t* n_entries;    // [B]
   int32_t* topk_out;           // [B][k]
+  // Candidate rows (a pool): the keys row covers ids[B][n_ids] and the
+  // fallback streams those rows with their entry ids (n_entries unused).
+  const int32_t* ids = nullptr;
+  int64_t n_ids = 0;
 };
 hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        int64_t n_cap, const int32_t* topk, int k,

@@ -167,3 +167,43 @@ def _check_group_one(wl, st, b, n, n_keep, k, res):
         assert ok, (b, layer, msg_l)
         _attn_ok(wl, st, b, layer, ids_l[0], out_l[0])
     print(b, msg, flush=True)
+
+
+def test_reindex_crowded_pool_fallback():
+    """A pool whose first candidate group holds 200 copies of the row's best
+    indexer key (far more than a group keeps): the pool's candidates cannot
+    hold the top k, so the exact fallback over the pool decides, with the
+    pool's entry ids; the copies tie and the lower ids win.  Pool positions
+    are every other entry from 1 (ascending), with a tail of -1 padding."""
+    wl = dataclasses.replace(WORKLOADS[2], cid=305, B=2, n=30000)
+    st = workload.build(wl, DEV)
+    k, n_pool = 512, 12000
+    pool = np.full((wl.B, n_pool), -1, np.int32)
+    pool[:, :11000] = np.arange(11000, dtype=np.int32) * 2 + 1
+    ids_planted = pool[0, 40:240]
+    for b in range(wl.B):
+        ic = st.idx_codes[b].cpu().numpy()
+        isc = st.idx_scales[b].cpu().numpy()
+        sc = O.indexer_scores(bf16_bits(st.q_idx[b]), st.w[b].cpu().numpy(),
+                              O.unpack_idx(ic[pool[b, :11000]],
+                                           isc[pool[b, :11000]]))
+        best = int(pool[b, int(np.argmax(sc))])
+        rows = torch.from_numpy(ids_planted.astype(np.int64)).to(DEV)
+        st.idx_codes[b, rows] = st.idx_codes[b, best].clone()
+        st.idx_scales[b, rows] = st.idx_scales[b, best].clone()
+    pool_t = torch.from_numpy(pool).to(DEV)
+    out, ids = csa2.reindex_decode(st.cache, pool_t, st.q_idx, st.w, st.q[0],
+                                   st.swa[0], st.n_swa, k, st.scale)
+    torch.cuda.synchronize()
+    out, ids = out.float().cpu().numpy(), ids.cpu().numpy()
+    for b in range(wl.B):
+        gv = pool[b, :11000]
+        ic = st.idx_codes[b].cpu().numpy()
+        isc = st.idx_scales[b].cpu().numpy()
+        fine = O.indexer_scores(bf16_bits(st.q_idx[b]), st.w[b].cpu().numpy(),
+                                O.unpack_idx(ic[gv], isc[gv]))
+        ok, msg = topk_set_ok(ids[b], fine, k, ids=gv)
+        assert ok, (b, msg)
+        assert set(ids_planted.tolist()) <= set(ids[b].tolist()), b
+        e = _attn_ok(wl, st, b, 0, ids[b], out[b])
+        print(b, msg, f"rel-L2 {e:.2e}", flush=True)
