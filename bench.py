@@ -250,18 +250,14 @@ def decode_kernels(wl):
     """The possible kernel sequences of one decode call, in launch order
     (top-k selections in one workgroup per row, or in two stages)."""
     if wl.pool:
-        # The pool scan keeps local candidates and the attention selects
-        # from them (one sequence per block selection variant), or, for
-        # pools the fused selection cannot take, a separate selection.
-        return [["block_scan", "block_topk", "pool_scan_local",
+        # Hierarchical: the block scan keeps local candidates and one
+        # workgroup per sequence selects the blocks (the pool), the pool
+        # scan keeps local candidates and the attention selects from them.
+        # (Shapes whose candidates do not fit take separate selections.)
+        return [["block_scan_local", "block_select", "pool_scan_local",
                  "attention_fused_select", "split_merge"],
-                ["block_scan", "block_chunk_select", "block_union_select",
-                 "pool_scan_local", "attention_fused_select", "split_merge"],
-                ["block_scan", "block_topk", "pool_scan", "pool_topk",
-                 "attention", "split_merge"],
-                ["block_scan", "block_chunk_select", "block_union_select",
-                 "pool_scan", "pool_chunk_select", "pool_union_select",
-                 "attention", "split_merge"]]
+                ["block_scan_local", "block_select", "pool_scan_local",
+                 "attention_fused_select"]]
     return [["scan_local_topk", "attention_fused_select", "split_merge"],
             ["scan_local_topk", "attention_fused_select"]]
 
@@ -307,7 +303,7 @@ def run_workload(args, wl, headline):
         r = kernel_times(lambda i: reuse(i, 1), M,
                          [["attention", "split_merge"], ["attention"]])
         kern.update({f"reuse_{n}": v for n, v in r.items()})
-    scan_name = "block_scan" if wl.pool else "scan_local_topk"
+    scan_name = "block_scan_local" if wl.pool else "scan_local_topk"
     t_scan = kern[scan_name]
     achieved = scan_bytes(wl) / t_scan / 1e9
     layers = 1 + wl.reuse_layers
@@ -330,8 +326,8 @@ def run_workload(args, wl, headline):
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic_from_profile() if wl.cid == HEADLINE else None,
-            "kernel": (("indexer_kernel<1, true, false, false, false, 8> "
-                        "(bf16 block-key scan)") if wl.pool else
+            "kernel": (("indexer_kernel<1, true, false, false, false, 8, 2> "
+                        "(bf16 block-key scan + local top-k)") if wl.pool else
                        f"indexer_kernel<0, true, false, false, false, T, L> "
                        f"(MXFP4 scan + local top-k)"),
             "algorithmic_bytes_per_launch": scan_bytes(wl),
@@ -454,7 +450,13 @@ def run_variants(args, wl, st, reps, planes, R, out, ids, ws):
     # caches of its own (the timed steps' caches stay as they are).
     cm, cd = wl.m, 7168
     c_h = inputs.hidden_states(900, wl.B, cm, cd, dev)
-    c_w = inputs.compressor_weights(900, cd, dev)
+    # The layer's weights are read from HBM at every step of a real decode
+    # (the other layers' weights pass in between), so they are rotated over
+    # copies like the caches: each copy is reused after >= 512 MB.
+    c_w0 = inputs.compressor_weights(900, cd, dev)
+    wbytes = sum(t.numel() * 2 for t in c_w0)
+    RW = math.ceil(2 * 256e6 / wbytes) + 1
+    c_ws_rot = [c_w0] + [tuple(t.clone() for t in c_w0) for _ in range(RW - 1)]
     c_rows = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
     c_slot = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
     c_bufs = [torch.zeros(sh, dtype=torch.uint8, device=dev)
@@ -464,14 +466,15 @@ def run_variants(args, wl, st, reps, planes, R, out, ids, ws):
         csa2.OP_COMPRESS, wl.B, cm, cd, None), dev)
 
     def step_compress(i):
-        csa2.compress_append(c_h, *c_w, c_rows, *c_bufs[:4], swa=c_bufs[4],
-                             swa_slot=c_slot, ws=c_ws)
+        csa2.compress_append(c_h, *c_ws_rot[i % RW], c_rows, *c_bufs[:4],
+                             swa=c_bufs[4], swa_slot=c_slot, ws=c_ws)
 
     s, _ = graph_time(step_compress, K, W, c_bufs)
     cbytes = (2 * 512 * cd * 2 + 128 * 512 * 2 + wl.B * cm * cd * 2
               + wl.B * (288 + 68 + cm * 512))
     v["compress_append"] = {
         "value": wl.B / s, "ms_per_step": s * 1e3, "m": cm, "d": cd,
+        "weight_replicas": RW,
         "algorithmic_bytes": cbytes, "achieved_GBs": cbytes / s / 1e9,
         "what": "csa2_compress_append: one new entry per sequence (C, Z "
                 "projections, softmax pooling, K^I, FP4/MXFP4/E4M3 append)"}

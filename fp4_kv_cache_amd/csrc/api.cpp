@@ -72,7 +72,8 @@ struct DecodeLayout {
   int kb = 0;
   size_t off_scores = 0, off_tmax = 0, off_bscores = 0,
          off_pool = 0, off_pscores = 0, off_lcand = 0, off_lbound = 0,
-         off_split = 0, off_attn = 0, total = 0;
+         off_blcand = 0, off_blbound = 0, off_split = 0, off_attn = 0,
+         total = 0;
 };
 
 inline size_t tiles_of(int64_t rows) { return (size_t)((rows + 31) / 32); }
@@ -122,6 +123,11 @@ DecodeLayout decode_layout(int B, int64_t n_cap, int k,
     off += align256((size_t)B * csa2::kLocalMaxCands * 8);
     L.off_lbound = off;
     off += align256((size_t)B * (csa2::kLocalMaxCands / 8) * 4);
+    // Local candidates of the block scan for the block selection.
+    L.off_blcand = off;
+    off += align256((size_t)B * csa2::kCandTopkMax * 8);
+    L.off_blbound = off;
+    off += align256((size_t)B * (csa2::kCandTopkMax / 8) * 4);
   }
   L.off_attn = off;
   off += align256(csa2::attn_workspace(B, k));
@@ -642,17 +648,40 @@ csa2_status decode_impl(const csa2_cache* kv, const csa2::IndexQuery& iq,
     float* pscores = reinterpret_cast<float*>(base + L.off_pscores);
     // Blocks of `block` entries: sequence b has ceil(n_entries[b] / block)
     // of them, which the scan and the select work out themselves.
-    e = csa2::launch_indexer(CSA2_KEYS_BF16, kv->block_keys, nullptr, L.nb,
-                             kv->n_entries, nullptr, L.nb, iq, B, bscores, s,
-                             tmax, nullptr, nullptr, pool->block);
-    if (e != hipSuccess) return hip_fail(e, "block indexer launch");
-    CSA2_MARK(lm);
-    e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb,
-                                kv->n_entries, nullptr, B, L.kb, pool->block,
-                                kv->n_entries, pool_ids, s, pool->block,
-                                base + L.off_split);
-    if (e != hipSuccess) return hip_fail(e, "block top-k launch");
-    CSA2_MARK(lm);
+    const csa2::LocalPlan bp =
+        csa2::local_plan(B, L.nb, L.kb, iq.q_scales != nullptr, false,
+                         csa2::kCandTopkMax);
+    if (bp.ok && bp.tpw == 8) {
+      // The block scan keeps local candidates; one workgroup per sequence
+      // then selects the blocks from them and expands the pool.
+      uint32_t* bkeys = reinterpret_cast<uint32_t*>(bscores);
+      uint2* blcand = reinterpret_cast<uint2*>(base + L.off_blcand);
+      uint32_t* blbound = reinterpret_cast<uint32_t*>(base + L.off_blbound);
+      e = csa2::launch_indexer_local(
+          reinterpret_cast<const uint8_t*>(kv->block_keys), nullptr, L.nb,
+          kv->n_entries, iq, B, bkeys, bp, blcand, blbound, s, nullptr, 0,
+          CSA2_KEYS_BF16, pool->block);
+      if (e != hipSuccess) return hip_fail(e, "block indexer launch");
+      CSA2_MARK(lm);
+      e = csa2::launch_cand_topk(blcand, blbound, bp.n_wg, bp.kloc, bkeys,
+                                 round32(L.nb), L.nb, kv->n_entries,
+                                 pool->block, B, L.kb, pool->block,
+                                 kv->n_entries, pool_ids, s);
+      if (e != hipSuccess) return hip_fail(e, "block top-k launch");
+      CSA2_MARK(lm);
+    } else {
+      e = csa2::launch_indexer(CSA2_KEYS_BF16, kv->block_keys, nullptr, L.nb,
+                               kv->n_entries, nullptr, L.nb, iq, B, bscores,
+                               s, tmax, nullptr, nullptr, pool->block);
+      if (e != hipSuccess) return hip_fail(e, "block indexer launch");
+      CSA2_MARK(lm);
+      e = csa2::launch_row_select(bscores, tmax, true, round32(L.nb), L.nb,
+                                  kv->n_entries, nullptr, B, L.kb,
+                                  pool->block, kv->n_entries, pool_ids, s,
+                                  pool->block, base + L.off_split);
+      if (e != hipSuccess) return hip_fail(e, "block top-k launch");
+      CSA2_MARK(lm);
+    }
     const csa2::LocalPlan pp = csa2::local_plan(B, L.n_cand, k,
                                                 iq.q_scales != nullptr, true);
     if (pp.ok) {

@@ -138,6 +138,7 @@ struct AttnArgs {
   const int32_t* n_entries;
   const int32_t* fb_ids;   // [B][fb_n] entry ids of the key rows, or null
   int64_t fb_n;
+  int n_div;               // entries per key row of the fallback (blocks)
   int32_t* topk_out;       // [B][k], written by each sequence's split 0
   AttnEpilogue epi;        // sink and de-rotation (final output only)
 };
@@ -147,14 +148,16 @@ static_assert(offsetof(AttnArgs, lbound) + sizeof(void*) <= 64,
 // Shared memory of the fused selection (512 threads), overlaid on the
 // attention's tile buffers, which are not in use yet: the candidate pass,
 // and over it the exact fallback's streaming store.
-struct CandSmem {
+template <int NC>
+struct CandSmemT {
   int32_t hist[4][256];             // one histogram per narrowing pass
   uint32_t red[4][8];
-  uint2 stage[4096];                // the candidates, in their global order
+  uint2 stage[NC];                  // the candidates, in their global order
 };
-struct FselSmem {
+template <int NC>
+struct FselSmemT {
   union {
-    CandSmem cand;
+    CandSmemT<NC> cand;
     struct {
       uint32_t key[512 * kStreamPer];
       int32_t id[512 * kStreamPer];
@@ -162,6 +165,7 @@ struct FselSmem {
     };
   };
 };
+using FselSmem = FselSmemT<4096>;     // the attention kernel's
 constexpr int kMaxK = 2048;
 
 // Raw gather registers for the 8 slots this lane dequantises in one tile.
@@ -226,11 +230,13 @@ struct FallbackSrc {
 // All 512 threads take part; ends with a barrier.  Only LDS is written here:
 // a global store before that barrier would make every wavefront wait at it
 // for the store to complete, so the ids go to topk_out at the kernel's end.
-template <int PER>
+template <int PER, typename Smem>
 __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
-                                             int32_t* sel_ids, FselSmem& fs) {
+                                             int32_t* sel_ids, Smem& fs) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  CandSmem& cs = fs.cand;
+  auto& cs = fs.cand;
+  static_assert(PER * 512 <= (int)(sizeof(cs.stage) / sizeof(uint2)),
+                "the candidate stage holds every pair");
   if (tid < 256) reinterpret_cast<int4*>(&cs.hist[0][0])[tid] = make_int4(0, 0, 0, 0);
   const int C = p.n_wg * p.kloc;
   const uint2* cr = p.lcand + (int64_t)b * C;
@@ -382,8 +388,10 @@ __device__ __forceinline__ void fused_select(const AttnArgs& p, int b,
     __syncthreads();
     int64_t len = p.fb_n;
     if (p.fb_ids == nullptr) {
+      // Visible rows: n_entries[b], or ceil(n_entries[b] / n_div) blocks.
       const int32_t ne = p.n_entries[b];
-      len = ne <= 0 ? 0 : ((int64_t)ne < p.n_cap ? ne : p.n_cap);
+      len = ne <= 0 ? 0 : ((int64_t)ne + p.n_div - 1) / p.n_div;
+      len = len < p.n_cap ? len : p.n_cap;
     }
     const FallbackSrc src{p.keys + (int64_t)b * p.ld,
                           p.fb_ids ? p.fb_ids + (int64_t)b * p.fb_n : nullptr};
@@ -977,6 +985,47 @@ hipError_t launch_combine(const uint16_t* part_o, const float* part_ml,
   }
 }
 
+// Exact top-k of local candidates for a selection that no attention kernel
+// follows: the blocks of the hierarchical pool.  One workgroup of 512
+// threads per sequence runs the fused selection (its exact fallback streams
+// the sequence's whole key row) and writes each chosen id expanded by
+// `block` -- positions id*block .. id*block+block-1, those at or past
+// limit[b] as -1 -- ascending, -1 padded to k*block.
+using CandTopkSmem = FselSmemT<kCandTopkMax>;
+constexpr int kCandTopkSmemBytes = (int)sizeof(CandTopkSmem) + (kMaxK + 64) * 4;
+
+template <int CPER>
+__global__ __launch_bounds__(512) void cand_topk_kernel(AttnArgs p, int block,
+                                                        const int32_t* limit,
+                                                        int32_t* out) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  int32_t* sel = reinterpret_cast<int32_t*>(smem_raw + sizeof(CandTopkSmem));
+  const int b = blockIdx.x;
+  fused_select<CPER>(p, b, sel, *reinterpret_cast<CandTopkSmem*>(smem_raw));
+  const int64_t lim = limit ? (int64_t)limit[b] : INT64_MAX;
+  const int64_t n = (int64_t)p.k * block;
+  int32_t* o = out + (int64_t)b * n;
+  for (int64_t q = threadIdx.x; q < n; q += 512) {
+    const int32_t id = sel[q / block];
+    const int64_t pos = (int64_t)id * block + q % block;
+    o[q] = (id >= 0 && pos < lim) ? (int32_t)pos : -1;
+  }
+}
+
+template <int CPER>
+hipError_t launch_cand_topk_kernel(const AttnArgs& a, int block,
+                                   const int32_t* limit, int32_t* out,
+                                   hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(
+      reinterpret_cast<const void*>(cand_topk_kernel<CPER>),
+      kCandTopkSmemBytes, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((cand_topk_kernel<CPER>), dim3(a.B), dim3(512),
+                     kCandTopkSmemBytes, s, a, block, limit, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int attn_splits(int B, int k) {
@@ -1037,6 +1086,7 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   a.out = out;
   a.B = B;
   a.n_tiles = (k + kWindow + kTile - 1) / kTile;
+  a.n_div = 1;
   a.epi = epi;
   a.splits = attn_splits(B, k);
   a.tiles_per_split = (a.n_tiles + a.splits - 1) / a.splits;
@@ -1075,6 +1125,36 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   e = launch_combine<2>(a.part_o, a.part_ml, a.splits, B, out, epi, s);
   if (e == hipSuccess && marks) e = marks->mark();
   return e;
+}
+
+hipError_t launch_cand_topk(const uint2* lcand, const uint32_t* lbound,
+                            int n_wg, int kloc, const uint32_t* keys,
+                            int64_t ld, int64_t n_rows,
+                            const int32_t* n_entries, int n_div, int B, int k,
+                            int block, const int32_t* limit, int32_t* out,
+                            hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int C = n_wg * kloc;
+  if (k < 1 || k > kMaxK || C < 1 || C > kCandTopkMax || n_div < 1 ||
+      block < 1)
+    return hipErrorInvalidValue;
+  AttnArgs a{};
+  a.B = B;
+  a.k = k;
+  a.n_wg = n_wg;
+  a.kloc = kloc;
+  a.lcand = lcand;
+  a.lbound = lbound;
+  a.keys = keys;
+  a.ld = ld;
+  a.n_cap = n_rows;
+  a.n_entries = n_entries;
+  a.n_div = n_div;
+  if (C <= 1024) return launch_cand_topk_kernel<2>(a, block, limit, out, s);
+  if (C <= 2048) return launch_cand_topk_kernel<4>(a, block, limit, out, s);
+  if (C <= 4096) return launch_cand_topk_kernel<8>(a, block, limit, out, s);
+  if (C <= 5120) return launch_cand_topk_kernel<10>(a, block, limit, out, s);
+  return launch_cand_topk_kernel<16>(a, block, limit, out, s);
 }
 
 }  // namespace csa2

@@ -189,8 +189,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   constexpr bool kScaledOp = QFP4 && KEYFMT == 0;
   constexpr int D = Depth<KEYFMT, kScaledOp>::value;
   constexpr int T = TPW;
-  static_assert(LOCAL == 0 || (KEYS && !BLK && KEYFMT == 0),
-                "local candidates: MXFP4 keys, selection keys");
+  static_assert(LOCAL == 0 || (KEYS && !BLK && (KEYFMT == 0 || !CAND)),
+                "local candidates: selection keys, no block maxima");
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -512,25 +512,27 @@ void launch_q(int B, hipStream_t s, const void* k_codes,
                                     n_entries, cand, n_rows, iq, scores, tmax,
                                     bmax, btmax, n_div);
 }
-template <bool QFP4, int T, int LOCAL, bool CAND>
+template <int KF, bool QFP4, int T, int LOCAL, bool CAND>
 hipError_t launch_local(int B, hipStream_t s, const void* k_codes,
                         const uint8_t* k_scales, int64_t n_cap,
                         const int32_t* n_entries, const int32_t* cand,
                         int64_t n_rows, const IndexQuery& iq, uint32_t* keys,
-                        const LocalPlan& lp, uint2* lcand, uint32_t* lbound) {
+                        const LocalPlan& lp, uint2* lcand, uint32_t* lbound,
+                        int n_div) {
   const int smem = (kWaves * T * 32 + kWaves * 256 + 16) * 4;
   const int64_t epb = (int64_t)kWaves * T * 32;
   hipLaunchKernelGGL(
-      (indexer_kernel<0, true, QFP4, false, CAND, T, LOCAL>),
+      (indexer_kernel<KF, true, QFP4, false, CAND, T, LOCAL>),
       dim3((unsigned)((n_rows + epb - 1) / epb), (unsigned)B), dim3(256),
       smem, s, k_codes, k_scales, n_cap, n_entries, cand, n_rows, iq.q,
       iq.q_scales, iq.w, reinterpret_cast<float*>(keys), nullptr, nullptr,
-      nullptr, 1, lcand, lbound, lp.kloc);
+      nullptr, n_div, lcand, lbound, lp.kloc);
   return hipGetLastError();
 }
 }  // namespace
 
-LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4, bool cand) {
+LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4, bool cand,
+                     int max_cands) {
   LocalPlan lp;
   if (B < 1 || n_cap < 1 || k < 1) return lp;
   // The same wavefront length as the plain scan (see kLongScanWaves); a
@@ -543,15 +545,17 @@ LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4, bool cand) {
   // Groups of one wavefront's rows while every group can keep 20 pairs (a
   // group expects k * rows / n of the row's winners: 4 for 512 of 32,768
   // in 256 rows, so 20 are exceeded with probability ~1e-9 on independent
-  // scores), else groups of a workgroup's rows keeping 16 or more.
+  // scores), else groups of a workgroup's rows keeping 16 or more (40 when
+  // there is room: 2,048 of 131,072 blocks in 1,024 rows expect 16, and
+  // exceed 40 with probability ~3e-8).
   for (int per_wave = 1; per_wave >= 0; --per_wave) {
     const int64_t groups = per_wave ? n_wg * kWaves : n_wg;
     const int64_t rows = per_wave ? epb / kWaves : epb;
     const int64_t kmin = per_wave ? 20 : 16;
-    int64_t kl = std::max<int64_t>(per_wave ? 20 : 64,
+    int64_t kl = std::max<int64_t>(per_wave ? 20 : 40,
                                    (2 * (int64_t)k + groups - 1) / groups);
     kl = std::min<int64_t>(kl, rows);
-    kl = std::min<int64_t>(kl, kLocalMaxCands / groups);
+    kl = std::min<int64_t>(kl, max_cands / groups);
     if (kl < std::min<int64_t>(kmin, rows) || kl * groups < 2 * (int64_t)k)
       continue;
     lp.ok = true;
@@ -569,18 +573,34 @@ hipError_t launch_indexer_local(const uint8_t* k_codes,
                                 const IndexQuery& iq, int B, uint32_t* keys,
                                 const LocalPlan& lp, uint2* lcand,
                                 uint32_t* lbound, hipStream_t s,
-                                const int32_t* cand, int64_t n_rows) {
+                                const int32_t* cand, int64_t n_rows,
+                                int keyfmt, int n_div) {
   if (B == 0) return hipSuccess;
   if (!lp.ok) return hipErrorInvalidValue;
   const bool q4 = iq.q_scales != nullptr;
   const bool c = cand != nullptr;
   if (!c) n_rows = n_cap;
   if (n_rows < 1) return hipErrorInvalidValue;
+  if (keyfmt == 1) {
+    // bf16 block keys: rows are blocks of n_div entries, 8 tiles.
+    if (c || lp.tpw != 8) return hipErrorInvalidValue;
+#define CSA2_LOCAL_B(Q, L)                                                   \
+    if (q4 == Q && (lp.per_wave ? 1 : 2) == L)                               \
+      return launch_local<1, Q, 8, L, false>(B, s, k_codes, nullptr, n_cap,  \
+                                             n_entries, nullptr, n_rows, iq,  \
+                                             keys, lp, lcand, lbound, n_div);
+    CSA2_LOCAL_B(false, 1)
+    CSA2_LOCAL_B(false, 2)
+    CSA2_LOCAL_B(true, 1)
+    CSA2_LOCAL_B(true, 2)
+#undef CSA2_LOCAL_B
+    return hipErrorInvalidValue;
+  }
 #define CSA2_LOCAL(Q, T, L, C)                                               \
   if (q4 == Q && lp.tpw == T && (lp.per_wave ? 1 : 2) == L && c == C)        \
-    return launch_local<Q, T, L, C>(B, s, k_codes, k_scales, n_cap,          \
-                                    n_entries, cand, n_rows, iq, keys, lp,    \
-                                    lcand, lbound);
+    return launch_local<0, Q, T, L, C>(B, s, k_codes, k_scales, n_cap,       \
+                                       n_entries, cand, n_rows, iq, keys, lp, \
+                                       lcand, lbound, 1);
   CSA2_LOCAL(true, 8, 1, false)
   CSA2_LOCAL(true, 8, 2, false)
   CSA2_LOCAL(false, 8, 1, false)

@@ -54,7 +54,9 @@ hipError_t launch_indexer(int keyfmt, const void* k_codes,
 // all, at most kLocalMaxCands); ok is false when the row is too long.
 // With candidate ids (cand [B][n_rows], as launch_indexer's) the rows are
 // the candidates, the keys go to keys[B][round32(n_rows)] and the pairs
-// carry the entry ids.
+// carry the entry ids.  keyfmt 1 (bf16): the rows are bf16 block
+// keys (k_codes; blocks of n_div entries, so ceil(n_entries / n_div) rows
+// are valid), without candidate ids.
 constexpr int kLocalMaxCands = 4096;
 struct LocalPlan {
   bool ok = false;
@@ -64,7 +66,7 @@ struct LocalPlan {
   int kloc = 0;
 };
 LocalPlan local_plan(int B, int64_t n_cap, int k, bool qfp4,
-                     bool cand = false);
+                     bool cand = false, int max_cands = kLocalMaxCands);
 hipError_t launch_indexer_local(const uint8_t* k_codes,
                                 const uint8_t* k_scales, int64_t n_cap,
                                 const int32_t* n_entries,
@@ -72,7 +74,8 @@ hipError_t launch_indexer_local(const uint8_t* k_codes,
                                 const LocalPlan& lp, uint2* lcand,
                                 uint32_t* lbound, hipStream_t s,
                                 const int32_t* cand = nullptr,
-                                int64_t n_rows = 0);
+                                int64_t n_rows = 0,
+                                int keyfmt = 0, int n_div = 1);
 
 // topk.hip
 // Exact per-row top-k (see topk.hip) of float scores (keys == false) or of
@@ -154,6 +157,19 @@ struct FusedSelect {
   const int32_t* ids = nullptr;
   int64_t n_ids = 0;
 };
+constexpr int kCandTopkMax = 8192;
+// Exact top-k of the local candidates of launch_indexer_local (at most
+// kCandTopkMax pairs per sequence; the fused selection's test and
+// its exact fallback over keys[B][ld], whose first ceil(n_entries[b] /
+// n_div) rows, at most n_rows, are visible), each chosen id expanded by
+// `block` into out[B][k * block] (positions at or past limit[b] -> -1;
+// ascending, -1 padded).  One workgroup per sequence.
+hipError_t launch_cand_topk(const uint2* lcand, const uint32_t* lbound,
+                            int n_wg, int kloc, const uint32_t* keys,
+                            int64_t ld, int64_t n_rows,
+                            const int32_t* n_entries, int n_div, int B, int k,
+                            int block, const int32_t* limit, int32_t* out,
+                            hipStream_t s);
 hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
                        int64_t n_cap, const int32_t* topk, int k,
                        const uint16_t* q, const uint8_t* swa,
