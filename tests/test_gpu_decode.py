@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from oracle import csa2 as O
+from oracle import formats as F
 from fp4_kv_cache_amd import csa2, inputs, workload
 from fp4_kv_cache_amd.inputs import WORKLOADS
 from _util import REL_L2_TOL, bf16_bits, rel_l2, topk_set_ok
@@ -130,3 +131,40 @@ def test_ragged_n_entries_in_one_batch():
         assert np.all(ids[b][ids[b] >= 0] < ne[b])
         if np.array_equal(ids[b], sel):
             assert rel_l2(out[b], ref) <= REL_L2_TOL
+
+
+def test_pool_crowded_block_group_fallback():
+    """The hierarchical decode with 300 copies of a sequence's best block
+    key planted in blocks 200 .. 499 (far more than the block scan's
+    candidate group of those rows keeps): the block candidates cannot hold
+    the top 2,048 blocks, so the block selection's exact fallback decides.
+    The oracle runs the pages' hierarchy on the same (planted) block keys."""
+    wl = dataclasses.replace(WORKLOADS[4], cid=106, B=2, n=8 * 16384,
+                             pool=(2048, 8))
+    st = workload.build(wl, DEV)
+    planted = np.arange(200, 500)
+    for b in range(wl.B):
+        bk = st.block_keys[b].cpu().view(torch.int16).numpy().view(np.uint16)
+        qi = bf16_bits(st.q_idx[b])
+        bs = O.indexer_scores(qi, st.w[b].cpu().numpy(),
+                              F.bf16_bits_to_f64(bk[:16384]))
+        best = int(np.argmax(bs))
+        rows = torch.from_numpy(planted.astype(np.int64)).to(DEV)
+        st.block_keys[b, rows] = st.block_keys[b, best].clone()
+    out, ids, _ = _run(st)
+    for b in range(wl.B):
+        mc, ms, ic, isc = _oracle_caches(wl, b)
+        qi, w, q, sw = _oracle_query(wl, b)
+        bk = st.block_keys[b].cpu().view(torch.int16).numpy().view(np.uint16)
+        bk = bk[:16384]
+        sel, ref, pool, fine = O.hier_layer(
+            mc, ms, ic, isc, bk, wl.n, qi, w, q, sw, wl.n_swa, wl.k,
+            st.scale, n_keep=2048, block=8)
+        blocks = set((pool[pool >= 0] // 8).tolist())
+        assert set(planted.tolist()) <= blocks, b
+        ok, msg = topk_set_ok(ids[b], fine, wl.k, ids=pool[pool >= 0])
+        assert ok, (b, msg)
+        if np.array_equal(ids[b], sel):
+            e = rel_l2(out[b], ref)
+            assert e <= REL_L2_TOL, (b, e)
+        print(b, msg, flush=True)
