@@ -18,9 +18,9 @@ DEV = "cuda"
 
 def _shape_for(S):
     best = None
-    for B in range(1, 41):
-        for k in (16, 32, 48, 64, 96, 128, 160, 192, 256, 320, 384, 448, 512,
-                  640, 768, 1024, 1280, 1536, 2048):
+    for B in range(1, 257):
+        for k in (16, 32, 48, 64, 96, 128, 160, 192, 224, 256, 288, 320, 352,
+                  384, 448, 512, 640, 768, 1024, 1280, 1536, 2048):
             if planned_splits(B, k) == S and (best is None or
                                               B * k < best[0] * best[1]):
                 best = (B, k)

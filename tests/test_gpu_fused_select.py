@@ -110,8 +110,9 @@ def test_fused_select_crowded_group():
 
 def _split_shape(S):
     best = None
-    for B in range(1, 41):
-        for k in (64, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048):
+    for B in range(1, 257):
+        for k in (64, 96, 128, 160, 192, 224, 256, 288, 384, 512, 768, 1024,
+                  1536, 2048):
             if planned_splits(B, k) == S and (best is None or
                                               B * k < best[0] * best[1]):
                 best = (B, k)
