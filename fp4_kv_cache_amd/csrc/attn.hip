@@ -1007,13 +1007,24 @@ __global__ __launch_bounds__(512) void cand_topk_kernel(AttnArgs p, int block,
   int32_t* sel = reinterpret_cast<int32_t*>(smem_raw + sizeof(CandTopkSmem));
   const int b = blockIdx.x;
   fused_select<CPER>(p, b, sel, *reinterpret_cast<CandTopkSmem*>(smem_raw));
+  // One chosen id per thread at a time: its `block` positions are
+  // consecutive, so a block of 8 is two 16-byte stores (the rows of 32
+  // threads in a row make one contiguous run).
   const int64_t lim = limit ? (int64_t)limit[b] : INT64_MAX;
-  const int64_t n = (int64_t)p.k * block;
-  int32_t* o = out + (int64_t)b * n;
-  for (int64_t q = threadIdx.x; q < n; q += 512) {
-    const int32_t id = sel[q / block];
-    const int64_t pos = (int64_t)id * block + q % block;
-    o[q] = (id >= 0 && pos < lim) ? (int32_t)pos : -1;
+  int32_t* o = out + (int64_t)b * p.k * block;
+  for (int q = threadIdx.x; q < p.k; q += 512) {
+    const int32_t id = sel[q];
+    const int64_t base = (int64_t)id * block;
+    auto at = [&](int t) -> int32_t {
+      return (id >= 0 && base + t < lim) ? (int32_t)(base + t) : -1;
+    };
+    int32_t* dst = o + (int64_t)q * block;
+    if (block == 8) {
+      reinterpret_cast<int4*>(dst)[0] = make_int4(at(0), at(1), at(2), at(3));
+      reinterpret_cast<int4*>(dst)[1] = make_int4(at(4), at(5), at(6), at(7));
+    } else {
+      for (int t = 0; t < block; ++t) dst[t] = at(t);
+    }
   }
 }
 
@@ -1141,7 +1152,7 @@ hipError_t launch_cand_topk(const uint2* lcand, const uint32_t* lbound,
   if (B == 0) return hipSuccess;
   const int C = n_wg * kloc;
   if (k < 1 || k > kMaxK || C < 1 || C > kCandTopkMax || n_div < 1 ||
-      block < 1)
+      block < 1 || (block == 8 && reinterpret_cast<uintptr_t>(out) % 16))
     return hipErrorInvalidValue;
   AttnArgs a{};
   a.B = B;
