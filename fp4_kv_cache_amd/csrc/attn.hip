@@ -128,6 +128,7 @@ struct AttnArgs {
   const uint8_t* swa;
   float scale_log2;        // scale * log2(e)
   int n_tiles;
+  int n_main;              // tiles holding chosen entries: ceil(k / 32)
   uint16_t* out;           // final output when splits == 1
   uint16_t* part_o;        // [B][S][64][512] fp16, normalised per split
   float* part_ml;          // [B][S][64][2] (max in log2 units, sum)
@@ -544,6 +545,44 @@ __device__ __forceinline__ bool map_workgroup(int id, int B, int S, int& b,
   return b < B;
 }
 
+// A split's tiles in the order it runs them.  With given ids (no fused
+// selection) the pure window tiles (n_main .. n_tiles-1, rows that need no
+// ids) are dealt first, one to each of the first splits, and the chosen
+// entries' tiles evenly after them (any remainder to the last splits): a
+// split that starts on window rows gathers them while its first ids load,
+// which takes one memory round trip out of its prologue.  After a fused
+// selection the ids are in LDS and the splits take contiguous ranges of
+// tiles_per_split tiles.
+struct TileMap {
+  int w_cnt, wbase, S, m0, cnt;
+  __device__ __forceinline__ int phys(int t) const {
+    return t < w_cnt ? wbase + S * t : m0 + (t - w_cnt);
+  }
+};
+template <bool FSEL>
+__device__ __forceinline__ TileMap tile_map(const AttnArgs& p, int split) {
+  TileMap m;
+  const int S = p.splits;
+  m.S = S;
+  if constexpr (FSEL) {
+    m.w_cnt = 0;
+    m.wbase = 0;
+    m.m0 = split * p.tiles_per_split;
+    const int end = m.m0 + p.tiles_per_split;
+    m.cnt = (end < p.n_tiles ? end : p.n_tiles) - m.m0;
+    if (m.cnt < 0) m.cnt = 0;
+  } else {
+    const int n_win = p.n_tiles - p.n_main;
+    m.w_cnt = split < n_win ? (n_win - split + S - 1) / S : 0;
+    m.wbase = p.n_main + split;
+    const int base = p.n_main / S, extra = p.n_main % S;
+    const int first_extra = S - extra;
+    m.m0 = split * base + (split > first_extra ? split - first_extra : 0);
+    m.cnt = m.w_cnt + base + (split >= first_extra ? 1 : 0);
+  }
+  return m;
+}
+
 struct TileState {
   f32x4 acc[32];           // O^T accumulators: dims 16*blk + 4*q4 + r
   float m_run;             // exp2 reference point (log2 units)
@@ -560,14 +599,14 @@ struct TileState {
 // dequantised into LDS buffer P^1 while the math wavefronts read buffer P.
 template <int P>
 __device__ __forceinline__ void tile_produce(
-    const AttnArgs& p, const Bases& bs, const int32_t* ids, int t, int t1,
-    int quarter, int lane, int nswa, _Float16* bufs, int32_t* valid_base,
-    Raw (&raw)[2], uint32_t (&kinds)[2], int32_t& idn) {
+    const AttnArgs& p, const Bases& bs, const int32_t* ids, const TileMap& tm,
+    int t, int t1, int quarter, int lane, int nswa, _Float16* bufs,
+    int32_t* valid_base, Raw (&raw)[2], uint32_t (&kinds)[2], int32_t& idn) {
   const int tl = t1 - 1;
-  const int t3 = t + 3 < t1 ? t + 3 : tl;
+  const int t3 = tm.phys(t + 3 < t1 ? t + 3 : tl);
   const int32_t id3 = load_ids(p, ids, t3, t3, quarter, lane);
-  load_rows(p, bs, t + 2 < t1 ? t + 2 : tl, quarter, lane, nswa, idn, 0,
-            raw[P], kinds[P]);
+  load_rows(p, bs, tm.phys(t + 2 < t1 ? t + 2 : tl), quarter, lane, nswa, idn,
+            0, raw[P], kinds[P]);
   idn = id3;
   if (t + 1 < t1)
     dequant_store(raw[P ^ 1], kinds[P ^ 1], quarter, lane,
@@ -724,9 +763,9 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
   const int nswa_raw = p.n_swa[b + zero];
   const int nswa = nswa_raw < 0 ? 0 : (nswa_raw > kWindow ? kWindow : nswa_raw);
 
-  const int t0 = split * p.tiles_per_split;
-  int t1 = t0 + p.tiles_per_split;
-  if (t1 > p.n_tiles) t1 = p.n_tiles;
+  const TileMap tm = tile_map<FSEL>(p, split);
+  const int t0 = 0, t1 = tm.cnt;
+  const bool wfirst = tm.w_cnt > 0;   // the first tile is window rows
 
   // Gather pipeline (producers): while tile t runs on the matrix cores, the
   // rows of tiles t+1 and t+2 are in flight (a two-slot register ring, slot
@@ -793,10 +832,15 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
     // The rows of the first two tiles go out together (a producer holds no
     // accumulators, so nothing else wants their registers); the first is
     // dequantised into buffer 0.
-    const int32_t id01 = load_ids(p, ids, ta, tb, wave, lane);
-    idn = load_ids(p, ids, t0 + 2 < t1 ? t0 + 2 : ta, 0, wave, lane);
-    load_rows(p, bs, ta, wave, lane, nswa, id01, 0, raw[0], kinds[0]);
-    load_rows(p, bs, tb, wave, lane, nswa, id01, 8, raw[1], kinds[1]);
+    // A first tile of window rows needs no ids: its rows go out first.
+    if (wfirst)
+      load_rows(p, bs, tm.phys(ta), wave, lane, nswa, 0, 0, raw[0], kinds[0]);
+    const int32_t id01 = load_ids(p, ids, tm.phys(ta), tm.phys(tb), wave, lane);
+    idn = load_ids(p, ids, tm.phys(t0 + 2 < t1 ? t0 + 2 : ta), 0, wave, lane);
+    if (!wfirst)
+      load_rows(p, bs, tm.phys(ta), wave, lane, nswa, id01, 0, raw[0],
+                kinds[0]);
+    load_rows(p, bs, tm.phys(tb), wave, lane, nswa, id01, 8, raw[1], kinds[1]);
     if (t0 < t1) dequant_store(raw[0], kinds[0], wave, lane, bufs, valid_base);
   }
   __syncthreads();
@@ -818,11 +862,11 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
     }
   } else {
     for (int t = t0; t < t1; t += 2) {
-      tile_produce<0>(p, bs, ids, t, t1, wave, lane, nswa, bufs,
+      tile_produce<0>(p, bs, ids, tm, t, t1, wave, lane, nswa, bufs,
                       valid_base, raw, kinds, idn);
       __syncthreads();
       if (t + 1 < t1) {
-        tile_produce<1>(p, bs, ids, t + 1, t1, wave, lane, nswa, bufs,
+        tile_produce<1>(p, bs, ids, tm, t + 1, t1, wave, lane, nswa, bufs,
                         valid_base, raw, kinds, idn);
         __syncthreads();
       }
@@ -1106,6 +1150,7 @@ hipError_t launch_attn(const uint8_t* main_codes, const uint8_t* main_scales,
   a.epi = epi;
   a.splits = attn_splits(B, k);
   a.tiles_per_split = (a.n_tiles + a.splits - 1) / a.splits;
+  a.n_main = (k + kTile - 1) / kTile;
   if (a.splits > 1) {
     const size_t o = (size_t)B * a.splits * kHeads * 512 * 2;
     a.part_o = static_cast<uint16_t*>(ws);
