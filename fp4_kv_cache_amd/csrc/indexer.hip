@@ -156,6 +156,24 @@ __device__ __forceinline__ void entry_ids(const int32_t* cand, int b,
   }
 }
 
+// Selection keys of rows i0 .. i0+PER-1 of sequence b (i0 a multiple of
+// PER), as 16-byte stores into the key row, which is padded to a multiple of
+// 32 entries: rows past n_rows inside the padding take their key, 0
+// (invalid); runs past the padding are not written.
+template <int PER>
+__device__ __forceinline__ void store_keys(float* scores, int b,
+                                           int64_t n_rows, int64_t i0,
+                                           const uint32_t (&kk)[PER]) {
+  static_assert(PER % 4 == 0 && 32 % PER == 0, "whole 16-byte runs");
+  const int64_t ld32 = (n_rows + 31) & ~(int64_t)31;
+  if (i0 >= ld32) return;
+  uint4* dst = reinterpret_cast<uint4*>(
+      reinterpret_cast<uint32_t*>(scores) + (int64_t)b * ld32 + i0);
+#pragma unroll
+  for (int j = 0; j < PER; j += 4)
+    dst[j / 4] = make_uint4(kk[j], kk[j + 1], kk[j + 2], kk[j + 3]);
+}
+
 // KEYS: write selection keys (see score_key) instead of float scores, and
 // each 32-row tile's largest key to tmax[B][ceil(n_rows/32)]; with `bmax`
 // also each 8-row block's largest key to bmax[B][round32(nb)] (nb =
@@ -352,13 +370,18 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     } else {
       total[t] = -__builtin_inff();
     }
+    // Local candidates: the tile's keys go to the wavefront's stretch of
+    // LDS at once (LDS writes count apart from the loads' wait counts), so
+    // no score stays live across the loop.
+    if constexpr (LOCAL != 0)
+      if (half == 0) kl[wave * T * 32 + 32 * t + col] = score_key(total[t]);
   }
   // Stores after the loop keep the loads' wait counts static.
   static_assert(!BLK || T * 32 == 256, "a wavefront's rows are one "
                 "32-block group of the block maxima");
   uint32_t wmax = 0u;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
+  for (int t = 0; t < (LOCAL == 0 ? T : 0); ++t) {
     if (t >= nt) break;
     const int64_t i = base + 32 * t + col;
     if constexpr (KEYS) {
@@ -388,8 +411,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       if (LOCAL == 0 && lane == 0)
         tmax[(int64_t)b * ((n_rows + 31) >> 5) + ((base >> 5) + t)] = mx;
       if constexpr (BLK) wmax = max(wmax, mx);
-      if constexpr (LOCAL != 0)
-        if (half == 0) kl[wave * T * 32 + 32 * t + col] = key;
     } else {
       if (half == 0 && i < n_rows) scores[(int64_t)b * n_rows + i] = total[t];
     }
@@ -408,6 +429,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     uint32_t kk[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) kk[j] = kl[wave * T * 32 + lane * PER + j];
+    store_keys<PER>(scores, b, n_rows, base + lane * PER, kk);
     const uint32_t id0 = (uint32_t)(base + lane * PER);
     uint32_t eid[PER];
     entry_ids<CAND, PER>(cand, b, n_rows, id0, eid);
@@ -434,6 +456,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     uint32_t kk[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) kk[j] = kl[tid * PER + j];
+    store_keys<PER>(scores, b, n_rows,
+                    (int64_t)blockIdx.x * (kWaves * T * 32) + tid * PER, kk);
     const uint32_t id0 = (uint32_t)(blockIdx.x * (kWaves * T * 32) + tid * PER);
     uint32_t eid[PER];
     entry_ids<CAND, PER>(cand, b, n_rows, id0, eid);
