@@ -305,25 +305,58 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 #pragma unroll
       for (int s = 0; s < 8; ++s) qa[s] = key_operand<0>(q4, s, half);
     }
-  } else {
+  }
+  // bf16 query with local candidates (no wavefront leaves early): the
+  // workgroup reads the sequence's 8 KB query and 32 weights once,
+  // coalesced (thread i: 16-byte pieces i and i + 256), and stages them in
+  // LDS (head rows padded by 16 bytes); the first tiles' key loads are
+  // issued before the barrier, so they are in flight meanwhile.  Read per
+  // wavefront, the query was 32 KB of requests per workgroup ahead of the
+  // first key loads.
+  constexpr bool kStageQ = !QFP4 && LOCAL != 0;
+  __shared__ __align__(16) u32x4 q_lds[kStageQ ? kIdxHeads * 17 : 1];
+  __shared__ float w_lds[kStageQ ? kIdxHeads : 1];
+  u32x4 qv0, qv1;
+  float wv = 0.0f;
+  if constexpr (kStageQ) {
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(q_in) + (int64_t)b * kIdxHeads * kIdxDim);
+    qv0 = qsrc[threadIdx.x];
+    qv1 = qsrc[threadIdx.x + 256];
+    if (threadIdx.x < kIdxHeads) wv = w[b * kIdxHeads + threadIdx.x];
+  } else if constexpr (!QFP4) {
     const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
         static_cast<const uint16_t*>(q_in) +
         ((int64_t)b * kIdxHeads + col) * kIdxDim + 64 * half);
 #pragma unroll
     for (int s = 0; s < 8; ++s) qa[s] = qrow[s];
   }
-  // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
-  float wr[16];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      wr[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 * half + r];
-
   RawKey<KEYFMT> buf[D + 1];
 #pragma unroll
   for (int t = 0; t < D; ++t)
     load_key<KEYFMT, kScaledOp>(buf[t], seq_codes, seq_scales, row_of(t), half);
+  // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
+  float wr[16];
+  if constexpr (kStageQ) {
+    const int i0 = threadIdx.x, i1 = threadIdx.x + 256;
+    q_lds[(i0 >> 4) * 17 + (i0 & 15)] = qv0;
+    q_lds[(i1 >> 4) * 17 + (i1 & 15)] = qv1;
+    if (threadIdx.x < kIdxHeads) w_lds[threadIdx.x] = wv;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qa[s] = bits_to_bf8(q_lds[col * 17 + 8 * half + s]);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wr[4 * a + r] = w_lds[8 * a + 4 * half + r];
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        wr[4 * a + r] = w[b * kIdxHeads + 8 * a + 4 * half + r];
+  }
   float total[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
