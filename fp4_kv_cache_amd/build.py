@@ -27,6 +27,11 @@ FLAGS = [
     # Keep the compiler from forming packed float32 arithmetic.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # Preload each kernel's first 14 dwords of arguments into scalar
+    # registers at dispatch (the code keeps a fallback entry that loads them
+    # when the firmware does not preload): the first scalar load of the
+    # arguments otherwise misses the cache at every kernel start.
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
 ]
 
 # Per-source additions: matrix-core accumulators in ordinary VGPRs.  The

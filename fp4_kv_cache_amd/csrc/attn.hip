@@ -146,6 +146,31 @@ struct AttnArgs {
 static_assert(offsetof(AttnArgs, lbound) + sizeof(void*) <= 64,
               "the kernel's first accesses share one line");
 
+// The fields above the 64-byte mark are also passed ahead of the struct as
+// plain arguments (14 dwords): the build preloads a kernel's leading
+// scalar arguments into scalar registers at dispatch, so the kernel's
+// first steps need no argument load.  The kernel puts them back into a
+// local copy of the struct.
+#define CSA2_ATTN_HEAD_PARAMS                                                \
+  int h_B, int h_splits, int h_k, int h_n_wg, int h_kloc, int h_tps,         \
+      const uint16_t *h_q, const int32_t *h_n_swa, const uint2 *h_lcand,     \
+      const uint32_t *h_lbound
+#define CSA2_ATTN_HEAD_ARGS(a)                                               \
+  (a).B, (a).splits, (a).k, (a).n_wg, (a).kloc, (a).tiles_per_split, (a).q,  \
+      (a).n_swa, (a).lcand, (a).lbound
+#define CSA2_ATTN_HEAD_RESTORE(p, a)                                         \
+  AttnArgs p = (a);                                                          \
+  p.B = h_B;                                                                 \
+  p.splits = h_splits;                                                       \
+  p.k = h_k;                                                                 \
+  p.n_wg = h_n_wg;                                                           \
+  p.kloc = h_kloc;                                                           \
+  p.tiles_per_split = h_tps;                                                 \
+  p.q = h_q;                                                                 \
+  p.n_swa = h_n_swa;                                                         \
+  p.lcand = h_lcand;                                                         \
+  p.lbound = h_lbound
+
 // Shared memory of the fused selection (512 threads), overlaid on the
 // attention's tile buffers, which are not in use yet: the candidate pass,
 // and over it the exact fallback's streaming store.
@@ -735,7 +760,9 @@ constexpr int kUnionBytes = (kSmemBytes > kFselBytes ? kSmemBytes : kFselBytes);
 constexpr int kFusedSmemBytes = kUnionBytes + (kMaxK + 64) * 4;  // + spare
 
 template <bool FSEL, int CPER>
-__global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
+__global__ __launch_bounds__(512, 1) void attn_kernel(CSA2_ATTN_HEAD_PARAMS,
+                                                      AttnArgs args) {
+  CSA2_ATTN_HEAD_RESTORE(p, args);
   extern __shared__ __align__(16) uint8_t smem_raw[];
   _Float16* bufs = reinterpret_cast<_Float16*>(smem_raw);
   int32_t* valid_base = reinterpret_cast<int32_t*>(smem_raw + 2 * kBufElems * 2);
@@ -891,19 +918,19 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs p) {
     // partial keeps its own sum; the merge adds the sink once).  With no key
     // at all (m_run = -inf) the output is zero either way.
     float den = l_tot;
-    if (final_out && p.epi.sink != nullptr)
-      den += exp2f(p.epi.sink[head] * kLog2e - m_run);
+    if (final_out && args.epi.sink != nullptr)
+      den += exp2f(args.epi.sink[head] * kLog2e - m_run);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    if (final_out && p.epi.pos != nullptr) {
+    if (final_out && args.epi.pos != nullptr) {
       // De-rotate dims 448..511 (blocks 28..31): this lane holds dims
       // 16*blk + 4*q4 + r, pairs (r = 0, 1) and (r = 2, 3).
-      const int32_t t = p.epi.pos[b];
+      const int32_t t = args.epi.pos[b];
 #pragma unroll
       for (int blk = 28; blk < 32; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
           float c, sn;
-          rope_cs(t, p.epi.rope_w[8 * (blk - 28) + 2 * q4 + r / 2], c, sn);
+          rope_cs(t, args.epi.rope_w[8 * (blk - 28) + 2 * q4 + r / 2], c, sn);
           float x = acc[blk][r], y = acc[blk][r + 1];
           rotate_pair(x, y, c, sn);
           acc[blk][r] = x;
@@ -1044,9 +1071,12 @@ using CandTopkSmem = FselSmemT<kCandTopkMax>;
 constexpr int kCandTopkSmemBytes = (int)sizeof(CandTopkSmem) + (kMaxK + 64) * 4;
 
 template <int CPER>
-__global__ __launch_bounds__(512) void cand_topk_kernel(AttnArgs p, int block,
+__global__ __launch_bounds__(512) void cand_topk_kernel(CSA2_ATTN_HEAD_PARAMS,
+                                                        AttnArgs args,
+                                                        int block,
                                                         const int32_t* limit,
                                                         int32_t* out) {
+  CSA2_ATTN_HEAD_RESTORE(p, args);
   extern __shared__ __align__(16) uint8_t smem_raw[];
   int32_t* sel = reinterpret_cast<int32_t*>(smem_raw + sizeof(CandTopkSmem));
   const int b = blockIdx.x;
@@ -1082,7 +1112,8 @@ hipError_t launch_cand_topk_kernel(const AttnArgs& a, int block,
       kCandTopkSmemBytes, lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((cand_topk_kernel<CPER>), dim3(a.B), dim3(512),
-                     kCandTopkSmemBytes, s, a, block, limit, out);
+                     kCandTopkSmemBytes, s, CSA2_ATTN_HEAD_ARGS(a), a, block,
+                     limit, out);
   return hipGetLastError();
 }
 
@@ -1120,7 +1151,7 @@ hipError_t launch_attn_kernel(const AttnArgs& a, unsigned grid, hipStream_t s) {
       reinterpret_cast<const void*>(attn_kernel<FSEL, CPER>), bytes, lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_kernel<FSEL, CPER>), dim3(grid), dim3(512), bytes,
-                     s, a);
+                     s, CSA2_ATTN_HEAD_ARGS(a), a);
   return hipGetLastError();
 }
 }  // namespace
