@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kWaves * 64) void compress_gemm_kernel(
         float v = red[0][row][c];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) v += red[w][row][c];
-        part[((int64_t)slice * M + m0 + row) * kN + col0 + c] = v;
+        __builtin_nontemporal_store(
+            v, &part[((int64_t)slice * M + m0 + row) * kN + col0 + c]);
       }
     }
     // The next pass reuses `red` (no barrier after the last pass: one
@@ -128,8 +129,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 // of its channels and its 32 rows of W^IK (thread c: 32 weights of output
 // 32j + c/16) -- is requested at the start, so it waits for memory about
 // once.  MT: a bound on m known at compile time (the tokens' loads
-// unrolled), or 0 for a loop over tokens.
-template <int MT>
+// unrolled), or 0 for a loop over tokens; SMAX: a bound on the slice count
+// (8 up to d = 8192), so no more loads are issued than there are slices.
+template <int MT, int SMAX>
 __global__ __launch_bounds__(512) void compress_epilogue_kernel(
     const float* __restrict__ part, int M, int m, int S,
     const uint16_t* __restrict__ w_ik, const int32_t* __restrict__ rows,
@@ -156,9 +158,9 @@ __global__ __launch_bounds__(512) void compress_epilogue_kernel(
   float cv[kMaxM], zv[kMaxM];
   auto token = [&](int i) {
     const int64_t row = (int64_t)b * m + i;
-    float pc[kMaxS], pz[kMaxS];
+    float pc[SMAX], pz[SMAX];
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s) {
+    for (int s = 0; s < SMAX; ++s) {
       const int sl = s < S ? s : S - 1;
       const int64_t at = ((int64_t)sl * M + row) * kN + c;
       pc[s] = part[at];
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(512) void compress_epilogue_kernel(
     }
     float cs = 0.0f, zs = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s)
+    for (int s = 0; s < SMAX; ++s)
       if (s < S) { cs += pc[s]; zs += pz[s]; }
     cv[i] = cs;
     zv[i] = zs;
@@ -202,20 +204,23 @@ __global__ __launch_bounds__(512) void compress_epilogue_kernel(
   }
   __syncthreads();
   // K^I = C_bar W^IK: a sixteenth of output o's dot per thread (channels
-  // 32sx .. 32sx+31), then the sixteen in order.
-  float acc = 0.0f;
+  // 32sx .. 32sx+31, as four chains of eight summed in a fixed order), then
+  // the sixteen in order.
+  float ac[4];
   const float4* cb4 = reinterpret_cast<const float4*>(cbar + 32 * sx);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float4 x0 = cb4[2 * i], x1 = cb4[2 * i + 1];
     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float a = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc += bf16_bits_to_f32(wv[i][e] & 0xFFFFu) * xs[2 * e];
-      acc += bf16_bits_to_f32(wv[i][e] >> 16) * xs[2 * e + 1];
+      a += bf16_bits_to_f32(wv[i][e] & 0xFFFFu) * xs[2 * e];
+      a += bf16_bits_to_f32(wv[i][e] >> 16) * xs[2 * e + 1];
     }
+    ac[i] = a;
   }
-  kpart[c] = acc;
+  kpart[c] = (ac[0] + ac[1]) + (ac[2] + ac[3]);
   __syncthreads();
   const int64_t row = rows[b];
   const bool ok = row >= 0 && row < n_cap;   // other rows are not written
@@ -289,9 +294,12 @@ hipError_t launch_compress(const uint16_t* h, int B, int m, int d,
                      dim3(kWaves * 64), 0, s, h, M, d, w_kv, w_z, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  auto epi = m <= 2 ? compress_epilogue_kernel<2>
-             : m <= 4 ? compress_epilogue_kernel<4>
-                      : compress_epilogue_kernel<0>;
+  auto epi = S <= 8 ? (m <= 2   ? compress_epilogue_kernel<2, 8>
+                       : m <= 4 ? compress_epilogue_kernel<4, 8>
+                                : compress_epilogue_kernel<0, 8>)
+                    : (m <= 2   ? compress_epilogue_kernel<2, kMaxS>
+                       : m <= 4 ? compress_epilogue_kernel<4, kMaxS>
+                                : compress_epilogue_kernel<0, kMaxS>);
   hipLaunchKernelGGL(epi, dim3((unsigned)B, 4), dim3(512), 0, s, part, M, m, S,
                      w_ik, rows, n_cap, main_codes, main_scales, idx_codes,
                      idx_scales, swa, swa_slot, cbar_out, ki_out, c_out);

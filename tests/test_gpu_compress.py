@@ -19,8 +19,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
+# (2, 3, 9216): nine reduction slices (the epilogue's 16-slice instance);
+# (2, 6, 2048): more tokens than the unrolled epilogue instances take.
 @pytest.mark.parametrize("B,m,d", [(3, 2, 512), (5, 1, 1040), (2, 4, 7168),
-                                   (32, 2, 7168)])
+                                   (32, 2, 7168), (2, 3, 9216), (2, 6, 2048)])
 def test_compress_append(B, m, d):
     cid = 500 + m
     h = inputs.hidden_states(cid, B, m, d, DEV)
