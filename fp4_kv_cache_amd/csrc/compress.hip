@@ -43,9 +43,12 @@ __host__ __device__ constexpr int n_slices(int d) {
 // Workgroup (column tile, slice): 32 output columns over the slice's 64
 // k-steps; wavefront w takes k-steps 8w .. 8w+7 of the slice.  All of a
 // wavefront's loads are issued before its matrix ops (one memory latency
-// per pass, not one per k-step); its weight operands stay in registers
-// across the 64-row passes over the hidden rows.  k-steps past the end read
-// a clamped step and enter as zero operands.
+// per pass, not one per k-step): a scheduling barrier keeps the compiler
+// from interleaving them with the matrix ops, which left about one load in
+// flight per wavefront.  Its weight operands stay in registers across the
+// 64-row passes over the hidden rows.  k-steps past the end (only in the
+// last slice) read a clamped step and enter as zero operands, set after the
+// pass's loads are issued, since the test waits for the weights.
 __global__ __launch_bounds__(kWaves * 64) void compress_gemm_kernel(
     const uint16_t* __restrict__ h, int M, int d,
     const uint16_t* __restrict__ w_kv, const uint16_t* __restrict__ w_z,
@@ -72,9 +75,7 @@ __global__ __launch_bounds__(kWaves * 64) void compress_gemm_kernel(
 #pragma unroll
   for (int j = 0; j < kSteps; ++j)
     bw[j] = *reinterpret_cast<const bf16x8*>(wrow + kofs[j]);
-#pragma unroll
-  for (int j = 0; j < kSteps; ++j)
-    if (!kin[j]) bw[j] = bf16x8{};
+  const bool ragged = ks0 + kSteps > nks;     // wavefront-uniform
   for (int m0 = 0; m0 < M; m0 += kMChunk) {
     // Rows past M read a clamped row; their results are never stored.
     const int ra = m0 + r < M ? m0 + r : M - 1;
@@ -86,6 +87,12 @@ __global__ __launch_bounds__(kWaves * 64) void compress_gemm_kernel(
     for (int j = 0; j < kSteps; ++j) {
       a0[j] = *reinterpret_cast<const bf16x8*>(ha + kofs[j]);
       a1[j] = *reinterpret_cast<const bf16x8*>(hb + kofs[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (ragged) {
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j)
+        if (!kin[j]) bw[j] = bf16x8{};
     }
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
