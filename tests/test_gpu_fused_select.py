@@ -5,7 +5,8 @@ whole key row when the candidates cannot be shown to hold the top k.
 
 Cases: sequences whose winners are spread (the candidate path), all-equal
 scores (every group ties at its bound: fallback), one group holding far
-more winners than it keeps (fallback), rows shorter than k, the top-k ids
+more winners than it keeps (fallback), rows shorter than k, a 64-row
+batch with ragged rows and the fallback over it, the top-k ids
 written to topk_out by the same call, and every split count the attention
 plans, each sequence of the batch checked, twice in a row on the same
 workspace."""
@@ -106,6 +107,30 @@ def test_fused_select_crowded_group():
     for b in range(wl.B):
         print(b, _check(st, out, ids, b, wl.n))
         assert set(range(100, 300)) <= set(ids[b].tolist())
+
+
+def test_fused_select_full_generation_batch():
+    """A batch of 64 rows of 16,384 entries (one full generation of scan
+    workgroups on 256 CUs), ragged rows, sampled sequences against the
+    oracle; then a zero indexer query, where every group ties at its bound
+    and the exact fallback reads the key row the scan wrote."""
+    n, B = 16384, 64
+    wl = dataclasses.replace(WORKLOADS[1], cid=204, B=B, n=n)
+    st = workload.build(wl, DEV)
+    ne = np.full(B, n, dtype=np.int32)
+    ne[1], ne[2], ne[3], ne[B - 2] = n - 1000, 5000, 300, 9173
+    st.n_entries.copy_(torch.from_numpy(ne))
+    sample = sorted({0, 1, 2, 3, 5, B // 4, B // 2, 3 * B // 4, B - 2, B - 1})
+    out, ids = _decode(st)
+    for b in sample:
+        print(b, _check(st, out, ids, b, int(ne[b])))
+        assert np.all(ids[b][ids[b] >= 0] < ne[b])
+    qz = torch.zeros_like(st.q_idx)
+    out, ids = _decode(st, qz)
+    for b in sample[:4] + [B - 1]:
+        assert ids[b].tolist() == list(range(min(wl.k, int(ne[b])))) + \
+            [-1] * max(0, wl.k - int(ne[b])), b
+        _check(st, out, ids, b, int(ne[b]), q_idx=qz, exact_ids=True)
 
 
 def _split_shape(S):
