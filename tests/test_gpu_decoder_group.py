@@ -5,7 +5,7 @@ pool with their own indexer query.
 
 Top-k sets follow the gap rule (the pool by the gap of the block maxima at
 the n_keep boundary), attention is compared at rel-L2 <= 5e-3 on the GPU's
-own id set, and every Reindex layer is judged on the GPU's pool."""
+own id set, and every Reindex layer is checked on the GPU's pool."""
 import dataclasses
 
 import numpy as np

@@ -5,7 +5,7 @@ one by one against the oracle on the same drawn inputs.
 
 For a sampled sequence b the oracle packs b's indexer keys from the drawn
 latents (and must reproduce the GPU's bytes), scores every visible entry in
-float64 (or, hierarchically, the block keys and then the pool) and judges the
+float64 (or, hierarchically, the block keys and then the pool) and checks the
 GPU's top-k set by the gap rule.  The attention output is compared, at
 rel-L2 <= 5e-3, with the oracle's attention over the GPU's own id set; only
 those main rows are packed on the host, again bit-compared with the GPU's."""
@@ -35,7 +35,7 @@ def _query(wl, b, layer=0):
 
 
 def _check_pool_ids(g, bs, n, n_keep, block):
-    """Top-k judged inside the pool.  When the block scores leave no near-tie
+    """Top-k checked inside the pool.  When the block scores leave no near-tie
     at the n_keep boundary the pools must agree and the fine top-k follows
     the gap rule; otherwise every chosen position must lie in a block whose
     score is within the tolerance of the boundary or above it."""
