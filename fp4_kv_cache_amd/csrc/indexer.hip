@@ -195,12 +195,14 @@ __device__ __forceinline__ void store_keys(float* scores, int b,
 // or a workgroup's (LOCAL == 2: larger groups for long rows).
 template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false, bool CAND = false,
           int TPW = kTilesPerWave, int LOCAL = 0>
+// The arguments a wavefront needs before its first key loads come first:
+// the first 14 dwords are preloaded into scalar registers at dispatch.
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
-    int64_t n_cap, const int32_t* __restrict__ n_entries,
-    const int32_t* __restrict__ cand, int64_t n_rows,
-    const void* __restrict__ q_in, const uint8_t* __restrict__ q_scales,
-    const float* __restrict__ w, float* __restrict__ scores,
+    int64_t n_cap, const void* __restrict__ q_in,
+    const float* __restrict__ w, int64_t n_rows,
+    const int32_t* __restrict__ n_entries, const int32_t* __restrict__ cand,
+    const uint8_t* __restrict__ q_scales, float* __restrict__ scores,
     uint32_t* __restrict__ tmax, uint32_t* __restrict__ bmax,
     uint32_t* __restrict__ btmax, int n_div, uint2* __restrict__ lcand,
     uint32_t* __restrict__ lbound, int kloc) {
@@ -282,6 +284,14 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     if constexpr (CAND) return crow_v[t];
     else return r0 + 32u * t < lim ? r0 + 32u * t : 0u;
   };
+  // The first tiles' rows are bounded by the cache alone, so their loads
+  // do not wait for the sequence's entry count (their scores are masked
+  // by it like every other tile's).
+  const uint32_t lim_rows = (uint32_t)n_rows;
+  auto row_pf = [&](int t) -> uint32_t {
+    if constexpr (CAND) return crow_v[t];
+    else return r0 + 32u * t < lim_rows ? r0 + 32u * t : 0u;
+  };
   auto valid = [&](int t) -> bool {
     if constexpr (CAND) return (vmask >> t) & 1u;
     else return r0 + 32u * t < lim;
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   RawKey<KEYFMT> buf[D + 1];
 #pragma unroll
   for (int t = 0; t < D; ++t)
-    load_key<KEYFMT, kScaledOp>(buf[t], seq_codes, seq_scales, row_of(t), half);
+    load_key<KEYFMT, kScaledOp>(buf[t], seq_codes, seq_scales, row_pf(t), half);
   // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
   float wr[16];
   if constexpr (kStageQ) {
@@ -535,23 +545,23 @@ void launch_one(int B, hipStream_t s, const void* k_codes,
   if (KEYFMT == 0 && !QFP4 && !bmax && !cand && waves >= kLongScanWaves)
     hipLaunchKernelGGL((indexer_kernel<0, KEYS, false, false, false, 16>),
                        grid_for(16), dim3(256), 0, s, k_codes, k_scales,
-                       n_cap, n_entries, cand, n_rows, iq.q, iq.q_scales,
-                       iq.w, scores, tmax, bmax, btmax, n_div, nullptr,
+                       n_cap, iq.q, iq.w, n_rows, n_entries, cand,
+                       iq.q_scales, scores, tmax, bmax, btmax, n_div, nullptr,
                        nullptr, 0);
   else if (KEYS && KEYFMT == 0 && !QFP4 && bmax)
     hipLaunchKernelGGL((indexer_kernel<0, true, false, true>), grid,
-                       dim3(256), 0, s, k_codes, k_scales, n_cap, n_entries,
-                       cand, n_rows, iq.q, iq.q_scales, iq.w, scores, tmax,
+                       dim3(256), 0, s, k_codes, k_scales, n_cap, iq.q,
+                       iq.w, n_rows, n_entries, cand, iq.q_scales, scores, tmax,
                        bmax, btmax, n_div, nullptr, nullptr, 0);
   else if (cand)
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4, false, true>),
                        grid, dim3(256), 0, s, k_codes, k_scales, n_cap,
-                       n_entries, cand, n_rows, iq.q, iq.q_scales, iq.w,
+                       iq.q, iq.w, n_rows, n_entries, cand, iq.q_scales,
                        scores, tmax, bmax, btmax, n_div, nullptr, nullptr, 0);
   else
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256),
-                       0, s, k_codes, k_scales, n_cap, n_entries, cand,
-                       n_rows, iq.q, iq.q_scales, iq.w, scores, tmax, bmax,
+                       0, s, k_codes, k_scales, n_cap, iq.q, iq.w,
+                       n_rows, n_entries, cand, iq.q_scales, scores, tmax, bmax,
                        btmax, n_div, nullptr, nullptr, 0);
 }
 template <int KEYFMT, bool KEYS>
@@ -581,8 +591,8 @@ hipError_t launch_local(int B, hipStream_t s, const void* k_codes,
   hipLaunchKernelGGL(
       (indexer_kernel<KF, true, QFP4, false, CAND, T, LOCAL>),
       dim3((unsigned)((n_rows + epb - 1) / epb), (unsigned)B), dim3(256),
-      smem, s, k_codes, k_scales, n_cap, n_entries, cand, n_rows, iq.q,
-      iq.q_scales, iq.w, reinterpret_cast<float*>(keys), nullptr, nullptr,
+      smem, s, k_codes, k_scales, n_cap, iq.q, iq.w, n_rows, n_entries, cand,
+      iq.q_scales, reinterpret_cast<float*>(keys), nullptr, nullptr,
       nullptr, n_div, lcand, lbound, lp.kloc);
   return hipGetLastError();
 }
