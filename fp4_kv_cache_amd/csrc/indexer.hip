@@ -195,13 +195,15 @@ __device__ __forceinline__ void store_keys(float* scores, int b,
 // or a workgroup's (LOCAL == 2: larger groups for long rows).
 template <int KEYFMT, bool KEYS, bool QFP4, bool BLK = false, bool CAND = false,
           int TPW = kTilesPerWave, int LOCAL = 0>
-// The arguments a wavefront needs before its first key loads come first:
-// the first 14 dwords are preloaded into scalar registers at dispatch.
+// The arguments a wavefront needs before its first key loads (the key
+// planes, the query, the weights, the candidate ids and the row count) come
+// first: the first 14 dwords are preloaded into scalar registers at
+// dispatch.  The entry count is read after the first key loads are issued.
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t n_cap, const void* __restrict__ q_in,
-    const float* __restrict__ w, int64_t n_rows,
-    const int32_t* __restrict__ n_entries, const int32_t* __restrict__ cand,
+    const float* __restrict__ w, const int32_t* __restrict__ cand,
+    int64_t n_rows, const int32_t* __restrict__ n_entries,
     const uint8_t* __restrict__ q_scales, float* __restrict__ scores,
     uint32_t* __restrict__ tmax, uint32_t* __restrict__ bmax,
     uint32_t* __restrict__ btmax, int n_div, uint2* __restrict__ lcand,
@@ -268,13 +270,15 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       const int64_t i = base + 32 * t + col;
       cv[t] = crow[i < n_rows ? i : n_rows - 1];
     }
+    // Rows to load are bounded by the cache (so the loads do not wait for
+    // the entry count); validity also needs the id below the entry count.
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t i = base + 32 * t + col;
       const int64_t e = cv[t];
-      const bool v = (i < n_rows) & (e >= 0) & (e < n);
-      vmask |= (v ? 1u : 0u) << t;
-      crow_v[t] = v ? (uint32_t)e : 0u;
+      const bool in = (i < n_rows) & (e >= 0);
+      vmask |= ((in & (e < n)) ? 1u : 0u) << t;
+      crow_v[t] = (in & (e < n_cap)) ? (uint32_t)e : 0u;
     }
   }
   // Plain rows: valid below lim = min(n_rows, n); base < 2^24.
@@ -545,23 +549,23 @@ void launch_one(int B, hipStream_t s, const void* k_codes,
   if (KEYFMT == 0 && !QFP4 && !bmax && !cand && waves >= kLongScanWaves)
     hipLaunchKernelGGL((indexer_kernel<0, KEYS, false, false, false, 16>),
                        grid_for(16), dim3(256), 0, s, k_codes, k_scales,
-                       n_cap, iq.q, iq.w, n_rows, n_entries, cand,
+                       n_cap, iq.q, iq.w, cand, n_rows, n_entries,
                        iq.q_scales, scores, tmax, bmax, btmax, n_div, nullptr,
                        nullptr, 0);
   else if (KEYS && KEYFMT == 0 && !QFP4 && bmax)
     hipLaunchKernelGGL((indexer_kernel<0, true, false, true>), grid,
                        dim3(256), 0, s, k_codes, k_scales, n_cap, iq.q,
-                       iq.w, n_rows, n_entries, cand, iq.q_scales, scores, tmax,
+                       iq.w, cand, n_rows, n_entries, iq.q_scales, scores, tmax,
                        bmax, btmax, n_div, nullptr, nullptr, 0);
   else if (cand)
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4, false, true>),
                        grid, dim3(256), 0, s, k_codes, k_scales, n_cap,
-                       iq.q, iq.w, n_rows, n_entries, cand, iq.q_scales,
+                       iq.q, iq.w, cand, n_rows, n_entries, iq.q_scales,
                        scores, tmax, bmax, btmax, n_div, nullptr, nullptr, 0);
   else
     hipLaunchKernelGGL((indexer_kernel<KEYFMT, KEYS, QFP4>), grid, dim3(256),
                        0, s, k_codes, k_scales, n_cap, iq.q, iq.w,
-                       n_rows, n_entries, cand, iq.q_scales, scores, tmax, bmax,
+                       cand, n_rows, n_entries, iq.q_scales, scores, tmax, bmax,
                        btmax, n_div, nullptr, nullptr, 0);
 }
 template <int KEYFMT, bool KEYS>
@@ -591,7 +595,7 @@ hipError_t launch_local(int B, hipStream_t s, const void* k_codes,
   hipLaunchKernelGGL(
       (indexer_kernel<KF, true, QFP4, false, CAND, T, LOCAL>),
       dim3((unsigned)((n_rows + epb - 1) / epb), (unsigned)B), dim3(256),
-      smem, s, k_codes, k_scales, n_cap, iq.q, iq.w, n_rows, n_entries, cand,
+      smem, s, k_codes, k_scales, n_cap, iq.q, iq.w, cand, n_rows, n_entries,
       iq.q_scales, reinterpret_cast<float*>(keys), nullptr, nullptr,
       nullptr, n_div, lcand, lbound, lp.kloc);
   return hipGetLastError();
