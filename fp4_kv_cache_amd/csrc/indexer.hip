@@ -242,12 +242,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   // n_div) (rows are blocks of n_div entries; 32-bit unsigned, exact for
   // these ranges), never past the cache.  The MXFP4 scan carries no
   // division: it would sit before every wavefront's first load.
-  const int32_t ne = n_entries[b];
-  int64_t n = ne <= 0 ? 0 : (int64_t)ne;
-  if constexpr (KEYFMT == 1)
-    if (ne > 0 && n_div > 1)
-      n = (int64_t)(((uint32_t)ne + (uint32_t)n_div - 1u) / (uint32_t)n_div);
-  n = n > n_cap ? n_cap : n;
   const void* seq_codes = static_cast<const uint8_t*>(k_codes) +
                           (int64_t)b * n_cap * (KEYFMT == 0 ? 64 : 256);
   const uint8_t* seq_scales =
@@ -271,34 +265,24 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       cv[t] = crow[i < n_rows ? i : n_rows - 1];
     }
     // Rows to load are bounded by the cache (so the loads do not wait for
-    // the entry count); validity also needs the id below the entry count.
+    // the entry count); validity (below) also needs the id below the count.
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t i = base + 32 * t + col;
       const int64_t e = cv[t];
-      const bool in = (i < n_rows) & (e >= 0);
-      vmask |= ((in & (e < n)) ? 1u : 0u) << t;
-      crow_v[t] = (in & (e < n_cap)) ? (uint32_t)e : 0u;
+      const bool in = (i < n_rows) & (e >= 0) & (e < n_cap);
+      vmask |= (in ? 1u : 0u) << t;
+      crow_v[t] = in ? (uint32_t)e : 0u;
     }
   }
-  // Plain rows: valid below lim = min(n_rows, n); base < 2^24.
-  const uint32_t lim = (uint32_t)(n_rows < n ? n_rows : n);
-  const uint32_t r0 = (uint32_t)base + (uint32_t)col;
-  auto row_of = [&](int t) -> uint32_t {
-    if constexpr (CAND) return crow_v[t];
-    else return r0 + 32u * t < lim ? r0 + 32u * t : 0u;
-  };
   // The first tiles' rows are bounded by the cache alone, so their loads
   // do not wait for the sequence's entry count (their scores are masked
   // by it like every other tile's).
+  const uint32_t r0 = (uint32_t)base + (uint32_t)col;
   const uint32_t lim_rows = (uint32_t)n_rows;
   auto row_pf = [&](int t) -> uint32_t {
     if constexpr (CAND) return crow_v[t];
     else return r0 + 32u * t < lim_rows ? r0 + 32u * t : 0u;
-  };
-  auto valid = [&](int t) -> bool {
-    if constexpr (CAND) return (vmask >> t) & 1u;
-    else return r0 + 32u * t < lim;
   };
 
   // A operand: head `col`, dims 64*half + 8*s .. +7 for step s (bf16), or
@@ -307,18 +291,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   bf16x8 qa[kScaledOp ? 1 : 8];
   RawKey<0> q4;
   if constexpr (QFP4) {
+    // The codes now; the scales (their pointer is not a preloaded
+    // argument) after the first key loads.
     const int64_t head = (int64_t)b * kIdxHeads + col;
     const u32x4* qp = reinterpret_cast<const u32x4*>(
         static_cast<const uint8_t*>(q_in) + head * 64 + 32 * half);
     q4.c0 = qp[0];
     q4.c1 = qp[1];
-    q4.sc = *reinterpret_cast<const uint32_t*>(q_scales + head * 4);
-    if constexpr (kScaledOp) {
-      q4.sc >>= 16 * half;
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qa[s] = key_operand<0>(q4, s, half);
-    }
   }
   // bf16 query with local candidates (no wavefront leaves early): the
   // workgroup reads the sequence's 8 KB query and 32 weights once,
@@ -349,6 +328,45 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 #pragma unroll
   for (int t = 0; t < D; ++t)
     load_key<KEYFMT, kScaledOp>(buf[t], seq_codes, seq_scales, row_pf(t), half);
+  // The entry count, and everything that needs it, comes after the first
+  // key loads are issued (its pointer is not among the preloaded arguments,
+  // so its load would otherwise wait for an argument-line miss first).
+  __builtin_amdgcn_sched_barrier(0);
+  // Valid rows: n_entries[b], or for bf16 block keys ceil(n_entries[b] /
+  // n_div) (rows are blocks of n_div entries; 32-bit unsigned, exact for
+  // these ranges), never past the cache.
+  if constexpr (QFP4) {
+    const int64_t head = (int64_t)b * kIdxHeads + col;
+    q4.sc = *reinterpret_cast<const uint32_t*>(q_scales + head * 4);
+    if constexpr (kScaledOp) {
+      q4.sc >>= 16 * half;
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qa[s] = key_operand<0>(q4, s, half);
+    }
+  }
+  const int32_t ne = n_entries[b];
+  int64_t n = ne <= 0 ? 0 : (int64_t)ne;
+  if constexpr (KEYFMT == 1)
+    if (ne > 0 && n_div > 1)
+      n = (int64_t)(((uint32_t)ne + (uint32_t)n_div - 1u) / (uint32_t)n_div);
+  n = n > n_cap ? n_cap : n;
+  if constexpr (CAND) {
+    // A named row is valid below the entry count (n <= n_cap).
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      if ((int64_t)crow_v[t] >= n) vmask &= ~(1u << t);
+  }
+  // Plain rows: valid below lim = min(n_rows, n); base < 2^24.
+  const uint32_t lim = (uint32_t)(n_rows < n ? n_rows : n);
+  auto row_of = [&](int t) -> uint32_t {
+    if constexpr (CAND) return crow_v[t];
+    else return r0 + 32u * t < lim ? r0 + 32u * t : 0u;
+  };
+  auto valid = [&](int t) -> bool {
+    if constexpr (CAND) return (vmask >> t) & 1u;
+    else return r0 + 32u * t < lim;
+  };
   // Weights of the 16 output rows this lane holds: head 8a + 4*half + r.
   float wr[16];
   if constexpr (kStageQ) {
