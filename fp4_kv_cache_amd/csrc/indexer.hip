@@ -35,9 +35,13 @@
 // are 2h and 2h+1.  Every product is exact; the sums are float32.  The
 // bf16 block keys take the query dequantised to bf16, which is exact.
 //
-// Tile maxima (the decode path): each 32-row tile's largest score is also
-// written (one wave reduction per tile); the top-k stage uses them to read
-// only the tiles that can hold a winner.
+// Selection keys: with KEYS the scores are written as order-preserving
+// uint32 keys, and either each 32-row tile's largest key (the top-k stage
+// then reads only the tiles that can hold a winner) or, in the decode path,
+// each group's own top entries and a bound (local candidates, below), from
+// which the attention workgroups select the top-k themselves.  There the
+// sequence's query is read once per workgroup and staged in LDS, and
+// nothing the first key loads do not need is read before them.
 #include "common.h"
 #include "internal.h"
 #include "select.h"
