@@ -133,6 +133,44 @@ def test_fused_select_full_generation_batch():
         _check(st, out, ids, b, int(ne[b]), q_idx=qz, exact_ids=True)
 
 
+@pytest.mark.parametrize("case", range(10))
+def test_fused_decode_random_shapes(case):
+    """Seeded random shapes: batch 1-40, 1-6,000 entries, k a multiple of
+    16 up to 1,024, window lengths 0-128 per sequence, ragged entry counts
+    (including empty rows and rows shorter than k); every sequence against
+    the oracle."""
+    rng = np.random.default_rng(9000 + case)
+    B = int(rng.integers(1, 41))
+    n = int(rng.integers(1, 6001))
+    k = 16 * int(rng.integers(1, 65))
+    wl = dataclasses.replace(WORKLOADS[1], cid=300 + case, B=B, n=n, k=k)
+    st = workload.build(wl, DEV)
+    ne = rng.integers(0, n + 1, B).astype(np.int32)
+    ne[0] = n
+    st.n_entries.copy_(torch.from_numpy(ne))
+    ns = rng.integers(0, 129, B).astype(np.int32)
+    st.n_swa.copy_(torch.from_numpy(ns))
+    wl_ns = [int(x) for x in ns]
+    out, ids = _decode(st)
+    for b in range(B):
+        if ne[b] == 0:
+            assert np.all(ids[b] == -1), b
+        mc, ms, ic, isc, sw = _host(st, b)
+        qi = bf16_bits(st.q_idx[b])
+        w = st.w[b].cpu().numpy()
+        q = bf16_bits(st.q[0][b])
+        sel, ref, sc = O.full_layer(mc, ms, ic, isc, int(ne[b]), qi, w, q, sw,
+                                    wl_ns[b], k, st.scale)
+        ok, msg = topk_set_ok(ids[b], sc, k)
+        assert ok, (case, b, msg)
+        if ne[b] == 0 and wl_ns[b] == 0:
+            continue                      # no key at all: nothing to attend
+        if np.array_equal(ids[b], sel):
+            e = rel_l2(out[b], ref)
+            assert e <= REL_L2_TOL, (case, b, e)
+    print(case, B, n, k, "ok", flush=True)
+
+
 def _split_shape(S):
     best = None
     for B in range(1, 257):
