@@ -168,3 +168,25 @@ def test_pool_crowded_block_group_fallback():
             e = rel_l2(out[b], ref)
             assert e <= REL_L2_TOL, (b, e)
         print(b, msg, flush=True)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_pool_decode_random_shapes(case):
+    """Seeded random hierarchical decodes: batch 1-6, 3,000-40,000 entries
+    (ragged last block), pools of 128-2,048 blocks of 8, k a multiple of 16
+    below the pool's positions; every sequence against the oracle's
+    hierarchy (block keys bit for bit, pool, top-k by the gap rule,
+    attention)."""
+    rng = np.random.default_rng(9100 + case)
+    B = int(rng.integers(1, 7))
+    n = int(rng.integers(3000, 40001))
+    n_keep = int(rng.choice([128, 512, 1024, 2048]))
+    k = 16 * int(rng.integers(1, 33))
+    k = min(k, (n_keep * 8) // 2)
+    wl = dataclasses.replace(WORKLOADS[4], cid=400 + case, B=B, n=n, k=k,
+                             pool=(n_keep, 8))
+    st = workload.build(wl, DEV)
+    out, ids, _ = _run(st)
+    for b in range(B):
+        msg, errs = _check_seq(st, b, out, ids)
+        print(case, B, n, n_keep, k, b, msg, errs, flush=True)
