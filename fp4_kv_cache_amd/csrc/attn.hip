@@ -146,11 +146,13 @@ struct AttnArgs {
 static_assert(offsetof(AttnArgs, lbound) + sizeof(void*) <= 64,
               "the kernel's first accesses share one line");
 
-// The fields above the 64-byte mark are also passed ahead of the struct as
+// The fields before the 64-byte mark are also passed ahead of the struct as
 // plain arguments (14 dwords): the build preloads a kernel's leading
-// scalar arguments into scalar registers at dispatch, so the kernel's
-// first steps need no argument load.  The kernel puts them back into a
-// local copy of the struct.
+// scalar arguments into scalar registers at dispatch (a struct argument is
+// not preloaded), so the kernel's first steps need no argument load.  The
+// kernel puts them back into a local copy of the struct; that copy's `epi`
+// is not used (it holds an array indexed per lane, which would put the
+// copy in scratch memory): the epilogue reads the argument struct's own.
 #define CSA2_ATTN_HEAD_PARAMS                                                \
   int h_B, int h_splits, int h_k, int h_n_wg, int h_kloc, int h_tps,         \
       const uint16_t *h_q, const int32_t *h_n_swa, const uint2 *h_lcand,     \
